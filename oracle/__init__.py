@@ -1,0 +1,224 @@
+"""CPU oracle for the FP8 quantized linear layer (dense block-scaled and 2:4 sparse).
+
+TEST INFRASTRUCTURE ONLY.  Tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package; the library and its
+Python binding never do.  It shares no code with the HIP path.
+
+The arithmetic lives in ``oracle.c`` (plain C, compiled with gcc into
+``liboracle.so``); this module only marshals numpy arrays.  The definitions it
+follows are cited in ``oracle.c``:
+
+* "FP8 a granularite fine" (transformers docs), intro bullets and section
+  "Chemin rapide de DeepGEMM": 128x128 weight blocks, dynamic per-token
+  1x128 activation groups;
+* "Deployer la parcimonie 2:4 avec FP8 sur Hopper", pipeline steps 2, 4, 6, 7
+  and practical example 1: groups of 4 along K, keep the top two scores,
+  recalibrate scales after pruning, export values + masks;
+* "Combiner elagage et quantification", section "La cle": keep the two
+  largest of every four.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against
+closed forms, brute force and exact rational arithmetic; none is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GROUP = 128
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no fast-math, no FTZ)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
+               "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            I = ctypes.c_int64
+            lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+            lib.oracle_e4m3_decode.restype = ctypes.c_double
+            lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+            lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+            lib.oracle_quant_act.argtypes = [P, I, I, P, P]
+            lib.oracle_quant_wblock.argtypes = [P, I, I, P, P]
+            lib.oracle_prune24_mask.argtypes = [P, P, I, I, P]
+            lib.oracle_prune24_compress.argtypes = [P, P, I, I, P, P, P]
+            lib.oracle_decompress24.argtypes = [P, P, I, I, P]
+            lib.oracle_gemm.argtypes = [P, P, P, P, I, I, I, P]
+            lib.oracle_gemm_rows.argtypes = [P, P, P, P, I, I, I, P, I, P]
+            lib.oracle_num_threads.restype = ctypes.c_int
+            for f in ("oracle_quant_act", "oracle_quant_wblock", "oracle_prune24_mask",
+                      "oracle_prune24_compress", "oracle_decompress24", "oracle_gemm",
+                      "oracle_gemm_rows"):
+                getattr(lib, f).restype = None
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check_bf16(x: np.ndarray, name: str):
+    if x.dtype != np.uint16 or x.ndim != 2:
+        raise TypeError(f"{name}: expected a 2-D uint16 array of bf16 bits")
+
+
+# ----------------------------------------------------------------- codec ----
+
+def e4m3_decode(code: int) -> float:
+    """Value of one E4M3FN code (NaN for 0x7F / 0xFF)."""
+    return _load().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(v: float) -> int:
+    """Round a real value to the nearest E4M3FN code, ties to even, saturating at +-448."""
+    return int(_load().oracle_e4m3_encode(float(v)))
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """fp64 value of each of the 256 codes."""
+    return np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_encode_array(v: np.ndarray) -> np.ndarray:
+    """Element-wise encode of a float array (slow: one C call per element)."""
+    lib = _load()
+    flat = np.asarray(v, dtype=np.float64).ravel()
+    out = np.fromiter((lib.oracle_e4m3_encode(float(t)) for t in flat), dtype=np.uint8, count=flat.size)
+    return out.reshape(np.shape(v))
+
+
+# ------------------------------------------------------------ quantizers ----
+
+def quant_act(x_bf16: np.ndarray):
+    """Per-token 1x128 quantization: returns (codes [M,K] u8, scales [M,K/128] f32)."""
+    _check_bf16(x_bf16, "x")
+    x = np.ascontiguousarray(x_bf16)
+    M, K = x.shape
+    assert K % GROUP == 0
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M, K // GROUP), np.float32)
+    if M:
+        _load().oracle_quant_act(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_wblock(w_bf16: np.ndarray):
+    """128x128 block quantization: returns (codes [N,K] u8, scales [N/128,K/128] f32)."""
+    _check_bf16(w_bf16, "w")
+    w = np.ascontiguousarray(w_bf16)
+    N, K = w.shape
+    assert N % GROUP == 0 and K % GROUP == 0
+    q = np.empty((N, K), np.uint8)
+    s = np.empty((N // GROUP, K // GROUP), np.float32)
+    _load().oracle_quant_wblock(_ptr(w), N, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+# ------------------------------------------------------------------ 2:4 -----
+
+def prune24_mask(w_bf16: np.ndarray, col_norm: np.ndarray | None = None) -> np.ndarray:
+    """Boolean keep-mask [N,K]: exactly two per group of 4 along K."""
+    _check_bf16(w_bf16, "w")
+    w = np.ascontiguousarray(w_bf16)
+    N, K = w.shape
+    assert K % 4 == 0
+    keep = np.empty((N, K), np.uint8)
+    c = None if col_norm is None else np.ascontiguousarray(col_norm, dtype=np.float32)
+    if c is not None:
+        assert c.shape == (K,)
+    _load().oracle_prune24_mask(_ptr(w), None if c is None else _ptr(c), N, K, _ptr(keep))
+    return keep.astype(bool)
+
+
+def prune24_compress(w_bf16: np.ndarray, col_norm: np.ndarray | None = None):
+    """Prune 2:4, block scales over kept values, quantize, pack.
+
+    Returns (vals [N,K/2] u8, meta [N,K/8] u8, scales [N/128,K/128] f32).
+    """
+    _check_bf16(w_bf16, "w")
+    w = np.ascontiguousarray(w_bf16)
+    N, K = w.shape
+    assert N % GROUP == 0 and K % GROUP == 0
+    c = None if col_norm is None else np.ascontiguousarray(col_norm, dtype=np.float32)
+    vals = np.empty((N, K // 2), np.uint8)
+    meta = np.empty((N, K // 8), np.uint8)
+    s = np.empty((N // GROUP, K // GROUP), np.float32)
+    _load().oracle_prune24_compress(_ptr(w), None if c is None else _ptr(c), N, K,
+                                    _ptr(vals), _ptr(meta), _ptr(s))
+    return vals, meta, s
+
+
+def decompress24(vals: np.ndarray, meta: np.ndarray) -> np.ndarray:
+    """Dense codes [N,K] from the packed 2:4 form (0x00 at pruned places)."""
+    vals = np.ascontiguousarray(vals, dtype=np.uint8)
+    meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    N, K2 = vals.shape
+    K = 2 * K2
+    assert meta.shape == (N, K // 8)
+    q = np.empty((N, K), np.uint8)
+    _load().oracle_decompress24(_ptr(vals), _ptr(meta), N, K, _ptr(q))
+    return q
+
+
+# ------------------------------------------------------------------ GEMM ----
+
+def gemm(xq, xs, wq, ws, rows: np.ndarray | None = None) -> np.ndarray:
+    """fp64 Y = sum over K blocks of (sx * sw) * (exact fp64 block dot product).
+
+    ``rows`` (optional int64 indices) restricts the output to those rows of Y.
+    """
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    ws = np.ascontiguousarray(ws, dtype=np.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape == (N, K) and xs.shape == (M, K // GROUP) and ws.shape == (N // GROUP, K // GROUP)
+    lib = _load()
+    if rows is None:
+        y = np.empty((M, N), np.float64)
+        if M:
+            lib.oracle_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y))
+        return y
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    assert r.ndim == 1 and (r.size == 0 or (r.min() >= 0 and r.max() < M))
+    y = np.empty((r.size, N), np.float64)
+    if r.size:
+        lib.oracle_gemm_rows(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(r), r.size, _ptr(y))
+    return y
+
+
+def sparse24_gemm(xq, xs, vals, meta, ws, rows: np.ndarray | None = None) -> np.ndarray:
+    """The GEMM on the decompressed 2:4 weight (pruned places contribute zero)."""
+    return gemm(xq, xs, decompress24(vals, meta), ws, rows=rows)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle GEMM runs on."""
+    return int(_load().oracle_num_threads())

@@ -1,0 +1,445 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test ties one oracle function to a closed form, a library routine, exact
+rational arithmetic or brute force, chosen so that a plausible slip (wrong
+bias, wrong tie rule, a dropped scale, a transposed operand, a wrong nibble
+order) fails at least one of them.
+"""
+from __future__ import annotations
+
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from exact_ref import (E4M3_POS, best_pair, bf16_value, decode_exact, f32_round, nearest_e4m3,
+                       quantize_exact)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32(x):
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+# ------------------------------------------------------------ e4m3 decode ---
+
+def test_decode_golden_points():
+    with open(os.path.join(GOLDEN, "e4m3_points.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(rows) >= 10
+    for code, val in rows:
+        got = oracle.e4m3_decode(int(code, 16))
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val))
+
+
+def test_decode_all_codes_vs_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode_table()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert set(np.nonzero(nan)[0].tolist()) == {0x7F, 0xFF}
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_decode_vs_exact_table():
+    for code, val in E4M3_POS:
+        assert Fraction(oracle.e4m3_decode(code)) == val
+        assert Fraction(oracle.e4m3_decode(code | 0x80)) == -val
+
+
+# ------------------------------------------------------------ e4m3 encode ---
+
+def test_encode_roundtrip_all_codes():
+    for c in range(256):
+        v = oracle.e4m3_decode(c)
+        e = oracle.e4m3_encode(v)
+        if c in (0x7F, 0xFF):
+            assert e in (0x7F, 0xFF)
+        else:
+            assert e == c, (hex(c), v, hex(e))
+
+
+def test_encode_saturation_and_specials():
+    assert oracle.e4m3_encode(448.0) == 0x7E
+    assert oracle.e4m3_encode(449.0) == 0x7E
+    assert oracle.e4m3_encode(1e30) == 0x7E
+    assert oracle.e4m3_encode(math.inf) == 0x7E
+    assert oracle.e4m3_encode(-math.inf) == 0xFE
+    assert oracle.e4m3_encode(-500.0) == 0xFE
+    assert oracle.e4m3_encode(math.nan) in (0x7F, 0xFF)
+    assert oracle.e4m3_encode(0.0) == 0x00
+    assert oracle.e4m3_encode(-0.0) == 0x80
+    assert oracle.e4m3_encode(-1e-30) == 0x80          # negative underflow keeps the sign
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00      # tie between 0 and 2^-9 -> even (0)
+    assert oracle.e4m3_encode(3 * 2.0 ** -10) == 0x02  # tie between codes 1 and 2 -> 2
+    assert oracle.e4m3_encode(432.0) == 0x7E           # tie 416 / 448 -> 0x7E (even)
+    assert oracle.e4m3_encode(f32(432.0 - 2 ** -15)) == 0x7D
+
+
+def test_encode_all_bf16_vs_torch_cast():
+    """Every bf16 value with |v| <= 448: torch's RNE cast is an independent encoder."""
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    ok = np.isfinite(vals) & (np.abs(vals) <= 448)
+    v = vals[ok]
+    ref = torch.from_numpy(v.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode_array(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+    # above 448 torch does not saturate; the rule is saturation
+    big = vals[np.isfinite(vals) & (np.abs(vals) > 448)]
+    got_big = oracle.e4m3_encode_array(big.astype(np.float64))
+    assert np.array_equal(got_big, np.where(big > 0, 0x7E, 0xFE).astype(np.uint8))
+
+
+def test_encode_near_midpoints_vs_brute_force():
+    """fp32 values at and one ulp around every midpoint: exhaustive nearest search."""
+    vals = [v for _, v in E4M3_POS]
+    cases = []
+    for lo, hi in zip(vals[:-1], vals[1:]):
+        mid = float((lo + hi) / 2)
+        cases += [mid, float(np.nextafter(np.float32(mid), np.float32(0))),
+                  float(np.nextafter(np.float32(mid), np.float32(1000)))]
+    for v in cases:
+        for sgn in (1.0, -1.0):
+            want = nearest_e4m3(Fraction(v), negative=sgn < 0)
+            assert oracle.e4m3_encode(sgn * v) == want, (v, sgn)
+
+
+def test_encode_random_fp32_vs_torch():
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal(200000) * np.exp(rng.uniform(-14, 6.2, 200000))).astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode_array(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------- activation quantization ---
+
+def _bf16_bits(vals):
+    return si.to_bf16_bits(torch.tensor(np.asarray(vals, dtype=np.float32)))
+
+
+def test_quant_act_exact_small():
+    """Whole-path check on a small X with crafted groups, against exact arithmetic."""
+    rng = np.random.default_rng(11)
+    M, K = 5, 384
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.exp(rng.uniform(-3, 3, (M, 1))).astype(np.float32)
+    x[1, 128:256] = 0.0                                   # all-zero group
+    x[1, 130] = -0.0
+    x[2, 0:128] = rng.standard_normal(128).astype(np.float32) * 1e-39  # bf16 subnormals
+    x[3, 256:384] = 1e20 * rng.standard_normal(128).astype(np.float32)
+    xb = _bf16_bits(x)
+    q, s = oracle.quant_act(xb)
+    for m in range(M):
+        for kb in range(K // 128):
+            g = [bf16_value(int(b)) for b in xb[m, kb * 128:(kb + 1) * 128]]
+            s_ref, codes = quantize_exact(g)
+            assert s[m, kb] == np.float32(s_ref), (m, kb)
+            assert q[m, kb * 128:(kb + 1) * 128].tolist() == codes, (m, kb)
+    assert s[1, 1] == 0.0 and q[1, 130] == 0x80
+    assert 0 < s[2, 0] < np.finfo(np.float32).tiny   # subnormal fp32 scale
+
+
+def test_quant_act_division_is_not_reciprocal():
+    """Codes follow x/s, which differs from x*(448/amax) in rare cases."""
+    xb = si.activations(64, 4096, outliers=False)
+    q, s = oracle.quant_act(xb)
+    x = si.bf16_bits_to_f32(xb).reshape(64, 32, 128)
+    amax = np.abs(x).max(axis=2, keepdims=True)
+    recip = (np.float32(448) / amax).astype(np.float32)
+    alt = torch.from_numpy((x * recip).astype(np.float32).reshape(64, 4096)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    div = torch.from_numpy((x / s.reshape(64, 32, 1)).astype(np.float32).reshape(64, 4096)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, div)
+    assert not np.array_equal(q, alt)
+
+
+def test_quant_act_invariants():
+    xb = si.activations(32, 4096)
+    q, s = oracle.quant_act(xb)
+    x = si.bf16_bits_to_f32(xb).astype(np.float64).reshape(32, 32, 128)
+    qq = q.reshape(32, 32, 128)
+    # every non-zero group reaches the largest code
+    assert np.all((qq & 0x7F).max(axis=2) == 0x7E)
+    # reconstruction within half an e4m3 step (relative 2^-4, absolute 2^-10 in the subnormal range)
+    dec = oracle.e4m3_decode_table()[qq]
+    r = x / s.reshape(32, 32, 1).astype(np.float64)
+    step = np.where(np.abs(r) >= 2.0 ** -6, 2.0 ** np.floor(np.log2(np.maximum(np.abs(r), 1e-300))) / 8, 2.0 ** -9)
+    assert np.all(np.abs(dec - r) <= step / 2 * (1 + 1e-6))
+
+
+def test_quant_act_scale_invariance():
+    xb = si.activations(8, 1024, outliers=False)
+    q, s = oracle.quant_act(xb)
+    for j in (-5, 3, 17):
+        xj = si.to_bf16_bits(torch.from_numpy(si.bf16_bits_to_f32(xb) * np.float32(2.0 ** j)))
+        qj, sj = oracle.quant_act(xj)
+        assert np.array_equal(qj, q)
+        assert np.array_equal(sj, (s * np.float32(2.0 ** j)).astype(np.float32))
+
+
+def test_quant_act_token_and_group_independence():
+    """Changing one group changes only that group's codes and scale (no transposition)."""
+    xb = si.activations(6, 512, outliers=False)
+    q, s = oracle.quant_act(xb)
+    xb2 = xb.copy()
+    xb2[4, 256:384] = _bf16_bits(np.linspace(-3, 5, 128))
+    q2, s2 = oracle.quant_act(xb2)
+    diff = q != q2
+    assert diff[4, 256:384].any() and not diff[:4].any() and not diff[5].any()
+    assert not diff[4, :256].any() and not diff[4, 384:].any()
+    sd = s != s2
+    assert sd[4, 2] and sd.sum() == 1
+
+
+# ---------------------------------------------------- weight quantization ---
+
+@pytest.mark.parametrize("N,K", [(128, 128), (256, 128), (128, 256)])
+def test_quant_wblock_exact(N, K):
+    w = si.weights(N, K)
+    w[0, 0] = _bf16_bits([3.0])[0]   # one large value in block (0,0)
+    q, s = oracle.quant_wblock(w)
+    for nb in range(N // 128):
+        for kb in range(K // 128):
+            blk = w[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128].ravel()
+            vals = [bf16_value(int(b)) for b in blk]
+            s_ref, codes = quantize_exact(vals)
+            assert s[nb, kb] == np.float32(s_ref)
+            got = q[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128].ravel().tolist()
+            assert got == codes
+
+
+def test_quant_wblock_block_scale_layout():
+    """Scale (nb,kb) depends only on its block: planting a big value moves one scale."""
+    w = si.weights(256, 384)
+    _, s = oracle.quant_wblock(w)
+    w2 = w.copy()
+    w2[200, 300] = _bf16_bits([10.0])[0]   # block (1, 2)
+    _, s2 = oracle.quant_wblock(w2)
+    changed = np.argwhere(s != s2)
+    assert changed.tolist() == [[1, 2]]
+    assert s2[1, 2] == np.float32(10.0) / np.float32(448.0)
+
+
+# ------------------------------------------------------------------ 2:4 ------
+
+def test_prune_golden_groups():
+    with open(os.path.join(GOLDEN, "prune24_groups.txt")) as f:
+        rows = [ln for ln in f if ln.strip() and not ln.startswith("#")]
+    for ln in rows:
+        wv, cv, kv = [p.split() for p in ln.split("|")]
+        w = np.zeros((1, 128), np.float32)
+        c = np.ones(128, np.float32)
+        w[0, 4:8] = [float(t) for t in wv]
+        c[4:8] = [float(t) for t in cv]
+        keep = oracle.prune24_mask(_bf16_bits(w), c)
+        assert np.nonzero(keep[0, 4:8])[0].tolist() == [int(t) for t in kv], ln
+
+
+def test_prune_brute_force_with_ties():
+    rng = np.random.default_rng(3)
+    N, K = 16, 256
+    w = rng.integers(-3, 4, (N, K)).astype(np.float32)   # many ties
+    c = rng.integers(0, 3, K).astype(np.float32)
+    wb = _bf16_bits(w)
+    for cn in (None, c):
+        keep = oracle.prune24_mask(wb, cn)
+        assert np.all(keep.reshape(N, K // 4, 4).sum(axis=2) == 2)
+        for n in range(N):
+            for g in range(K // 4):
+                sc = [abs(Fraction(float(w[n, 4 * g + j]))) * (1 if cn is None else Fraction(float(cn[4 * g + j])))
+                      for j in range(4)]
+                i, j = best_pair(sc)
+                assert np.nonzero(keep[n, 4 * g:4 * g + 4])[0].tolist() == [i, j]
+
+
+def test_prune_activation_aware_exact_scores():
+    """Scores are exact products: an fp32 product would tie these two, fp64 does not."""
+    w = np.zeros((1, 128), np.float32)
+    c = np.ones(128, np.float32)
+    a = f32(1.0 + 2 ** -7)          # bf16-exact
+    b = f32(1.0)
+    ca = f32(1.0 - 2 ** -23)
+    cb = f32(1.0 + 2 ** -7 - 2 ** -22)
+    # a*ca = 1 + 2^-7 - 2^-23 - 2^-30 ; b*cb = 1 + 2^-7 - 2^-22  -> a*ca is larger
+    w[0, :4] = [a, b, 0.0, 0.0]
+    c[:4] = [ca, cb, 1.0, 1.0]
+    keep = oracle.prune24_mask(_bf16_bits(w), c)
+    assert keep[0, :4].tolist() == [True, True, False, False]
+    w[0, :4] = [0.0, b, a, 0.0]
+    c[:4] = [1.0, cb, ca, 1.0]
+    keep = oracle.prune24_mask(_bf16_bits(w), c)
+    assert keep[0, :4].tolist() == [False, True, True, False]
+    # now three candidates: a*ca > b*cb, so with a third big value b is dropped
+    w[0, :4] = [0.0, b, a, 4.0]
+    c[:4] = [1.0, cb, ca, 1.0]
+    keep = oracle.prune24_mask(_bf16_bits(w), c)
+    assert keep[0, :4].tolist() == [False, False, True, True]
+
+
+def test_prune_matches_page_topk_snippet_on_tie_free_groups():
+    """The top-2-by-|w| snippet of the 2:4 cookbook (practical example 1), on groups without ties."""
+    w = si.weights(128, 1024)
+    keep = oracle.prune24_mask(w)
+    wt = torch.from_numpy(si.bf16_bits_to_f32(w))
+    g = wt.reshape(128, 256, 4).abs()
+    top2 = g.topk(k=2, dim=-1).indices
+    mask = torch.zeros_like(g, dtype=torch.bool)
+    mask.scatter_(-1, top2, True)
+    srt = g.sort(dim=-1, descending=True).values
+    tie_free = (srt[..., 1] != srt[..., 2]).numpy()
+    assert tie_free.mean() > 0.99
+    assert np.array_equal(keep.reshape(128, 256, 4)[tie_free], mask.numpy()[tie_free])
+
+
+def test_compress_roundtrip_and_cross_path_identity():
+    w = si.weights(256, 512)
+    c = si.column_norms(si.calibration_batch(512))
+    for cn in (None, c):
+        vals, meta, s = oracle.prune24_compress(w, cn)
+        keep = oracle.prune24_mask(w, cn)
+        # pruned bf16 weights, then plain block quantization
+        wp = np.where(keep, w, np.uint16(0)).astype(np.uint16)
+        qd, sd = oracle.quant_wblock(wp)
+        assert np.array_equal(s, sd)
+        dense = oracle.decompress24(vals, meta)
+        assert np.array_equal(dense, qd)
+        # nibbles are valid (i0 < i1) and describe the mask
+        nib = np.stack([meta & 15, meta >> 4], axis=-1).reshape(256, 128)
+        assert set(np.unique(nib).tolist()) <= {4, 8, 12, 9, 13, 14}
+        i0, i1 = nib & 3, nib >> 2
+        km = keep.reshape(256, 128, 4)
+        rows = np.arange(256)[:, None]
+        grp = np.arange(128)[None, :]
+        assert km[rows, grp, i0].all() and km[rows, grp, i1].all()
+        # values in index order
+        assert np.array_equal(vals.reshape(256, 128, 2)[..., 0], qd.reshape(256, 128, 4)[rows, grp, i0])
+
+
+def test_compress_nibble_order_by_hand():
+    w = np.zeros((128, 128), np.float32)
+    w[0, 0:4] = [0, 5, 0, 7]       # group 0 keeps (1,3) -> nibble 1 | 3<<2 = 13
+    w[0, 4:8] = [9, 0, 8, 0]       # group 1 keeps (0,2) -> nibble 0 | 2<<2 = 8
+    vals, meta, s = oracle.prune24_compress(_bf16_bits(w))
+    assert meta[0, 0] == 13 | (8 << 4)
+    assert s[0, 0] == np.float32(9.0) / np.float32(448.0)
+    enc = lambda v: oracle.e4m3_encode(f32(np.float32(v) / s[0, 0]))
+    assert vals[0, :4].tolist() == [enc(5), enc(7), 0x7E, enc(8)]
+    assert enc(7) == 123 and enc(5) == 120 and enc(8) == 124
+
+
+def test_postprune_scale_uses_kept_values_only():
+    w = np.full((128, 128), 0.01, np.float32)
+    w[5, 8:12] = [100.0, 0.5, 0.6, 0.0]     # 100 is kept
+    w[6, 8:12] = [0.0, 200.0, 300.0, 400.0]  # 200 is dropped
+    _, _, s = oracle.prune24_compress(_bf16_bits(w))
+    assert s[0, 0] == np.float32(400.0) / np.float32(448.0)
+    w[6, 8:12] = [0.0, 0.0, 300.0, 0.0]
+    w[7, 0:4] = [500.0, 600.0, 700.0, 800.0]  # 500, 600 dropped
+    _, _, s = oracle.prune24_compress(_bf16_bits(w))
+    assert s[0, 0] == np.float32(800.0) / np.float32(448.0)
+
+
+# ------------------------------------------------------------------ GEMM -----
+
+def _dequant(q, s, rows_per_scale_row, blocks_along_rows=False):
+    dec = np.array([float(decode_exact(c)) if c not in (0x7F, 0xFF) else np.nan for c in range(256)])
+    return dec[q]
+
+
+def test_gemm_exact_fraction_tiny():
+    rng = np.random.default_rng(5)
+    M, N, K = 3, 128, 256
+    xq, xs = oracle.quant_act(si.to_bf16_bits(torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))))
+    wq, ws = oracle.quant_wblock(si.weights(N, K))
+    y = oracle.gemm(xq, xs, wq, ws)
+    for m in range(M):
+        for n in range(0, N, 7):
+            acc = Fraction(0)
+            for kb in range(K // 128):
+                p = sum(decode_exact(int(xq[m, k])) * decode_exact(int(wq[n, k])) for k in range(kb * 128, kb * 128 + 128))
+                acc += Fraction(float(xs[m, kb])) * Fraction(float(ws[n // 128, kb])) * p
+            assert abs(Fraction(y[m, n]) - acc) <= abs(acc) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 1000)
+
+
+def test_gemm_vs_numpy_dequant_matmul():
+    M, N, K = 40, 384, 512
+    xq, xs = oracle.quant_act(si.activations(M, K))
+    wq, ws = oracle.quant_wblock(si.weights(N, K))
+    dec = np.array([float(decode_exact(c)) if c not in (0x7F, 0xFF) else np.nan for c in range(256)])
+    xd = dec[xq] * np.repeat(xs.astype(np.float64), 128, axis=1)
+    wd = dec[wq] * np.repeat(np.repeat(ws.astype(np.float64), 128, axis=0), 128, axis=1)
+    ref = xd @ wd.T
+    y = oracle.gemm(xq, xs, wq, ws)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    rows = np.array([0, 7, 39], np.int64)
+    assert np.array_equal(oracle.gemm(xq, xs, wq, ws, rows=rows), y[rows])
+
+
+def test_gemm_integer_special_case():
+    """Power-of-two scales and small-integer codes: Y is an exact int64 matmul."""
+    rng = np.random.default_rng(9)
+    M, N, K = 16, 256, 384
+    int_codes = {v: c for c, v in ((c, float(decode_exact(c))) for c in range(256) if c not in (0x7F, 0xFF))
+                 if float(v).is_integer() and abs(v) <= 16}
+    vals = np.array(sorted(int_codes))
+    xi = rng.choice(vals, (M, K))
+    wi = rng.choice(vals, (N, K))
+    xq = np.vectorize(int_codes.get)(xi).astype(np.uint8)
+    wq = np.vectorize(int_codes.get)(wi).astype(np.uint8)
+    xe = rng.integers(-3, 4, (M, K // 128))
+    we = rng.integers(-3, 4, (N // 128, K // 128))
+    xs = (2.0 ** xe).astype(np.float32)
+    ws = (2.0 ** we).astype(np.float32)
+    y = oracle.gemm(xq, xs, wq, ws)
+    # exact: scale everything by 2^6 to stay integral
+    ref = np.zeros((M, N), dtype=object)
+    xi64 = xi.astype(np.int64)
+    wi64 = wi.astype(np.int64)
+    for kb in range(K // 128):
+        p = xi64[:, kb * 128:(kb + 1) * 128] @ wi64[:, kb * 128:(kb + 1) * 128].T
+        sc = xe[:, kb][:, None] + np.repeat(we[:, kb], 128)[None, :]
+        ref = ref + np.vectorize(lambda a, e: Fraction(int(a)) * Fraction(2) ** int(e))(p, sc)
+    assert all(Fraction(y[m, n]) == ref[m, n] for m in range(M) for n in range(N))
+
+
+def test_gemm_block_identity():
+    """W = identity blocks with code 1.0 and scale 1: Y equals dequantized X."""
+    M, K = 8, 256
+    xq, xs = oracle.quant_act(si.activations(M, K))
+    wq = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(wq, 0x38)   # 1.0
+    ws = np.ones((K // 128, K // 128), np.float32)
+    y = oracle.gemm(xq, xs, wq, ws)
+    dec = oracle.e4m3_decode_table()
+    ref = dec[xq] * np.repeat(xs.astype(np.float64), 128, axis=1)
+    assert np.array_equal(y, ref)
+    # and the scale of W's block row scales the matching outputs only
+    ws2 = ws.copy()
+    ws2[1, :] = 2.0
+    y2 = oracle.gemm(xq, xs, wq, ws2)
+    assert np.array_equal(y2[:, :128], ref[:, :128]) and np.array_equal(y2[:, 128:], 2 * ref[:, 128:])
+
+
+def test_sparse_gemm_equals_dense_on_decompressed():
+    M, N, K = 16, 256, 512
+    xq, xs = oracle.quant_act(si.activations(M, K))
+    w = si.weights(N, K)
+    vals, meta, s = oracle.prune24_compress(w)
+    y = oracle.sparse24_gemm(xq, xs, vals, meta, s)
+    keep = oracle.prune24_mask(w)
+    wq, ws = oracle.quant_wblock(np.where(keep, w, np.uint16(0)).astype(np.uint16))
+    assert np.array_equal(y, oracle.gemm(xq, xs, wq, ws))
