@@ -64,28 +64,34 @@ double oracle_e4m3_decode(uint8_t c) {
     return S ? -v : v;
 }
 
+/* The 127 non-negative finite values in increasing order (codes 0x00..0x7E). */
+static double e4m3_pos[127];
+
+__attribute__((constructor)) static void init_e4m3_table(void) {
+    for (int c = 0; c < 127; c++) e4m3_pos[c] = oracle_e4m3_decode((uint8_t)c);
+}
+
 /*
  * Encode a real value (given as a double) to E4M3FN, round to nearest with
- * ties to the even code, saturating.  The 127 non-negative finite values are
- * walked in increasing order; the input is placed between two neighbours and
- * compared with their midpoint (midpoints have 5 significant bits, so they and
- * the comparison are exact in double).
+ * ties to the even code, saturating.  A bisection over the 127 non-negative
+ * finite values finds the neighbours lo <= |v| <= hi; |v| is then compared
+ * with their midpoint (midpoints have 5 significant bits, so they and the
+ * comparison are exact in double).
  */
 uint8_t oracle_e4m3_encode(double v) {
     uint8_t S = signbit(v) ? 0x80 : 0x00;
     double a = fabs(v);
     if (isnan(v)) return S | 0x7F;
-    if (a > 448.0) return S | 0x7E;
-    for (int c = 0; c < 126; c++) {
-        double lo = oracle_e4m3_decode((uint8_t)c);
-        double hi = oracle_e4m3_decode((uint8_t)(c + 1));
-        if (a > hi) continue;
-        double mid = (lo + hi) / 2.0;
-        if (a < mid) return S | (uint8_t)c;
-        if (a > mid) return S | (uint8_t)(c + 1);
-        return S | (uint8_t)((c % 2 == 0) ? c : c + 1); /* tie: even code */
+    if (a >= 448.0) return S | 0x7E;
+    int lo = 0, hi = 126; /* invariant: e4m3_pos[lo] <= a < e4m3_pos[hi] */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (e4m3_pos[mid] <= a) lo = mid; else hi = mid;
     }
-    return S | 0x7E; /* a == 448 */
+    double m = (e4m3_pos[lo] + e4m3_pos[hi]) / 2.0;
+    if (a < m) return S | (uint8_t)lo;
+    if (a > m) return S | (uint8_t)hi;
+    return S | (uint8_t)((lo % 2 == 0) ? lo : hi); /* tie: even code */
 }
 
 /* The value of one input divided by its scale, then encoded. */
@@ -103,6 +109,7 @@ static uint8_t quantize_one(float x, float s) {
  */
 void oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s) {
     int64_t KB = K / G;
+#pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; m++) {
         for (int64_t kb = 0; kb < KB; kb++) {
             float amax = 0.0f;
@@ -126,6 +133,7 @@ void oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float
  */
 void oracle_quant_wblock(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s) {
     int64_t NB = N / G, KB = K / G;
+#pragma omp parallel for schedule(static)
     for (int64_t nb = 0; nb < NB; nb++) {
         for (int64_t kb = 0; kb < KB; kb++) {
             float amax = 0.0f;
@@ -153,6 +161,7 @@ void oracle_quant_wblock(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, fl
  * and the first two are kept.  keep [N,K] receives 1 for kept, 0 for dropped.
  */
 void oracle_prune24_mask(const uint16_t *w, const float *c, int64_t N, int64_t K, uint8_t *keep) {
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; n++) {
         for (int64_t g = 0; g < K / 4; g++) {
             double sc[4];
@@ -188,6 +197,7 @@ void oracle_prune24_compress(const uint16_t *w, const float *c, int64_t N, int64
     uint8_t *keep = (uint8_t *)malloc((size_t)(N * K));
     oracle_prune24_mask(w, c, N, K, keep);
     /* block scales over the pruned matrix (dropped entries are zero) */
+#pragma omp parallel for schedule(static)
     for (int64_t nb = 0; nb < NB; nb++)
         for (int64_t kb = 0; kb < KB; kb++) {
             float amax = 0.0f;
@@ -199,6 +209,7 @@ void oracle_prune24_compress(const uint16_t *w, const float *c, int64_t N, int64
             s[nb * KB + kb] = amax / 448.0f;
         }
     memset(meta, 0, (size_t)(N * K / 8));
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; n++)
         for (int64_t g = 0; g < K / 4; g++) {
             float sc = s[(n / G) * KB + (4 * g) / G];
