@@ -1,0 +1,141 @@
+/*
+ * fp8lin: FP8 block-scaled and 2:4-sparse FP8 linear layers for AMD MI355X (gfx950).
+ *
+ * C ABI.  All tensors are dense, row-major and contiguous in device memory.
+ * bf16 values are passed as their raw 16-bit patterns (uint16_t).  FP8 codes
+ * are OCP E4M3FN bytes (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * no infinities, 0x7F/0xFF = NaN, largest finite 448), view-compatible with
+ * torch.float8_e4m3fn.  Scales are fp32.  G = 128 is the group / block edge.
+ *
+ * Ownership: the caller allocates every input and output; the library never
+ * allocates, frees or keeps a pointer after a call returns, keeps no state
+ * between calls besides a per-device architecture check, and needs no
+ * workspace.  Calls may be made from several host threads on different
+ * streams.
+ *
+ * Asynchrony: each call validates its arguments on the host, enqueues its
+ * kernels on `stream` (NULL = the default stream) and returns without
+ * synchronising.  A fault inside a kernel surfaces at the caller's next
+ * synchronisation, as for any HIP launch.
+ *
+ * Errors: on any error nothing is enqueued and every output is left untouched.
+ *   FP8L_ERR_NULL    a required pointer is NULL;
+ *   FP8L_ERR_SHAPE   M < 0, N <= 0, K <= 0, K % 128 != 0, N % 128 != 0, or a
+ *                    dimension above 2^24, or a matrix above 2^36 elements;
+ *   FP8L_ERR_ALIGN   a pointer is not 16-byte aligned;
+ *   FP8L_ERR_ALIAS   an output overlaps an input or another output;
+ *   FP8L_ERR_DEVICE  the current HIP device is missing or is not gfx950;
+ *   FP8L_ERR_LAUNCH  the kernel launch was rejected by the runtime.
+ * M == 0 (an empty batch) returns FP8L_OK without launching and without
+ * looking at the M-sized buffers.  There is no fallback path: an unsupported
+ * case is an error, never a silently slower kernel.
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int fp8l_status;
+enum {
+    FP8L_OK = 0,
+    FP8L_ERR_NULL = 1,
+    FP8L_ERR_SHAPE = 2,
+    FP8L_ERR_ALIGN = 3,
+    FP8L_ERR_ALIAS = 4,
+    FP8L_ERR_DEVICE = 5,
+    FP8L_ERR_LAUNCH = 6
+};
+
+/*
+ * Dynamic per-token activation quantization in 1x128 groups ("FP8 a
+ * granularite fine", transformers docs: intro bullets, activations quantized
+ * per token in groups of 128 input channels; section "Chemin rapide de
+ * DeepGEMM": dynamic activation scheme).
+ *
+ *   x [M,K] bf16            activations, one token per row
+ *   q [M,K] e4m3            q[m,k] = enc(fp32(x[m,k] / s[m,k/128]))
+ *   s [M,K/128] fp32        s[m,kb] = fp32(amax / 448), amax = max |x[m,k]| over
+ *                           the 128 channels of group kb; amax == 0 gives s = 0
+ *                           and signed-zero codes
+ * enc() rounds to nearest, ties to even, and saturates at +-448; both divisions
+ * are IEEE fp32 divisions.
+ */
+fp8l_status fp8_quant_act(const uint16_t *x, int64_t M, int64_t K,
+                          uint8_t *q, float *s, hipStream_t stream);
+
+/*
+ * Weight quantization in 128x128 blocks ("FP8 a granularite fine", intro
+ * bullets: weight_block_size = (128, 128)).  W is nn.Linear.weight [N,K]
+ * (K contiguous).
+ *
+ *   w [N,K] bf16
+ *   q [N,K] e4m3            q[n,k] = enc(fp32(w[n,k] / s[n/128,k/128]))
+ *   s [N/128,K/128] fp32    s = fp32(amax / 448), amax over the 128x128 block
+ */
+fp8l_status fp8_quant_weight_block(const uint16_t *w, int64_t N, int64_t K,
+                                   uint8_t *q, float *s, hipStream_t stream);
+
+/*
+ * 2:4 pruning along K, post-prune block scales and compression ("Deployer la
+ * parcimonie 2:4 avec FP8 sur Hopper": pipeline step 2, groups of 4
+ * contiguous values along K; step 4, magnitude or activation-aware scores,
+ * the two least important of every 4 dropped; step 6, FP8 scales re-derived
+ * after pruning; step 7, pruned weights exported with their 2:4 masks.
+ * "Combiner elagage et quantification", section "La cle": keep the two
+ * largest of every four).
+ *
+ *   w [N,K] bf16
+ *   col_norm [K] fp32 or NULL   score of w[n,k] = |w[n,k]| * col_norm[k]
+ *                               (activation-aware), or |w[n,k]| when NULL
+ *                               (magnitude); the product is compared exactly
+ *   vals [N,K/2] e4m3           the two kept codes of each group, lower index first
+ *   meta [N,K/8] u8             2-bit positions: group g of row n has nibble
+ *                               i0 | (i1 << 2) (i0 < i1 the kept positions) at
+ *                               bits 4*(g%2) .. 4*(g%2)+3 of meta[n, g/2]
+ *   s [N/128,K/128] fp32        fp32(amax / 448), amax over the kept values of
+ *                               the block; kept codes = enc(fp32(w / s))
+ * Each group keeps exactly two positions, the two largest scores; equal scores
+ * keep the lower index.
+ */
+fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N, int64_t K,
+                             uint8_t *vals, uint8_t *meta, float *s, hipStream_t stream);
+
+/*
+ * Block-scaled FP8 GEMM with fp32 accumulation ("FP8 a granularite fine",
+ * section "Chemin rapide de DeepGEMM": every FP8 linear with (128,128) weight
+ * blocks and dynamic activations runs as a block-scaled FP8 GEMM).
+ *
+ *   xq [M,K] e4m3, xs [M,K/128] fp32       from fp8_quant_act
+ *   wq [N,K] e4m3, ws [N/128,K/128] fp32   from fp8_quant_weight_block
+ *   y [M,N] bf16   y[m,n] = bf16_rne( sum_kb xs[m,kb] * ws[n/128,kb] *
+ *                                     sum_{k in kb} dec(xq[m,k]) * dec(wq[n,k]) )
+ * The inner block sums are exact FP8 products accumulated in fp32.
+ */
+fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                           int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+
+/*
+ * The same GEMM with a 2:4-compressed weight from prune24_compress ("Deployer
+ * la parcimonie 2:4 avec FP8 sur Hopper", introduction and performance notes:
+ * 2:4 GEMMs run on the sparse matrix units; here the sparse MFMA of gfx950).
+ * The pruned positions contribute zero.
+ *
+ *   wvals [N,K/2] e4m3, wmeta [N,K/8], ws [N/128,K/128] fp32
+ */
+fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t *wvals,
+                              const uint8_t *wmeta, const float *ws, int64_t M, int64_t N,
+                              int64_t K, uint16_t *y, hipStream_t stream);
+
+/* Static, never NULL, English text for a status code. */
+const char *fp8lin_status_str(fp8l_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LIN_H */

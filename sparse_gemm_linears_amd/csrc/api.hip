@@ -1,0 +1,162 @@
+// C entry points: host-side validation, then one launch on the caller's stream.
+// Validation order: NULL pointers, shapes, alignment, aliasing, device.  No
+// call enqueues anything before every check has passed.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/fp8lin.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 = unknown, 1 = gfx950, 2 = other
+
+struct Range {
+  const void *p;
+  int64_t bytes;
+};
+
+bool overlaps(const Range &a, const Range &b) {
+  if (a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Every output range against every input range and every other output range.
+bool any_alias(const Range *outs, int n_out, const Range *ins, int n_in) {
+  for (int i = 0; i < n_out; i++) {
+    for (int j = 0; j < n_in; j++)
+      if (overlaps(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < n_out; j++)
+      if (overlaps(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+fp8l_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return FP8L_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (known) return known == 1 ? FP8L_OK : FP8L_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8L_ERR_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FP8L_OK : FP8L_ERR_DEVICE;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 36;  // keeps every grid and index in range
+
+bool bad_mk(int64_t M, int64_t K) {
+  return M < 0 || K <= 0 || K % 128 != 0 || M > kMaxDim || K > kMaxDim || M * K > kMaxElems;
+}
+bool bad_nk(int64_t N, int64_t K) {
+  return N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0 || N > kMaxDim || K > kMaxDim || N * K > kMaxElems;
+}
+bool bad_mn(int64_t M, int64_t N) { return M * N > kMaxElems; }
+
+fp8l_status launched(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8L_ERR_LAUNCH;
+  }
+  return FP8L_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8l_status fp8_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, hipStream_t stream) {
+  if (bad_mk(M, K)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!x || !q || !s) return FP8L_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{x, M * K * 2}};
+  const Range outs[] = {{q, M * K}, {s, M * (K / 128) * 4}};
+  if (any_alias(outs, 2, ins, 1)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_quant_act(x, M, K, q, s, stream));
+}
+
+fp8l_status fp8_quant_weight_block(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
+                                   hipStream_t stream) {
+  if (bad_nk(N, K)) return FP8L_ERR_SHAPE;
+  if (!w || !q || !s) return FP8L_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{w, N * K * 2}};
+  const Range outs[] = {{q, N * K}, {s, (N / 128) * (K / 128) * 4}};
+  if (any_alias(outs, 2, ins, 1)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_quant_wblock(w, N, K, q, s, stream));
+}
+
+fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N, int64_t K, uint8_t *vals,
+                             uint8_t *meta, float *s, hipStream_t stream) {
+  if (bad_nk(N, K)) return FP8L_ERR_SHAPE;
+  if (!w || !vals || !meta || !s) return FP8L_ERR_NULL;
+  if (!aligned16(w) || !aligned16(vals) || !aligned16(meta) || !aligned16(s) ||
+      (col_norm && !aligned16(col_norm)))
+    return FP8L_ERR_ALIGN;
+  const Range ins[] = {{w, N * K * 2}, {col_norm, col_norm ? K * 4 : 0}};
+  const Range outs[] = {{vals, N * K / 2}, {meta, N * K / 8}, {s, (N / 128) * (K / 128) * 4}};
+  if (any_alias(outs, 3, ins, 2)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_prune24(w, col_norm, N, K, vals, meta, s, stream));
+}
+
+fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
+                           int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!xq || !xs || !wq || !ws || !y) return FP8L_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{xq, M * K}, {xs, M * (K / 128) * 4}, {wq, N * K}, {ws, (N / 128) * (K / 128) * 4}};
+  const Range outs[] = {{y, M * N * 2}};
+  if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_dense_gemm(xq, xs, wq, ws, M, N, K, y, stream));
+}
+
+fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t *wvals, const uint8_t *wmeta,
+                              const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!xq || !xs || !wvals || !wmeta || !ws || !y) return FP8L_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wvals) || !aligned16(wmeta) || !aligned16(ws) ||
+      !aligned16(y))
+    return FP8L_ERR_ALIGN;
+  const Range ins[] = {{xq, M * K},        {xs, M * (K / 128) * 4}, {wvals, N * K / 2},
+                       {wmeta, N * K / 8}, {ws, (N / 128) * (K / 128) * 4}};
+  const Range outs[] = {{y, M * N * 2}};
+  if (any_alias(outs, 1, ins, 5)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_sparse_gemm(xq, xs, wvals, wmeta, ws, M, N, K, y, stream));
+}
+
+const char *fp8lin_status_str(fp8l_status status) {
+  switch (status) {
+    case FP8L_OK: return "ok";
+    case FP8L_ERR_NULL: return "a required pointer is NULL";
+    case FP8L_ERR_SHAPE: return "unsupported shape (K and N must be positive multiples of 128, M >= 0, each <= 2^24)";
+    case FP8L_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FP8L_ERR_ALIAS: return "an output overlaps an input or another output";
+    case FP8L_ERR_DEVICE: return "no gfx950 (MI355X) device is current";
+    case FP8L_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

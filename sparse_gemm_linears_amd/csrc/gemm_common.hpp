@@ -1,0 +1,101 @@
+// Pieces shared by the dense and 2:4 sparse block-scaled GEMM kernels.
+//
+// Operand K layout inside one 128-wide K block (both GEMMs): lane group
+// g = lane/16 holds K bytes [16g, 16g+16) in register bytes 0..15 and
+// [64+16g, 64+16g+16) in bytes 16..31.  For the dense FP8 MFMA any layout
+// shared by A and B is correct; this one is the layout the sparse MFMA
+// expects of its dense operand when the compressed operand of lane group g
+// covers the 8 groups of 4 at K = [32g, 32g+32) (16 contiguous value bytes
+// and one 32-bit index word of the compressed weight).
+//
+// Output layout of a 16x16 MFMA with A = weight rows (n) and B = tokens (m):
+// lane l holds token m = l%16 and rows n = 4*(l/16) .. +3.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace fp8lin {
+
+__device__ __forceinline__ v8i make_v8i(const uint4 &lo, const uint4 &hi) {
+  v8i r;
+  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  return r;
+}
+
+__device__ __forceinline__ v4i make_v4i(const uint4 &v) {
+  v4i r;
+  r[0] = (int)v.x; r[1] = (int)v.y; r[2] = (int)v.z; r[3] = (int)v.w;
+  return r;
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// Dense operand fragment of one 128-wide K block straight from global memory:
+// `row` points at the first byte of the K block of this lane's row.
+__device__ __forceinline__ v8i load_frag_global(const uint8_t *row, int g) {
+  return make_v8i(ldg16(row + 16 * g), ldg16(row + 64 + 16 * g));
+}
+
+// LDS tiles hold rows of 128 bytes as eight 16-byte chunks; chunk c of row r
+// sits at chunk position c ^ swz(r).  swz depends on r % 16 only and permutes
+// the chunks of any 8 aligned consecutive rows, and across 16 aligned rows
+// those of the even and of the odd rows, so 16-lane fragment reads of one
+// chunk column hit distinct banks whether the LDS serves 128 or 256 bytes per
+// cycle.  Depending on r % 16 only lets a fragment row r = 16*t + l%16 use one
+// per-lane address plus a compile-time offset 2048*t.
+__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+
+// Fragment read at precomputed per-lane byte offsets (lo, hi chunk) plus a
+// compile-time displacement.
+__device__ __forceinline__ v8i load_frag_at(const uint8_t *lds_base, int lo, int hi, int disp) {
+  const uint4 a = *reinterpret_cast<const uint4 *>(lds_base + lo + disp);
+  const uint4 b = *reinterpret_cast<const uint4 *>(lds_base + hi + disp);
+  return make_v8i(a, b);
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4).
+// The 64 lanes of a wave write 1 KB of LDS at `lds_wave_base` in lane order
+// (lane l at +16*l); each lane supplies its own global source address.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+__device__ __forceinline__ void copy16_global_to_lds(const void *src, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void *)const_cast<void *>(src), (lds_void *)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until this wave's outstanding global loads (the LDS copies included)
+// have landed.
+__device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Pins a value in VGPRs at this point of the program: the computation that
+// produces it cannot be sunk below the pin (keeps the partial-product scaling
+// next to its MFMAs instead of piling up live partials).
+__device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
+
+// Pack four fp32 accumulators into four bf16 (RNE) for one 8-byte store.
+__device__ __forceinline__ uint2 pack_bf16x4(const v4f &v) {
+  return make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                    f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+}
+
+// Tile order.  Workgroups are dealt to the 8 XCDs round-robin (block b runs on
+// XCD b % 8), each XCD with its own L2.  The remap gives every XCD one
+// contiguous range of logical tile ids; the logical order then walks groups of
+// `group_m` token tiles column by column, so an XCD's concurrent tiles share
+// weight and activation panels in its L2.
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
+  const int total = tiles_m * tiles_n;
+  const int q = total / 8, r = total % 8;
+  const int xcd = b % 8, local = b / 8;
+  const int logical = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int per_group = group_m * tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int in_group = logical % per_group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
+
+}  // namespace fp8lin

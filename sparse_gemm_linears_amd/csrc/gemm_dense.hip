@@ -1,0 +1,319 @@
+// Dense block-scaled FP8 GEMM:  y[m,n] = bf16( sum_kb xs[m,kb] * ws[n/128,kb] * P(m,n,kb) ),
+// P = the exact FP8 dot product over one 128-wide K block, accumulated in fp32 by
+// v_mfma_f32_16x16x128_f8f6f4 (one instruction per 16x16 output tile and K block).
+//
+// The weight is MFMA operand A (rows = n) and the activations operand B
+// (columns = m), so one lane's four results share a token m and a weight block
+// row: the scale of a 16x16 partial is one fp32 product per lane, applied with
+// four FMAs into the running fp32 accumulator.
+//
+// Two kernels:
+//  * tile kernel (large M): BN x BM output tile per workgroup, 128-wide K steps
+//    staged through double-buffered, swizzled LDS, one barrier per step;
+//  * decode kernel (M <= 64): the weight streams from HBM straight into MFMA
+//    registers, the waves of a workgroup split K and meet in LDS at the end.
+#include <type_traits>
+
+#include "gemm_common.hpp"
+#include "launch.hpp"
+
+namespace fp8lin {
+
+// ============================================================== tile kernel ==
+
+template <int BN, int BM, int WN, int WM>
+struct DenseTile {
+  static constexpr int kWaves = WN * WM, kThreads = kWaves * 64;
+  static constexpr int kWaveN = BN / WN, kWaveM = BM / WM;
+  static constexpr int RT = kWaveN / 16, CT = kWaveM / 16;
+  static constexpr int kACopies = BN / 8 / kWaves, kBCopies = BM / 8 / kWaves;  // 1 KB = 8 rows per copy
+  static constexpr int kATile = BN * 128, kBTile = BM * 128;
+  static_assert(BN % (8 * kWaves) == 0 && BM % (8 * kWaves) == 0, "tile / wave mismatch");
+  static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
+  static_assert(kWaveN <= 128 && 128 % kWaveN == 0, "a wave's rows must sit in one 128-row scale block");
+  static_assert(BM <= kThreads, "one thread per token scale");
+};
+
+template <int BN, int BM, int WN, int WM>
+__global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *__restrict__ xq,
+                                                                const float *__restrict__ xs,
+                                                                const uint8_t *__restrict__ wq,
+                                                                const float *__restrict__ ws, int M, int N,
+                                                                int K, uint16_t *__restrict__ y, int tiles_m,
+                                                                int tiles_n, int group_m) {
+  using C = DenseTile<BN, BM, WN, WM>;
+  // One LDS object per stage and panel: copies into one stage and fragment
+  // reads of the other are then known not to overlap, so reads never wait for
+  // the copies in flight.
+  __shared__ __align__(16) uint8_t lds_a0[C::kATile], lds_a1[C::kATile];
+  __shared__ __align__(16) uint8_t lds_b0[C::kBTile], lds_b1[C::kBTile];
+  __shared__ float lds_s0[BM], lds_s1[BM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, lr = lane & 15;
+  const int cj = lane >> 3, cp = lane & 7;  // copy lane -> (row in an 8-row slab, chunk position)
+  const int KB = K / kGroup, NB = N / kGroup;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  const int m_base = tm * BM, n_base = tn * BN;
+  const int wn0 = (wave / WM) * C::kWaveN, wm0 = (wave % WM) * C::kWaveM;
+
+  // Copy slab i of this wave covers tile rows r0 = (i*kWaves + wave)*8 .. +7;
+  // lane (cj, cp) writes LDS chunk position cp of row r0+cj, i.e. logical
+  // chunk cp ^ swz(r0+cj); r0 % 16 = 8*(wave % 2) for every i.
+  const int copy_chunk = 16 * (cp ^ swz(cj + 8 * (wave & 1)));
+  const uint32_t a_lane = (uint32_t)(cj * K + copy_chunk);
+  uint32_t b_lane[C::kBCopies];
+#pragma unroll
+  for (int i = 0; i < C::kBCopies; i++) {
+    const int r0 = m_base + (i * C::kWaves + wave) * 8;
+    b_lane[i] = (uint32_t)((min(r0 + cj, M - 1) - min(r0, M - 1)) * K + copy_chunk);
+  }
+  const float *s_src = xs + (int64_t)min(m_base + min(tid, BM - 1), M - 1) * KB;
+  float s_reg = 0.0f;
+
+  // One 128-wide K block of the weight and token panels into LDS stage `st`.
+  // Rows past the matrix edge re-read valid rows; their results are never stored.
+  auto issue_copies = [&](int kb, int st) {
+    const int64_t koff = (int64_t)kb * kGroup;
+#pragma unroll
+    for (int i = 0; i < C::kACopies; i++) {
+      const int r0 = (i * C::kWaves + wave) * 8;
+      const uint8_t *base = wq + (int64_t)min(n_base + r0, N - 8) * K + koff;
+      copy16_global_to_lds(base + a_lane, (st ? lds_a1 : lds_a0) + r0 * 128);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kBCopies; i++) {
+      const int r0 = (i * C::kWaves + wave) * 8;
+      const uint8_t *base = xq + (int64_t)min(m_base + r0, M - 1) * K + koff;
+      copy16_global_to_lds(base + b_lane[i], (st ? lds_b1 : lds_b0) + r0 * 128);
+    }
+    if (tid < BM) s_reg = s_src[kb];
+  };
+  auto store_scales = [&](int st) {
+    if (tid < BM) (st ? lds_s1 : lds_s0)[tid] = s_reg;
+  };
+
+  // per-lane fragment read offsets (row lr of a 16-row slab, chunks g and g+4)
+  const int fr_lo = lr * 128 + ((g ^ swz(lr)) << 4);
+  const int fr_hi = lr * 128 + (((g + 4) ^ swz(lr)) << 4);
+  const int a_lo = wn0 * 128 + fr_lo, a_hi = wn0 * 128 + fr_hi;
+  const int b_lo = wm0 * 128 + fr_lo, b_hi = wm0 * 128 + fr_hi;
+
+  v4f acc[C::RT][C::CT];
+#pragma unroll
+  for (int r = 0; r < C::RT; r++)
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int nb_wave = min((n_base + wn0) / kGroup, NB - 1);
+  const float *ws_row = ws + (int64_t)nb_wave * KB;
+
+  // One K step on stage ST: the next block's copies are in flight while the
+  // MFMAs of this one run.  Partials of row tile r are scaled into the
+  // accumulators while the MFMAs of row tile r+1 execute.
+  auto step = [&](int kb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    const bool more = kb + 1 < KB;
+    if (more) issue_copies(kb + 1, ST ^ 1);
+    const float sw = ws_row[kb];
+    v8i bf[C::CT];
+    float scl[C::CT];
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) {
+      bf[c] = load_frag_at(ST ? lds_b1 : lds_b0, b_lo, b_hi, c * 2048);
+      scl[c] = (ST ? lds_s1 : lds_s0)[wm0 + 16 * c + lr] * sw;
+    }
+    const uint8_t *At = ST ? lds_a1 : lds_a0;
+    v8i af_next = load_frag_at(At, a_lo, a_hi, 0);
+    v4f p_prev[C::CT];
+#pragma unroll
+    for (int r = 0; r < C::RT; r++) {
+      const v8i af = af_next;
+      if (r + 1 < C::RT) af_next = load_frag_at(At, a_lo, a_hi, (r + 1) * 2048);
+      v4f p_cur[C::CT];
+#pragma unroll
+      for (int c = 0; c < C::CT; c++) p_cur[c] = mfma_16x16x128_fp8(af, bf[c], v4f{0.f, 0.f, 0.f, 0.f});
+      if (r > 0) {
+#pragma unroll
+        for (int c = 0; c < C::CT; c++) {
+          acc[r - 1][c] += scl[c] * p_prev[c];
+          pin(acc[r - 1][c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < C::CT; c++) p_prev[c] = p_cur[c];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) {
+      acc[C::RT - 1][c] += scl[c] * p_prev[c];
+      pin(acc[C::RT - 1][c]);
+    }
+    if (more) {
+      wait_global_loads();
+      store_scales(ST ^ 1);
+    }
+    __syncthreads();
+  };
+
+  issue_copies(0, 0);
+  wait_global_loads();
+  store_scales(0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; kb += 2) {
+    step(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{});
+  }
+
+#pragma unroll
+  for (int c = 0; c < C::CT; c++) {
+    const int m = m_base + wm0 + 16 * c + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int r = 0; r < C::RT; r++) {
+      const int n = n_base + wn0 + 16 * r + 4 * g;
+      if (n < N) *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = pack_bf16x4(acc[r][c]);
+    }
+  }
+}
+
+// ============================================================ decode kernel ==
+
+// RT row tiles of 16 weight rows per workgroup, CT column tiles of 16 tokens
+// (M <= 16*CT), NW waves splitting the K blocks round-robin.
+template <int RT, int CT, int NW>
+__global__ __launch_bounds__(NW * 64) void dense_decode_kernel(const uint8_t *__restrict__ xq,
+                                                               const float *__restrict__ xs,
+                                                               const uint8_t *__restrict__ wq,
+                                                               const float *__restrict__ ws, int M, int N, int K,
+                                                               uint16_t *__restrict__ y) {
+  static_assert(128 % (16 * RT) == 0, "a workgroup's rows must sit in one 128-row scale block");
+  __shared__ v4f red[NW > 1 ? NW - 1 : 1][RT * CT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, lr = lane & 15;
+  const int KB = K / kGroup;
+  const int n0 = blockIdx.x * 16 * RT;
+  const float *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
+
+  const uint8_t *wrow[RT];
+#pragma unroll
+  for (int r = 0; r < RT; r++) wrow[r] = wq + (int64_t)(n0 + 16 * r + lr) * K;
+  const uint8_t *xrow[CT];
+  const float *srow[CT];
+#pragma unroll
+  for (int c = 0; c < CT; c++) {
+    const int m = min(16 * c + lr, M - 1);
+    xrow[c] = xq + (int64_t)m * K;
+    srow[c] = xs + (int64_t)m * KB;
+  }
+
+  v4f acc[RT][CT];
+#pragma unroll
+  for (int r = 0; r < RT; r++)
+#pragma unroll
+    for (int c = 0; c < CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  v8i a_cur[RT], b_cur[CT];
+  float s_cur[CT], sw_cur = 0.f;
+  auto load = [&](int kb, v8i(&a)[RT], v8i(&b)[CT], float(&s)[CT], float &sw) {
+    const int64_t off = (int64_t)kb * kGroup;
+#pragma unroll
+    for (int r = 0; r < RT; r++) a[r] = load_frag_global(wrow[r] + off, g);
+#pragma unroll
+    for (int c = 0; c < CT; c++) {
+      b[c] = load_frag_global(xrow[c] + off, g);
+      s[c] = srow[c][kb];
+    }
+    sw = ws_row[kb];
+  };
+
+  int kb = wave;
+  if (kb < KB) load(kb, a_cur, b_cur, s_cur, sw_cur);
+  for (; kb < KB; kb += NW) {
+    v8i a_nxt[RT], b_nxt[CT];
+    float s_nxt[CT], sw_nxt = 0.f;
+    const bool more = kb + NW < KB;
+    if (more) load(kb + NW, a_nxt, b_nxt, s_nxt, sw_nxt);
+#pragma unroll
+    for (int c = 0; c < CT; c++) {
+      const float scl = s_cur[c] * sw_cur;
+#pragma unroll
+      for (int r = 0; r < RT; r++) {
+        const v4f p = mfma_16x16x128_fp8(a_cur[r], b_cur[c], v4f{0.f, 0.f, 0.f, 0.f});
+        acc[r][c] += scl * p;
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < RT; r++) a_cur[r] = a_nxt[r];
+#pragma unroll
+      for (int c = 0; c < CT; c++) {
+        b_cur[c] = b_nxt[c];
+        s_cur[c] = s_nxt[c];
+      }
+      sw_cur = sw_nxt;
+    }
+  }
+
+  if (NW > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int r = 0; r < RT; r++)
+#pragma unroll
+        for (int c = 0; c < CT; c++) red[wave - 1][r * CT + c][lane] = acc[r][c];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < NW - 1; w++)
+#pragma unroll
+      for (int r = 0; r < RT; r++)
+#pragma unroll
+        for (int c = 0; c < CT; c++) acc[r][c] += red[w][r * CT + c][lane];
+  }
+#pragma unroll
+  for (int c = 0; c < CT; c++) {
+    const int m = 16 * c + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int r = 0; r < RT; r++) {
+      const int n = n0 + 16 * r + 4 * g;
+      *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = pack_bf16x4(acc[r][c]);
+    }
+  }
+}
+
+// ================================================================ dispatch ==
+
+template <int BN, int BM, int WN, int WM>
+static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int M, int N,
+                              int K, uint16_t *y, hipStream_t stream) {
+  using C = DenseTile<BN, BM, WN, WM>;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0, stream, xq,
+                     xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4);
+  return hipGetLastError();
+}
+
+template <int RT, int CT, int NW>
+static hipError_t launch_decode(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int M, int N,
+                                int K, uint16_t *y, hipStream_t stream) {
+  hipLaunchKernelGGL((dense_decode_kernel<RT, CT, NW>), dim3(N / (16 * RT)), dim3(NW * 64), 0, stream, xq, xs, wq,
+                     ws, M, N, K, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
+                             int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (m <= 16) return launch_decode<1, 1, 8>(xq, xs, wq, ws, m, n, k, y, stream);
+  if (m <= 32) return launch_decode<1, 2, 8>(xq, xs, wq, ws, m, n, k, y, stream);
+  if (m <= 64) return launch_decode<1, 4, 8>(xq, xs, wq, ws, m, n, k, y, stream);
+  return launch_tile<256, 256, 2, 4>(xq, xs, wq, ws, m, n, k, y, stream);
+}
+
+}  // namespace fp8lin

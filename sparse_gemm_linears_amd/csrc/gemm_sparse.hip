@@ -1,0 +1,354 @@
+// 2:4 sparse block-scaled FP8 GEMM on the gfx950 sparse MFMA
+// (v_smfmac_f32_16x16x128_fp8_fp8): the compressed weight is operand A
+// (16 rows x 64 kept values per 128-wide K block, plus one 32-bit index word
+// per lane), the activations the dense operand B.
+//
+// Lane l of A (row l%16, lane group g = l/16) holds the 16 value bytes of
+// groups 8g .. 8g+7 of the K block, i.e. vals[n, 64*kb + 16g .. +15], and the
+// index word meta[n, 16*kb + 4g .. +3] read as a little-endian uint32: group
+// 8g+j has its nibble i0 | i1 << 2 at bits 4j .. 4j+3, which is exactly the
+// packed form prune24_compress writes.  B follows the shared dense layout
+// (K bytes [16g, 16g+16) and [64+16g, 64+16g+16)).
+//
+// Scale handling, tiling and the two kernels (tile for large M, decode for
+// M <= 64) mirror the dense GEMM.
+#include <type_traits>
+
+#include "gemm_common.hpp"
+#include "launch.hpp"
+
+namespace fp8lin {
+
+__device__ __forceinline__ v4f smfmac_16x16x128_fp8(const v4i &a, const v8i &b, int idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, v4f{0.f, 0.f, 0.f, 0.f}, idx, 0, 0);
+}
+
+// LDS row of 64 value bytes = four 16-byte chunks; chunk c of row r sits at
+// position c ^ vswz(r).  vswz depends on r % 16 only and spreads the 16-lane
+// reads of one chunk column of 16 aligned rows (or of 8 aligned rows) over
+// distinct banks for 256- and 128-byte-per-cycle LDS alike.
+__device__ __forceinline__ int vswz(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
+
+// ============================================================== tile kernel ==
+
+template <int BN, int BM, int WN, int WM>
+struct SparseTile {
+  static constexpr int kWaves = WN * WM, kThreads = kWaves * 64;
+  static constexpr int kWaveN = BN / WN, kWaveM = BM / WM;
+  static constexpr int RT = kWaveN / 16, CT = kWaveM / 16;
+  // per K block: values 64 B/row (1 KB copy = 16 rows), index words 16 B/row
+  // (1 KB copy = 64 rows), tokens 128 B/row (1 KB copy = 8 rows)
+  static constexpr int kVCopies = BN / 16 / kWaves, kBCopies = BM / 8 / kWaves;
+  static constexpr int kMCopyWaves = BN / 64;
+  static constexpr int kVTile = BN * 64, kMTile = BN * 16, kBTile = BM * 128;
+  static_assert(BN % (16 * kWaves) == 0 && BM % (8 * kWaves) == 0 && kMCopyWaves <= kWaves, "tile mismatch");
+  static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
+  static_assert(kWaveN <= 128 && 128 % kWaveN == 0, "a wave's rows must sit in one 128-row scale block");
+  static_assert(BM <= kThreads, "one thread per token scale");
+};
+
+template <int BN, int BM, int WN, int WM>
+__global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t *__restrict__ xq,
+                                                                 const float *__restrict__ xs,
+                                                                 const uint8_t *__restrict__ wv,
+                                                                 const uint8_t *__restrict__ wm,
+                                                                 const float *__restrict__ ws, int M, int N, int K,
+                                                                 uint16_t *__restrict__ y, int tiles_m,
+                                                                 int tiles_n, int group_m) {
+  using C = SparseTile<BN, BM, WN, WM>;
+  // one LDS object per stage and panel (see the dense tile kernel)
+  __shared__ __align__(16) uint8_t lds_v0[C::kVTile], lds_v1[C::kVTile];
+  __shared__ __align__(16) uint8_t lds_m0[C::kMTile], lds_m1[C::kMTile];
+  __shared__ __align__(16) uint8_t lds_b0[C::kBTile], lds_b1[C::kBTile];
+  __shared__ float lds_s0[BM], lds_s1[BM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, lr = lane & 15;
+  const int cj = lane >> 3, cp = lane & 7;
+  const int KB = K / kGroup, NB = N / kGroup;
+  const int64_t vrow_bytes = K / 2, mrow_bytes = K / 8;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  const int m_base = tm * BM, n_base = tn * BN;
+  const int wn0 = (wave / WM) * C::kWaveN, wm0 = (wave % WM) * C::kWaveM;
+
+  // value copies: slab i covers rows r0 = (i*kWaves + wave)*16 .. +15, lane l
+  // writes chunk position l%4 of row r0 + l/4 (logical chunk (l%4) ^ vswz(row))
+  const int vrow_in_slab = lane >> 2, vpos = lane & 3;
+  const uint32_t v_lane = (uint32_t)(vrow_in_slab * vrow_bytes + 16 * (vpos ^ vswz(vrow_in_slab)));
+  // index-word copies: one 64-row slab per wave for waves < kMCopyWaves
+  const uint32_t m_lane = (uint32_t)(lane * mrow_bytes);
+  // token copies as in the dense kernel
+  const int copy_chunk = 16 * (cp ^ swz(cj + 8 * (wave & 1)));
+  uint32_t b_lane[C::kBCopies];
+#pragma unroll
+  for (int i = 0; i < C::kBCopies; i++) {
+    const int r0 = m_base + (i * C::kWaves + wave) * 8;
+    b_lane[i] = (uint32_t)((min(r0 + cj, M - 1) - min(r0, M - 1)) * K + copy_chunk);
+  }
+  const float *s_src = xs + (int64_t)min(m_base + min(tid, BM - 1), M - 1) * KB;
+  float s_reg = 0.0f;
+
+  auto issue_copies = [&](int kb, int st) {
+#pragma unroll
+    for (int i = 0; i < C::kVCopies; i++) {
+      const int r0 = (i * C::kWaves + wave) * 16;
+      const uint8_t *base = wv + (int64_t)min(n_base + r0, N - 16) * vrow_bytes + (int64_t)kb * 64;
+      copy16_global_to_lds(base + v_lane, (st ? lds_v1 : lds_v0) + r0 * 64);
+    }
+    if (wave < C::kMCopyWaves) {
+      const int r0 = wave * 64;
+      const uint8_t *base = wm + (int64_t)min(n_base + r0, N - 64) * mrow_bytes + (int64_t)kb * 16;
+      copy16_global_to_lds(base + m_lane, (st ? lds_m1 : lds_m0) + r0 * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kBCopies; i++) {
+      const int r0 = (i * C::kWaves + wave) * 8;
+      const uint8_t *base = xq + (int64_t)min(m_base + r0, M - 1) * K + (int64_t)kb * kGroup;
+      copy16_global_to_lds(base + b_lane[i], (st ? lds_b1 : lds_b0) + r0 * 128);
+    }
+    if (tid < BM) s_reg = s_src[kb];
+  };
+  auto store_scales = [&](int st) {
+    if (tid < BM) (st ? lds_s1 : lds_s0)[tid] = s_reg;
+  };
+
+  const int fr_lo = lr * 128 + ((g ^ swz(lr)) << 4);
+  const int fr_hi = lr * 128 + (((g + 4) ^ swz(lr)) << 4);
+  const int b_lo = wm0 * 128 + fr_lo, b_hi = wm0 * 128 + fr_hi;
+  const int v_off = (wn0 + lr) * 64 + ((g ^ vswz(lr)) << 4);
+  const int m_off = (wn0 + lr) * 16 + 4 * g;
+
+  v4f acc[C::RT][C::CT];
+#pragma unroll
+  for (int r = 0; r < C::RT; r++)
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int nb_wave = min((n_base + wn0) / kGroup, NB - 1);
+  const float *ws_row = ws + (int64_t)nb_wave * KB;
+
+  auto step = [&](int kb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    const bool more = kb + 1 < KB;
+    if (more) issue_copies(kb + 1, ST ^ 1);
+    const float sw = ws_row[kb];
+    v8i bf[C::CT];
+    float scl[C::CT];
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) {
+      bf[c] = load_frag_at(ST ? lds_b1 : lds_b0, b_lo, b_hi, c * 2048);
+      scl[c] = (ST ? lds_s1 : lds_s0)[wm0 + 16 * c + lr] * sw;
+    }
+    const uint8_t *Vt = ST ? lds_v1 : lds_v0;
+    const uint8_t *Mt = ST ? lds_m1 : lds_m0;
+    v4i af_next = make_v4i(*reinterpret_cast<const uint4 *>(Vt + v_off));
+    int ix_next = *reinterpret_cast<const int *>(Mt + m_off);
+    v4f p_prev[C::CT];
+#pragma unroll
+    for (int r = 0; r < C::RT; r++) {
+      const v4i af = af_next;
+      const int ix = ix_next;
+      if (r + 1 < C::RT) {
+        af_next = make_v4i(*reinterpret_cast<const uint4 *>(Vt + v_off + (r + 1) * 1024));
+        ix_next = *reinterpret_cast<const int *>(Mt + m_off + (r + 1) * 256);
+      }
+      v4f p_cur[C::CT];
+#pragma unroll
+      for (int c = 0; c < C::CT; c++) p_cur[c] = smfmac_16x16x128_fp8(af, bf[c], ix);
+      if (r > 0) {
+#pragma unroll
+        for (int c = 0; c < C::CT; c++) {
+          acc[r - 1][c] += scl[c] * p_prev[c];
+          pin(acc[r - 1][c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < C::CT; c++) p_prev[c] = p_cur[c];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) {
+      acc[C::RT - 1][c] += scl[c] * p_prev[c];
+      pin(acc[C::RT - 1][c]);
+    }
+    if (more) {
+      wait_global_loads();
+      store_scales(ST ^ 1);
+    }
+    __syncthreads();
+  };
+
+  issue_copies(0, 0);
+  wait_global_loads();
+  store_scales(0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; kb += 2) {
+    step(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{});
+  }
+
+#pragma unroll
+  for (int c = 0; c < C::CT; c++) {
+    const int m = m_base + wm0 + 16 * c + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int r = 0; r < C::RT; r++) {
+      const int n = n_base + wn0 + 16 * r + 4 * g;
+      if (n < N) *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = pack_bf16x4(acc[r][c]);
+    }
+  }
+}
+
+// ============================================================ decode kernel ==
+
+template <int RT, int CT, int NW>
+__global__ __launch_bounds__(NW * 64) void sparse_decode_kernel(const uint8_t *__restrict__ xq,
+                                                                const float *__restrict__ xs,
+                                                                const uint8_t *__restrict__ wv,
+                                                                const uint8_t *__restrict__ wm,
+                                                                const float *__restrict__ ws, int M, int N, int K,
+                                                                uint16_t *__restrict__ y) {
+  static_assert(128 % (16 * RT) == 0, "a workgroup's rows must sit in one 128-row scale block");
+  __shared__ v4f red[NW > 1 ? NW - 1 : 1][RT * CT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, lr = lane & 15;
+  const int KB = K / kGroup;
+  const int n0 = blockIdx.x * 16 * RT;
+  const float *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
+
+  const uint8_t *vrow[RT];
+  const uint8_t *mrow[RT];
+#pragma unroll
+  for (int r = 0; r < RT; r++) {
+    const int64_t n = n0 + 16 * r + lr;
+    vrow[r] = wv + n * (K / 2) + 16 * g;
+    mrow[r] = wm + n * (K / 8) + 4 * g;
+  }
+  const uint8_t *xrow[CT];
+  const float *srow[CT];
+#pragma unroll
+  for (int c = 0; c < CT; c++) {
+    const int m = min(16 * c + lr, M - 1);
+    xrow[c] = xq + (int64_t)m * K;
+    srow[c] = xs + (int64_t)m * KB;
+  }
+
+  v4f acc[RT][CT];
+#pragma unroll
+  for (int r = 0; r < RT; r++)
+#pragma unroll
+    for (int c = 0; c < CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  v4i a_cur[RT];
+  int i_cur[RT];
+  v8i b_cur[CT];
+  float s_cur[CT], sw_cur = 0.f;
+  auto load = [&](int kb, v4i(&a)[RT], int(&ix)[RT], v8i(&b)[CT], float(&s)[CT], float &sw) {
+#pragma unroll
+    for (int r = 0; r < RT; r++) {
+      a[r] = make_v4i(ldg16(vrow[r] + (int64_t)kb * 64));
+      ix[r] = *reinterpret_cast<const int *>(mrow[r] + (int64_t)kb * 16);
+    }
+#pragma unroll
+    for (int c = 0; c < CT; c++) {
+      b[c] = load_frag_global(xrow[c] + (int64_t)kb * kGroup, g);
+      s[c] = srow[c][kb];
+    }
+    sw = ws_row[kb];
+  };
+
+  int kb = wave;
+  if (kb < KB) load(kb, a_cur, i_cur, b_cur, s_cur, sw_cur);
+  for (; kb < KB; kb += NW) {
+    v4i a_nxt[RT];
+    int i_nxt[RT];
+    v8i b_nxt[CT];
+    float s_nxt[CT], sw_nxt = 0.f;
+    const bool more = kb + NW < KB;
+    if (more) load(kb + NW, a_nxt, i_nxt, b_nxt, s_nxt, sw_nxt);
+#pragma unroll
+    for (int c = 0; c < CT; c++) {
+      const float scl = s_cur[c] * sw_cur;
+#pragma unroll
+      for (int r = 0; r < RT; r++) {
+        const v4f p = smfmac_16x16x128_fp8(a_cur[r], b_cur[c], i_cur[r]);
+        acc[r][c] += scl * p;
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < RT; r++) {
+        a_cur[r] = a_nxt[r];
+        i_cur[r] = i_nxt[r];
+      }
+#pragma unroll
+      for (int c = 0; c < CT; c++) {
+        b_cur[c] = b_nxt[c];
+        s_cur[c] = s_nxt[c];
+      }
+      sw_cur = sw_nxt;
+    }
+  }
+
+  if (NW > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int r = 0; r < RT; r++)
+#pragma unroll
+        for (int c = 0; c < CT; c++) red[wave - 1][r * CT + c][lane] = acc[r][c];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < NW - 1; w++)
+#pragma unroll
+      for (int r = 0; r < RT; r++)
+#pragma unroll
+        for (int c = 0; c < CT; c++) acc[r][c] += red[w][r * CT + c][lane];
+  }
+#pragma unroll
+  for (int c = 0; c < CT; c++) {
+    const int m = 16 * c + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int r = 0; r < RT; r++) {
+      const int n = n0 + 16 * r + 4 * g;
+      *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = pack_bf16x4(acc[r][c]);
+    }
+  }
+}
+
+// ================================================================ dispatch ==
+
+template <int BN, int BM, int WN, int WM>
+static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
+                              const float *ws, int M, int N, int K, uint16_t *y, hipStream_t stream) {
+  using C = SparseTile<BN, BM, WN, WM>;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                     stream, xq, xs, wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4);
+  return hipGetLastError();
+}
+
+template <int RT, int CT, int NW>
+static hipError_t launch_decode(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
+                                const float *ws, int M, int N, int K, uint16_t *y, hipStream_t stream) {
+  hipLaunchKernelGGL((sparse_decode_kernel<RT, CT, NW>), dim3(N / (16 * RT)), dim3(NW * 64), 0, stream, xq, xs, wv,
+                     wm, ws, M, N, K, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
+                              const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (m <= 16) return launch_decode<1, 1, 8>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+  if (m <= 32) return launch_decode<1, 2, 8>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+  if (m <= 64) return launch_decode<1, 4, 8>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+  return launch_tile<256, 256, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+}
+
+}  // namespace fp8lin

@@ -1,0 +1,19 @@
+// Kernel launchers behind the C entry points.  Arguments are already
+// validated; each returns the runtime's launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, hipStream_t stream);
+hipError_t launch_quant_wblock(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, hipStream_t stream);
+hipError_t launch_prune24(const uint16_t *w, const float *col_norm, int64_t N, int64_t K, uint8_t *vals,
+                          uint8_t *meta, float *s, hipStream_t stream);
+hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
+                             int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
+                              const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+
+}  // namespace fp8lin

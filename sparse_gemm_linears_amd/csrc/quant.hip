@@ -1,0 +1,112 @@
+// Activation (per-token 1x128) and weight (128x128 block) e4m3 quantizers.
+//
+// Both are HBM-bound streaming kernels: 16-byte loads of bf16, the group /
+// block maximum of |x| by cross-lane and LDS reductions, one IEEE fp32
+// division per element, integer RNE encoding, packed stores.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8lin {
+
+// ---------------------------------------------------------------------------
+// Activations: 16 lanes own one 1x128 group (8 bf16 = 16 bytes per lane).  A
+// 256-thread block covers 16 groups; groups are numbered row-major over
+// [M, K/128], so consecutive lanes read consecutive bytes of a row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x,
+                                                        uint8_t* __restrict__ q,
+                                                        float* __restrict__ s,
+                                                        int64_t n_groups) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t grp = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = grp < n_groups;
+  // group grp covers elements [grp*128, grp*128+128) of the flattened [M,K] array
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (live) raw = *reinterpret_cast<const uint4*>(x + grp * kGroup + lane16 * 8);
+  uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    amax_bits = max(amax_bits, bf16_abs_bits(w[i] & 0xFFFFu));
+    amax_bits = max(amax_bits, bf16_abs_bits(w[i] >> 16));
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 16));
+  const float sc = bf16_to_f32(amax_bits) / 448.0f;
+  uint32_t packed[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    uint32_t c0 = quantize(bf16_to_f32(w[2 * i] & 0xFFFFu), sc);
+    uint32_t c1 = quantize(bf16_to_f32(w[2 * i] >> 16), sc);
+    uint32_t c2 = quantize(bf16_to_f32(w[2 * i + 1] & 0xFFFFu), sc);
+    uint32_t c3 = quantize(bf16_to_f32(w[2 * i + 1] >> 16), sc);
+    packed[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+  if (live) {
+    *reinterpret_cast<uint2*>(q + grp * kGroup + lane16 * 8) = make_uint2(packed[0], packed[1]);
+    if (lane16 == 0) s[grp] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weights: one 256-thread block per 128x128 block.  Thread t owns columns
+// 8*(t%16) .. +7 of rows t/16 + 16*i, i = 0..7 (128 bytes of bf16).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_wblock_kernel(const uint16_t* __restrict__ w,
+                                                           int64_t K, uint8_t* __restrict__ q,
+                                                           float* __restrict__ s) {
+  __shared__ uint32_t wave_max[4];
+  const int t = threadIdx.x;
+  const int64_t KB = K / kGroup, nb = blockIdx.x / KB, kb = blockIdx.x % KB;
+  const int col = 8 * (t & 15);
+  const int64_t base = (nb * kGroup + (t >> 4)) * K + kb * kGroup + col;
+  uint4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) raw[i] = *reinterpret_cast<const uint4*>(w + base + (int64_t)i * 16 * K);
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint32_t v[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      amax_bits = max(amax_bits, max(bf16_abs_bits(v[j] & 0xFFFFu), bf16_abs_bits(v[j] >> 16)));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 64));
+  if ((t & 63) == 0) wave_max[t >> 6] = amax_bits;
+  __syncthreads();
+  amax_bits = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+  const float sc = bf16_to_f32(amax_bits) / 448.0f;
+  if (t == 0) s[nb * KB + kb] = sc;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint32_t v[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    uint32_t packed[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      uint32_t c0 = quantize(bf16_to_f32(v[2 * h] & 0xFFFFu), sc);
+      uint32_t c1 = quantize(bf16_to_f32(v[2 * h] >> 16), sc);
+      uint32_t c2 = quantize(bf16_to_f32(v[2 * h + 1] & 0xFFFFu), sc);
+      uint32_t c3 = quantize(bf16_to_f32(v[2 * h + 1] >> 16), sc);
+      packed[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    *reinterpret_cast<uint2*>(q + base + (int64_t)i * 16 * K) = make_uint2(packed[0], packed[1]);
+  }
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                            hipStream_t stream) {
+  const int64_t n_groups = M * (K / kGroup);
+  const int64_t blocks = (n_groups + 15) / 16;
+  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, s, n_groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_wblock(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(quant_wblock_kernel, dim3((unsigned)((N / kGroup) * (K / kGroup))), dim3(256), 0, stream, w,
+                     K, q, s);
+  return hipGetLastError();
+}
+
+}  // namespace fp8lin
