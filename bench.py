@@ -1,0 +1,294 @@
+"""Benchmark of the FP8 quantized linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch, for each of the four
+Llama-3-8B linears (QKV 4096->6144, o_proj 4096->4096, gate/up 4096->28672,
+down 14336->4096) at M = 4096 tokens:
+    fp8_quant_act(X) -> fp8_quant_weight_block(W) -> fp8_block_gemm
+    prune24_compress(W, ||x_k||) -> fp8_sparse24_gemm
+Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+
+`value` is the step's algorithmic GEMM work divided by the step time: 2*M*N*K
+for each dense GEMM plus M*N*K for each 2:4 GEMM (the pruned half of the
+multiply-adds is never done), in TFLOP/s.  The JSON line also carries the
+roofline of the dominant kernel (the dense gate/up GEMM), per-kernel times
+taken with HIP events on the launch stream, the decode-M GEMMs (HBM GB/s, with
+the weights rotated through enough copies to defeat the caches) and the CPU
+oracle timed on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s & % MFMA peak (dense, 2:4); decode-M HBM GB/s"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-decode", action="store_true", help="skip the decode-M GEMM measurements")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="token rows in the CPU oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the FP8 linear layer is built and timed on a single MI355X; "
+              "multi-GPU runs are not part of this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_gemm_linears_amd as sgl
+    import synth_inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sgl.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M = si.PREFILL_M
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ------------------------------------------------------------ inputs ----
+    layers = []
+    for name, K, N in si.LLAMA3_8B:
+        x = bf16(si.activations(M, K))
+        w = bf16(si.weights(N, K))
+        c = torch.from_numpy(si.column_norms(si.calibration_batch(K))).to(dev)
+        L = dict(name=name, K=K, N=N, x=x, w=w, c=c,
+                 xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                 xs=torch.empty((M, K // 128), dtype=torch.float32, device=dev),
+                 wq=torch.empty((N, K), dtype=torch.uint8, device=dev),
+                 ws=torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev),
+                 wv=torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+                 wm=torch.empty((N, K // 8), dtype=torch.uint8, device=dev),
+                 ws2=torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev),
+                 y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                 y2=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+        layers.append(L)
+    torch.cuda.synchronize()
+
+    kernels = ("quant_act", "quant_wblock", "prune24", "dense_gemm", "sparse_gemm")
+
+    def step(events=None):
+        for li, L in enumerate(layers):
+            calls = (
+                lambda: sgl.fp8_quant_act(L["x"], L["xq"], L["xs"]),
+                lambda: sgl.fp8_quant_weight_block(L["w"], L["wq"], L["ws"]),
+                lambda: sgl.prune24_compress(L["w"], L["c"], L["wv"], L["wm"], L["ws2"]),
+                lambda: sgl.fp8_block_gemm(L["xq"], L["xs"], L["wq"], L["ws"], L["y"]),
+                lambda: sgl.fp8_sparse24_gemm(L["xq"], L["xs"], L["wv"], L["wm"], L["ws2"], L["y2"]),
+            )
+            for ki, f in enumerate(calls):
+                if events is not None:
+                    events[li][ki][0].record()
+                f()
+                if events is not None:
+                    events[li][ki][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------- timed whole steps ----
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ----------------------------------- per-kernel times (HIP events) ------
+    durations = {(li, ki): [] for li in range(len(layers)) for ki in range(len(kernels))}
+    for _ in range(args.steps):
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in kernels] for _ in layers]
+        step(ev)
+        torch.cuda.synchronize()
+        for li in range(len(layers)):
+            for ki in range(len(kernels)):
+                durations[(li, ki)].append(ev[li][ki][0].elapsed_time(ev[li][ki][1]) * 1e3)  # us
+
+    def bytes_of(kname, K, N):
+        if kname == "quant_act":
+            return 2 * M * K + M * K + 4 * M * K // 128
+        if kname == "quant_wblock":
+            return 2 * N * K + N * K + 4 * (N // 128) * (K // 128)
+        if kname == "prune24":
+            return 2 * N * K + N * K // 2 + N * K // 8 + 4 * (N // 128) * (K // 128) + 4 * K
+        return None
+
+    per_kernel = {}
+    dense_flops = sparse_flops = 0
+    for li, L in enumerate(layers):
+        K, N = L["K"], L["N"]
+        dense_flops += 2 * M * N * K
+        sparse_flops += M * N * K
+        for ki, kname in enumerate(kernels):
+            us = float(np.mean(durations[(li, ki)]))
+            entry = {"us": round(us, 2)}
+            if kname == "dense_gemm":
+                tf = 2 * M * N * K / us / 1e6
+                entry.update(tflops=round(tf, 1), frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4))
+            elif kname == "sparse_gemm":
+                tf = M * N * K / us / 1e6
+                dense_us = float(np.mean(durations[(li, kernels.index("dense_gemm"))]))
+                entry.update(tflops_algorithmic=round(tf, 1), tflops_dense_equivalent=round(2 * tf, 1),
+                             frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4),
+                             speedup_vs_dense=round(dense_us / us, 3))
+            else:
+                gbs = bytes_of(kname, K, N) / us / 1e3
+                entry.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+            per_kernel[f"{L['name']}.{kname}"] = entry
+
+    gemm_flops = dense_flops + sparse_flops
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the dense gate/up GEMM
+    gi = [L["name"] for L in layers].index("gate_up")
+    Lg = layers[gi]
+    dom_us = float(np.mean(durations[(gi, kernels.index("dense_gemm"))]))
+    dom_flops = 2 * M * Lg["N"] * Lg["K"]
+    achieved = dom_flops / dom_us / 1e6
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "kernel": "fp8_block_gemm dense tile kernel, gate_up 4096x28672x4096",
+                "avg_launch_us": round(dom_us, 2), "flops_per_launch": dom_flops}
+
+    # free the prefill working set before the decode measurements
+    del layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    decode = None if args.no_decode else bench_decode(sgl, si, torch, np, dev, bf16)
+    cpu = None if args.no_cpu else cpu_baseline(si, np, args.cpu_rows)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "llama3_8b_linears_m4096: act quant + weight block quant + 2:4 prune/compress "
+                               "+ dense and 2:4 block-scaled FP8 GEMM",
+                   "tokens": M, "shapes_k_n": [[K, N] for _, K, N in si.LLAMA3_8B],
+                   "gemm_flops_per_step": gemm_flops, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": per_kernel,
+        "decode": decode,
+    }
+    print(json.dumps(out))
+
+
+def bench_decode(sgl, si, torch, np, dev, bf16):
+    """Decode-M GEMMs: dense at M in {1,8,32,64}, 2:4 at M=16, each shape with
+    enough weight copies (>= 1 GiB in total) that every call reads its weight
+    from HBM.  Each call is timed as a HIP-graph replay of back-to-back calls."""
+    res = {}
+    for name, K, N in si.LLAMA3_8B:
+        wq_bytes = N * K
+        copies = max(2, math.ceil((1 << 30) / wq_bytes))
+        w = bf16(si.weights(N, K))
+        c = torch.from_numpy(si.column_norms(si.calibration_batch(K))).to(dev)
+        wq0, ws0 = sgl.fp8_quant_weight_block(w)
+        wv0, wm0, ws20 = sgl.prune24_compress(w, c)
+        dense_w = [(wq0.clone(), ws0.clone()) for _ in range(copies)]
+        sparse_w = [(wv0.clone(), wm0.clone(), ws20.clone()) for _ in range(copies)]
+        del w, wq0, wv0, wm0
+        for M in (1, 8, 16, 32, 64):
+            x = bf16(si.activations(M, K))
+            xq, xs = sgl.fp8_quant_act(x)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            runs = {"dense": lambda i: sgl.fp8_block_gemm(xq, xs, dense_w[i][0], dense_w[i][1], y)}
+            if M == 16:
+                runs["sparse"] = lambda i: sgl.fp8_sparse24_gemm(xq, xs, *sparse_w[i], y)
+            for kind, f in runs.items():
+                us = time_graph(torch, f, copies)
+                if kind == "dense":
+                    nbytes = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
+                else:
+                    nbytes = N * K // 2 + N * K // 8 + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) \
+                        + 2 * M * N
+                gbs = nbytes / us / 1e3
+                res[f"{name}.M{M}.{kind}"] = {"us": round(us, 2), "gbs": round(gbs, 1),
+                                              "frac_hbm": round(gbs / 8000.0, 4)}
+            if "sparse" in runs:
+                res[f"{name}.M16.sparse"]["speedup_vs_dense"] = round(
+                    res[f"{name}.M16.dense"]["us"] / res[f"{name}.M16.sparse"]["us"], 3)
+        del dense_w, sparse_w
+        torch.cuda.empty_cache()
+    return res
+
+
+def time_graph(torch, f, copies, reps=3):
+    """Average time per call of f(i), i cycling over the weight copies, from a
+    captured HIP graph of `copies` back-to-back calls replayed `reps` times."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(min(copies, 3)):
+            f(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(copies):
+            f(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * copies)
+
+
+def cpu_baseline(si, np, rows):
+    """The CPU oracle on a bounded sample of the step: for each of the four
+    shapes, activation quant of `rows` tokens, weight block quant and 2:4
+    prune/compress of the whole weight, and the dense and 2:4 GEMMs of those
+    `rows` tokens.  Reported in the step's unit (algorithmic GEMM TFLOP/s);
+    input generation is not timed."""
+    import oracle
+
+    oracle.build()
+    inputs = [(si.activations(rows, K), si.weights(N, K), si.column_norms(si.calibration_batch(K)), K, N)
+              for _, K, N in si.LLAMA3_8B]
+    flops = 0
+    t0 = time.perf_counter()
+    for x, w, c, K, N in inputs:
+        xq, xs = oracle.quant_act(x)
+        wq, ws = oracle.quant_wblock(w)
+        v, m, s2 = oracle.prune24_compress(w, c)
+        oracle.gemm(xq, xs, wq, ws)
+        oracle.sparse24_gemm(xq, xs, v, m, s2)
+        flops += 3 * rows * N * K
+    total = time.perf_counter() - t0
+    return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(total, 2),
+            "sample": f"each Llama-3-8B shape: quant of {rows} token rows, block quant and 2:4 prune of the "
+                      f"whole weight, dense + 2:4 GEMM of the {rows} rows (fp64 oracle, OpenMP over rows)"}
+
+
+if __name__ == "__main__":
+    main()
