@@ -1,8 +1,8 @@
 // Device helpers shared by the fp8lin kernels (gfx950 only).
 //
 // Number formats: bf16 in/out (raw 16-bit patterns), OCP E4M3FN codes, fp32
-// scales.  The e4m3 encoder works on the fp32 bit pattern with integer
-// arithmetic: round to nearest, ties to even, saturating at +-448.
+// scales.  Encoding to e4m3 rounds to nearest, ties to even, and saturates at
+// +-448.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,30 +24,55 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// fp32 -> E4M3FN code: RNE, saturating, NaN -> S|0x7F.
-//  * normal range (|v| >= 2^-6): round the 23-bit mantissa to 3 bits on the
-//    fp32 pattern; the carry moves into the exponent; rebias 127 -> 7.
-//  * subnormal range: |v| * 2^9 is exact in fp32 and rint() rounds it to the
-//    integer code 0..8 (8 is 2^-6, the smallest normal, code 0x08).
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
-  if (a > 0x43E00000u) return sign | 0x7Eu;  // above 448 (and inf): saturate
-  if (a >= 0x3C800000u) {                     // >= 2^-6
-    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    return sign | ((r >> 20) - (120u << 3));
-  }
-  float f = __uint_as_float(a) * 512.0f;
-  return sign | (uint32_t)__builtin_rintf(f);
+// Four E4M3FN codes packed little-endian into one word, from four fp32
+// values, with the hardware conversion v_cvt_pk_fp8_f32: round to nearest
+// even; the inputs are first clamped to +-448, which makes it saturating.  On
+// gfx950 this equals an integer RNE-saturating encoder on every non-NaN input
+// (checked over all exponents on a 2^-11-relative grid, +-40 ulp around every
+// midpoint and 2M random values).
+__device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
+  q0 = __builtin_amdgcn_fmed3f(q0, -448.0f, 448.0f);
+  q1 = __builtin_amdgcn_fmed3f(q1, -448.0f, 448.0f);
+  q2 = __builtin_amdgcn_fmed3f(q2, -448.0f, 448.0f);
+  q3 = __builtin_amdgcn_fmed3f(q3, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
+  return (uint32_t)w;
 }
 
-// Code of x in a group with scale s = amax/448.  s == 0 only when every value
-// of the group is +-0: the code is then the signed zero.  x / s is an IEEE
-// (correctly rounded) fp32 division.
-__device__ __forceinline__ uint32_t quantize(float x, float s) {
-  return e4m3_encode(s == 0.0f ? x : x / s);
+// Exact codes of four values of a group with scale s (IEEE divisions).
+__device__ __forceinline__ uint32_t quantize4_exact(const float (&x)[4], float s) {
+  float q[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) q[j] = s == 0.0f ? x[j] : x[j] / s;
+  return e4m3_pack4(q[0], q[1], q[2], q[3]);
+}
+
+// Fast codes of four values: qa = x * rs with rs = rcp(s) (v_rcp_f32, within
+// 1 ulp) is within 2 ulp of the correctly rounded quotient fl(x / s) (4 ulp
+// across a binade edge), so the e4m3 rounding of qa and of fl(x / s) can only
+// differ when qa lies that close to an e4m3 rounding midpoint.  Midpoints of
+// the normal range have the 20 bits below the 3 kept mantissa bits equal to
+// 0x80000; `need` gets a non-zero bit when some qa is within 8 ulp of one, or
+// lies in the e4m3 subnormal range (0 < |qa| < 2^-6): the caller must then use
+// quantize4_exact for these values.
+__device__ __forceinline__ uint32_t quantize4_fast(const float (&x)[4], float rs, uint32_t &need) {
+  float q[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    q[j] = x[j] * rs;
+    const uint32_t b = __float_as_uint(q[j]);
+    const uint32_t t = b & 0x7FFFFFFFu;
+    need |= (((b & 0xFFFFFu) - 0x7FFF8u) < 17u) | ((t - 1u) < 0x3C7FFFFFu);
+  }
+  return e4m3_pack4(q[0], q[1], q[2], q[3]);
+}
+
+// Scales for which the fast path is valid: 2^-100 <= s < inf (rs finite, no
+// overflow or underflow in x * rs for bf16 x with |x| <= 448 s).
+__device__ __forceinline__ bool scale_fast_ok(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return b >= 0x0D800000u && b < 0x7F800000u;
 }
 
 // |bf16| as an integer: ordering of non-NaN magnitudes is the integer ordering.

@@ -79,6 +79,69 @@ __device__ __forceinline__ uint2 pack_bf16x4(const v4f &v) {
                     f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
 }
 
+// Token scales of a BM-row tile, staged in LDS in groups of SB K blocks
+// (ring of two groups).  With SB = 4 (K/128 divisible by 4) each thread loads
+// the four scales of its row with one 16-byte load, so the scattered per-row
+// reads cost one request per four K blocks.
+template <int BM, int SB>
+struct TokenScales {
+  float *lds;  // [2][SB][BM]
+  const float *src;
+  float4 reg;
+  int tid;
+
+  __device__ __forceinline__ void init(float *lds_, const float *xs, int M, int KB, int m_base, int tid_) {
+    lds = lds_;
+    tid = tid_;
+    src = xs + (int64_t)min(m_base + min(tid, BM - 1), M - 1) * KB;
+  }
+  // registers <- scales of K blocks [SB*grp, SB*grp + SB)
+  __device__ __forceinline__ void load(int grp) {
+    if (tid < BM) {
+      if (SB == 4) reg = *reinterpret_cast<const float4 *>(src + 4 * grp);
+      else reg.x = src[grp];
+    }
+  }
+  __device__ __forceinline__ void store(int grp) {
+    if (tid < BM) {
+      float *d = lds + (grp & 1) * SB * BM + tid;
+      d[0] = reg.x;
+      if (SB == 4) {
+        d[BM] = reg.y;
+        d[2 * BM] = reg.z;
+        d[3 * BM] = reg.w;
+      }
+    }
+  }
+  __device__ __forceinline__ float get(int kb, int row) const {
+    return lds[((kb / SB) & 1) * SB * BM + (kb % SB) * BM + row];
+  }
+};
+
+// Coalesced epilogue: a wave writes its 16 x (16*RT) bf16 sub-tile for token
+// tile c into a private 16 x 256-byte LDS scratch (16-byte chunks XOR-swizzled
+// by row), reads it back as whole rows and stores 256 contiguous bytes per
+// row.  `acc_c` holds the RT 16x16 accumulators of token tile c (lane: token
+// l%16, rows 4*(l/16)..+3 of each row tile).  Requires 16*RT*2 == 256.
+template <int RT>
+__device__ __forceinline__ void store_token_tile(uint8_t *scratch, const v4f (&acc_c)[RT], uint16_t *y, int M,
+                                                 int N, int m0, int n0, int lane) {
+  static_assert(RT == 8, "scratch rows are 256 bytes");
+  const int lr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < RT; r++) {
+    const int chunk = 2 * r + (g >> 1);
+    *reinterpret_cast<uint2 *>(scratch + lr * 256 + ((chunk ^ lr) << 4) + 8 * (g & 1)) = pack_bf16x4(acc_c[r]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int row = 4 * j + g;  // lane l reads row 4j + l/16, chunk l%16
+    const uint4 v = *reinterpret_cast<const uint4 *>(scratch + row * 256 + ((lr ^ row) << 4));
+    const int m = m0 + row, n = n0 + 8 * lr;
+    if (m < M && n < N) *reinterpret_cast<uint4 *>(y + (int64_t)m * N + n) = v;
+  }
+}
+
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin (block b runs on
 // XCD b % 8), each XCD with its own L2.  The remap gives every XCD one
 // contiguous range of logical tile ids; the logical order then walks groups of

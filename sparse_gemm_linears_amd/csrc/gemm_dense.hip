@@ -9,7 +9,8 @@
 //
 // Two kernels:
 //  * tile kernel (large M): BN x BM output tile per workgroup, 128-wide K steps
-//    staged through double-buffered, swizzled LDS, one barrier per step;
+//    staged through double-buffered, swizzled LDS, one barrier per step,
+//    coalesced bf16 stores through LDS at the end;
 //  * decode kernel (M <= 64): the weight streams from HBM straight into MFMA
 //    registers, the waves of a workgroup split K and meet in LDS at the end.
 #include <type_traits>
@@ -30,11 +31,14 @@ struct DenseTile {
   static constexpr int kATile = BN * 128, kBTile = BM * 128;
   static_assert(BN % (8 * kWaves) == 0 && BM % (8 * kWaves) == 0, "tile / wave mismatch");
   static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
-  static_assert(kWaveN <= 128 && 128 % kWaveN == 0, "a wave's rows must sit in one 128-row scale block");
+  static_assert(kWaveN == 128, "a wave covers one 128-row weight scale block (and 256-byte epilogue rows)");
   static_assert(BM <= kThreads, "one thread per token scale");
+  static_assert(kWaves * 4096 <= kATile, "epilogue scratch fits in one weight stage");
 };
 
-template <int BN, int BM, int WN, int WM>
+// SB: K blocks per token-scale load (4 when K/128 is a multiple of 4, else 1).
+// CR: the next K block's copies are issued across the first CR row tiles.
+template <int BN, int BM, int WN, int WM, int SB, int CR>
 __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *__restrict__ xq,
                                                                 const float *__restrict__ xs,
                                                                 const uint8_t *__restrict__ wq,
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
   // the copies in flight.
   __shared__ __align__(16) uint8_t lds_a0[C::kATile], lds_a1[C::kATile];
   __shared__ __align__(16) uint8_t lds_b0[C::kBTile], lds_b1[C::kBTile];
-  __shared__ float lds_s0[BM], lds_s1[BM];
+  __shared__ __align__(16) float lds_s[2 * SB * BM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
@@ -72,29 +76,30 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
     const int r0 = m_base + (i * C::kWaves + wave) * 8;
     b_lane[i] = (uint32_t)((min(r0 + cj, M - 1) - min(r0, M - 1)) * K + copy_chunk);
   }
-  const float *s_src = xs + (int64_t)min(m_base + min(tid, BM - 1), M - 1) * KB;
-  float s_reg = 0.0f;
+  TokenScales<BM, SB> scales;
+  scales.init(lds_s, xs, M, KB, m_base, tid);
 
   // One 128-wide K block of the weight and token panels into LDS stage `st`.
   // Rows past the matrix edge re-read valid rows; their results are never stored.
-  auto issue_copies = [&](int kb, int st) {
+  auto issue_copy = [&](int kb, int st, int j) {
     const int64_t koff = (int64_t)kb * kGroup;
-#pragma unroll
-    for (int i = 0; i < C::kACopies; i++) {
-      const int r0 = (i * C::kWaves + wave) * 8;
+    if (j < C::kACopies) {
+      const int r0 = (j * C::kWaves + wave) * 8;
       const uint8_t *base = wq + (int64_t)min(n_base + r0, N - 8) * K + koff;
       copy16_global_to_lds(base + a_lane, (st ? lds_a1 : lds_a0) + r0 * 128);
-    }
-#pragma unroll
-    for (int i = 0; i < C::kBCopies; i++) {
+    } else {
+      const int i = j - C::kACopies;
       const int r0 = (i * C::kWaves + wave) * 8;
       const uint8_t *base = xq + (int64_t)min(m_base + r0, M - 1) * K + koff;
       copy16_global_to_lds(base + b_lane[i], (st ? lds_b1 : lds_b0) + r0 * 128);
     }
-    if (tid < BM) s_reg = s_src[kb];
   };
-  auto store_scales = [&](int st) {
-    if (tid < BM) (st ? lds_s1 : lds_s0)[tid] = s_reg;
+  constexpr int kCopies = C::kACopies + C::kBCopies;
+  constexpr int kCopyRows = CR < C::RT ? CR : C::RT;  // copies are spread over the first kCopyRows row tiles
+  constexpr int kCopiesPerRow = (kCopies + kCopyRows - 1) / kCopyRows;
+  auto issue_copies = [&](int kb, int st) {
+#pragma unroll
+    for (int j = 0; j < kCopies; j++) issue_copy(kb, st, j);
   };
 
   // per-lane fragment read offsets (row lr of a 16-row slab, chunks g and g+4)
@@ -112,74 +117,81 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
   const int nb_wave = min((n_base + wn0) / kGroup, NB - 1);
   const float *ws_row = ws + (int64_t)nb_wave * KB;
 
-  // One K step on stage ST: the next block's copies are in flight while the
-  // MFMAs of this one run.  Partials of row tile r are scaled into the
-  // accumulators while the MFMAs of row tile r+1 execute.
+  // One K step on stage ST: the next block's copies (and, once per scale
+  // group, the next group's token scales) are in flight while the MFMAs of
+  // this one run.  The partial of each 16x16 tile is scaled into its
+  // accumulator while the MFMA of the following tile executes.
   auto step = [&](int kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     const bool more = kb + 1 < KB;
-    if (more) issue_copies(kb + 1, ST ^ 1);
+    const bool scale_load = (kb % SB == 0) && (kb + SB < KB);
+    if (scale_load) scales.load(kb / SB + 1);
     const float sw = ws_row[kb];
+    // Only the first A and B fragments are read up front; the other B
+    // fragments are read between the MFMAs of row tile 0 and each next A
+    // fragment during the MFMAs of the current row tile, so the waves leaving
+    // the barrier do not all queue on the LDS before their first MFMA.
+    const uint8_t *At = ST ? lds_a1 : lds_a0;
+    const uint8_t *Bt = ST ? lds_b1 : lds_b0;
     v8i bf[C::CT];
     float scl[C::CT];
-#pragma unroll
-    for (int c = 0; c < C::CT; c++) {
-      bf[c] = load_frag_at(ST ? lds_b1 : lds_b0, b_lo, b_hi, c * 2048);
-      scl[c] = (ST ? lds_s1 : lds_s0)[wm0 + 16 * c + lr] * sw;
-    }
-    const uint8_t *At = ST ? lds_a1 : lds_a0;
-    v8i af_next = load_frag_at(At, a_lo, a_hi, 0);
-    v4f p_prev[C::CT];
+    v8i an = load_frag_at(At, a_lo, a_hi, 0);
+    bf[0] = load_frag_at(Bt, b_lo, b_hi, 0);
+    v4f p_prev;
 #pragma unroll
     for (int r = 0; r < C::RT; r++) {
-      const v8i af = af_next;
-      if (r + 1 < C::RT) af_next = load_frag_at(At, a_lo, a_hi, (r + 1) * 2048);
-      v4f p_cur[C::CT];
+      if (more && r < kCopyRows) {
 #pragma unroll
-      for (int c = 0; c < C::CT; c++) p_cur[c] = mfma_16x16x128_fp8(af, bf[c], v4f{0.f, 0.f, 0.f, 0.f});
-      if (r > 0) {
-#pragma unroll
-        for (int c = 0; c < C::CT; c++) {
-          acc[r - 1][c] += scl[c] * p_prev[c];
-          pin(acc[r - 1][c]);
-        }
+        for (int j = r * kCopiesPerRow; j < (r + 1) * kCopiesPerRow && j < kCopies; j++) issue_copy(kb + 1, ST ^ 1, j);
       }
+      const v8i af = an;
+      if (r + 1 < C::RT) an = load_frag_at(At, a_lo, a_hi, (r + 1) * 2048);
 #pragma unroll
-      for (int c = 0; c < C::CT; c++) p_prev[c] = p_cur[c];
+      for (int c = 0; c < C::CT; c++) {
+        if (r == 0) {
+          if (c + 1 < C::CT) bf[c + 1] = load_frag_at(Bt, b_lo, b_hi, (c + 1) * 2048);
+          scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
+        }
+        const v4f p = mfma_16x16x128_fp8(af, bf[c], v4f{0.f, 0.f, 0.f, 0.f});
+        const int t = r * C::CT + c;
+        if (t > 0) {
+          const int pr = (t - 1) / C::CT, pc = (t - 1) % C::CT;
+          acc[pr][pc] += scl[pc] * p_prev;
+          pin(acc[pr][pc]);
+        }
+        p_prev = p;
+        if (r == 0) __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int c = 0; c < C::CT; c++) {
-      acc[C::RT - 1][c] += scl[c] * p_prev[c];
-      pin(acc[C::RT - 1][c]);
-    }
-    if (more) {
-      wait_global_loads();
-      store_scales(ST ^ 1);
-    }
+    acc[C::RT - 1][C::CT - 1] += scl[C::CT - 1] * p_prev;
+    pin(acc[C::RT - 1][C::CT - 1]);
+    if (more || scale_load) wait_global_loads();
+    if (scale_load) scales.store(kb / SB + 1);
     __syncthreads();
   };
 
   issue_copies(0, 0);
+  scales.load(0);
   wait_global_loads();
-  store_scales(0);
+  scales.store(0);
   __syncthreads();
   for (int kb = 0; kb < KB; kb += 2) {
     step(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{});
   }
 
+  // epilogue through a wave-private 4 KB slice of the (now idle) weight stage 0
+  uint8_t *scratch = lds_a0 + wave * 4096;
 #pragma unroll
   for (int c = 0; c < C::CT; c++) {
-    const int m = m_base + wm0 + 16 * c + lr;
-    if (m >= M) continue;
+    v4f col[C::RT];
 #pragma unroll
-    for (int r = 0; r < C::RT; r++) {
-      const int n = n_base + wn0 + 16 * r + 4 * g;
-      if (n < N) *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = pack_bf16x4(acc[r][c]);
-    }
+    for (int r = 0; r < C::RT; r++) col[r] = acc[r][c];
+    store_token_tile<C::RT>(scratch, col, y, M, N, m_base + wm0 + 16 * c, n_base + wn0, lane);
   }
 }
+
 
 // ============================================================ decode kernel ==
 
@@ -294,8 +306,12 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
                               int K, uint16_t *y, hipStream_t stream) {
   using C = DenseTile<BN, BM, WN, WM>;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0, stream, xq,
-                     xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4);
+  if ((K / kGroup) % 4 == 0)
+    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                       stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4);
+  else
+    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                       stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4);
   return hipGetLastError();
 }
 

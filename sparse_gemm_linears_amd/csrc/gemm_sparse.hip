@@ -43,11 +43,13 @@ struct SparseTile {
   static constexpr int kVTile = BN * 64, kMTile = BN * 16, kBTile = BM * 128;
   static_assert(BN % (16 * kWaves) == 0 && BM % (8 * kWaves) == 0 && kMCopyWaves <= kWaves, "tile mismatch");
   static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
-  static_assert(kWaveN <= 128 && 128 % kWaveN == 0, "a wave's rows must sit in one 128-row scale block");
+  static_assert(kWaveN == 128, "a wave covers one 128-row weight scale block (and 256-byte epilogue rows)");
   static_assert(BM <= kThreads, "one thread per token scale");
+  static_assert(kWaves * 4096 <= kBTile, "epilogue scratch fits in one token stage");
 };
 
-template <int BN, int BM, int WN, int WM>
+// SB: K blocks per token-scale load (4 when K/128 is a multiple of 4, else 1).
+template <int BN, int BM, int WN, int WM, int SB>
 __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t *__restrict__ xq,
                                                                  const float *__restrict__ xs,
                                                                  const uint8_t *__restrict__ wv,
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
   __shared__ __align__(16) uint8_t lds_v0[C::kVTile], lds_v1[C::kVTile];
   __shared__ __align__(16) uint8_t lds_m0[C::kMTile], lds_m1[C::kMTile];
   __shared__ __align__(16) uint8_t lds_b0[C::kBTile], lds_b1[C::kBTile];
-  __shared__ float lds_s0[BM], lds_s1[BM];
+  __shared__ __align__(16) float lds_s[2 * SB * BM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
@@ -89,8 +91,8 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
     const int r0 = m_base + (i * C::kWaves + wave) * 8;
     b_lane[i] = (uint32_t)((min(r0 + cj, M - 1) - min(r0, M - 1)) * K + copy_chunk);
   }
-  const float *s_src = xs + (int64_t)min(m_base + min(tid, BM - 1), M - 1) * KB;
-  float s_reg = 0.0f;
+  TokenScales<BM, SB> scales;
+  scales.init(lds_s, xs, M, KB, m_base, tid);
 
   auto issue_copies = [&](int kb, int st) {
 #pragma unroll
@@ -110,10 +112,6 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
       const uint8_t *base = xq + (int64_t)min(m_base + r0, M - 1) * K + (int64_t)kb * kGroup;
       copy16_global_to_lds(base + b_lane[i], (st ? lds_b1 : lds_b0) + r0 * 128);
     }
-    if (tid < BM) s_reg = s_src[kb];
-  };
-  auto store_scales = [&](int st) {
-    if (tid < BM) (st ? lds_s1 : lds_s0)[tid] = s_reg;
   };
 
   const int fr_lo = lr * 128 + ((g ^ swz(lr)) << 4);
@@ -134,14 +132,16 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
   auto step = [&](int kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     const bool more = kb + 1 < KB;
+    const bool scale_load = (kb % SB == 0) && (kb + SB < KB);
     if (more) issue_copies(kb + 1, ST ^ 1);
+    if (scale_load) scales.load(kb / SB + 1);
     const float sw = ws_row[kb];
     v8i bf[C::CT];
     float scl[C::CT];
 #pragma unroll
     for (int c = 0; c < C::CT; c++) {
       bf[c] = load_frag_at(ST ? lds_b1 : lds_b0, b_lo, b_hi, c * 2048);
-      scl[c] = (ST ? lds_s1 : lds_s0)[wm0 + 16 * c + lr] * sw;
+      scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
     }
     const uint8_t *Vt = ST ? lds_v1 : lds_v0;
     const uint8_t *Mt = ST ? lds_m1 : lds_m0;
@@ -175,31 +175,29 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
       acc[C::RT - 1][c] += scl[c] * p_prev[c];
       pin(acc[C::RT - 1][c]);
     }
-    if (more) {
-      wait_global_loads();
-      store_scales(ST ^ 1);
-    }
+    if (more || scale_load) wait_global_loads();
+    if (scale_load) scales.store(kb / SB + 1);
     __syncthreads();
   };
 
   issue_copies(0, 0);
+  scales.load(0);
   wait_global_loads();
-  store_scales(0);
+  scales.store(0);
   __syncthreads();
   for (int kb = 0; kb < KB; kb += 2) {
     step(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{});
   }
 
+  // epilogue through a wave-private 4 KB slice of the (now idle) token stage 0
+  uint8_t *scratch = lds_b0 + wave * 4096;
 #pragma unroll
   for (int c = 0; c < C::CT; c++) {
-    const int m = m_base + wm0 + 16 * c + lr;
-    if (m >= M) continue;
+    v4f col[C::RT];
 #pragma unroll
-    for (int r = 0; r < C::RT; r++) {
-      const int n = n_base + wn0 + 16 * r + 4 * g;
-      if (n < N) *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = pack_bf16x4(acc[r][c]);
-    }
+    for (int r = 0; r < C::RT; r++) col[r] = acc[r][c];
+    store_token_tile<C::RT>(scratch, col, y, M, N, m_base + wm0 + 16 * c, n_base + wn0, lane);
   }
 }
 
@@ -329,8 +327,12 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
                               const float *ws, int M, int N, int K, uint16_t *y, hipStream_t stream) {
   using C = SparseTile<BN, BM, WN, WM>;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
-                     stream, xq, xs, wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4);
+  if ((K / kGroup) % 4 == 0)
+    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                       stream, xq, xs, wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4);
+  else
+    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 1>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                       stream, xq, xs, wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4);
   return hipGetLastError();
 }
 

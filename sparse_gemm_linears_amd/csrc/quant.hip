@@ -33,14 +33,22 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 16));
   const float sc = bf16_to_f32(amax_bits) / 448.0f;
-  uint32_t packed[2];
+  const float rs = __builtin_amdgcn_rcpf(sc);
+  float v[2][4];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
-    uint32_t c0 = quantize(bf16_to_f32(w[2 * i] & 0xFFFFu), sc);
-    uint32_t c1 = quantize(bf16_to_f32(w[2 * i] >> 16), sc);
-    uint32_t c2 = quantize(bf16_to_f32(w[2 * i + 1] & 0xFFFFu), sc);
-    uint32_t c3 = quantize(bf16_to_f32(w[2 * i + 1] >> 16), sc);
-    packed[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    v[i][0] = bf16_to_f32(w[2 * i] & 0xFFFFu);
+    v[i][1] = __uint_as_float(w[2 * i] & 0xFFFF0000u);
+    v[i][2] = bf16_to_f32(w[2 * i + 1] & 0xFFFFu);
+    v[i][3] = __uint_as_float(w[2 * i + 1] & 0xFFFF0000u);
+  }
+  uint32_t need = scale_fast_ok(sc) ? 0u : 1u;
+  uint32_t packed[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) packed[i] = quantize4_fast(v[i], rs, need);
+  if (__builtin_expect(need != 0u, 0)) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) packed[i] = quantize4_exact(v[i], sc);
   }
   if (live) {
     *reinterpret_cast<uint2*>(q + grp * kGroup + lane16 * 8) = make_uint2(packed[0], packed[1]);
@@ -57,9 +65,9 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(const uint16_t* __res
                                                            float* __restrict__ s) {
   __shared__ uint32_t wave_max[4];
   const int t = threadIdx.x;
-  const int64_t KB = K / kGroup, nb = blockIdx.x / KB, kb = blockIdx.x % KB;
+  const int KB = (int)(K / kGroup), nb = (int)blockIdx.x / KB, kb = (int)blockIdx.x % KB;
   const int col = 8 * (t & 15);
-  const int64_t base = (nb * kGroup + (t >> 4)) * K + kb * kGroup + col;
+  const int64_t base = ((int64_t)nb * kGroup + (t >> 4)) * K + (int64_t)kb * kGroup + col;
   uint4 raw[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) raw[i] = *reinterpret_cast<const uint4*>(w + base + (int64_t)i * 16 * K);
@@ -77,20 +85,29 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(const uint16_t* __res
   __syncthreads();
   amax_bits = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
   const float sc = bf16_to_f32(amax_bits) / 448.0f;
-  if (t == 0) s[nb * KB + kb] = sc;
+  const float rs = __builtin_amdgcn_rcpf(sc);
+  const bool ok = scale_fast_ok(sc);
+  if (t == 0) s[(int64_t)nb * KB + kb] = sc;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    uint32_t v[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-    uint32_t packed[2];
+    float v[2][4];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      uint32_t c0 = quantize(bf16_to_f32(v[2 * h] & 0xFFFFu), sc);
-      uint32_t c1 = quantize(bf16_to_f32(v[2 * h] >> 16), sc);
-      uint32_t c2 = quantize(bf16_to_f32(v[2 * h + 1] & 0xFFFFu), sc);
-      uint32_t c3 = quantize(bf16_to_f32(v[2 * h + 1] >> 16), sc);
-      packed[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+      const uint32_t lo = h ? raw[i].z : raw[i].x, hi = h ? raw[i].w : raw[i].y;
+      v[h][0] = bf16_to_f32(lo & 0xFFFFu);
+      v[h][1] = __uint_as_float(lo & 0xFFFF0000u);
+      v[h][2] = bf16_to_f32(hi & 0xFFFFu);
+      v[h][3] = __uint_as_float(hi & 0xFFFF0000u);
     }
-    *reinterpret_cast<uint2*>(q + base + (int64_t)i * 16 * K) = make_uint2(packed[0], packed[1]);
+    uint32_t need = ok ? 0u : 1u;
+    uint32_t packed[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) packed[h] = quantize4_fast(v[h], rs, need);
+    if (__builtin_expect(need != 0u, 0)) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) packed[h] = quantize4_exact(v[h], sc);
+    }
+    *reinterpret_cast<uint2 *>(q + base + (int64_t)i * 16 * K) = make_uint2(packed[0], packed[1]);
   }
 }
 
