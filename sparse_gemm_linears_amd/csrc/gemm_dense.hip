@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "gemm_common.hpp"
+#include "gemm_decode.hpp"
 #include "launch.hpp"
 
 namespace fp8lin {
@@ -195,109 +196,18 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
 
 // ============================================================ decode kernel ==
 
-// RT row tiles of 16 weight rows per workgroup, CT column tiles of 16 tokens
-// (M <= 16*CT), NW waves splitting the K blocks round-robin.
-template <int RT, int CT, int NW>
-__global__ __launch_bounds__(NW * 64) void dense_decode_kernel(const uint8_t *__restrict__ xq,
-                                                               const float *__restrict__ xs,
-                                                               const uint8_t *__restrict__ wq,
-                                                               const float *__restrict__ ws, int M, int N, int K,
-                                                               uint16_t *__restrict__ y) {
-  static_assert(128 % (16 * RT) == 0, "a workgroup's rows must sit in one 128-row scale block");
-  __shared__ v4f red[NW > 1 ? NW - 1 : 1][RT * CT][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, lr = lane & 15;
-  const int KB = K / kGroup;
-  const int n0 = blockIdx.x * 16 * RT;
-  const float *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
-
-  const uint8_t *wrow[RT];
-#pragma unroll
-  for (int r = 0; r < RT; r++) wrow[r] = wq + (int64_t)(n0 + 16 * r + lr) * K;
-  const uint8_t *xrow[CT];
-  const float *srow[CT];
-#pragma unroll
-  for (int c = 0; c < CT; c++) {
-    const int m = min(16 * c + lr, M - 1);
-    xrow[c] = xq + (int64_t)m * K;
-    srow[c] = xs + (int64_t)m * KB;
+// Weight operand of the decode kernel: 32 bytes of one row's K block per lane.
+struct DenseWeight {
+  typedef v8i Frag;
+  const uint8_t *wq;
+  int K;
+  __device__ __forceinline__ Frag load(int64_t row, int kb, int g) const {
+    return load_frag_global(wq + row * K + (int64_t)kb * kGroup, g);
   }
-
-  v4f acc[RT][CT];
-#pragma unroll
-  for (int r = 0; r < RT; r++)
-#pragma unroll
-    for (int c = 0; c < CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  v8i a_cur[RT], b_cur[CT];
-  float s_cur[CT], sw_cur = 0.f;
-  auto load = [&](int kb, v8i(&a)[RT], v8i(&b)[CT], float(&s)[CT], float &sw) {
-    const int64_t off = (int64_t)kb * kGroup;
-#pragma unroll
-    for (int r = 0; r < RT; r++) a[r] = load_frag_global(wrow[r] + off, g);
-#pragma unroll
-    for (int c = 0; c < CT; c++) {
-      b[c] = load_frag_global(xrow[c] + off, g);
-      s[c] = srow[c][kb];
-    }
-    sw = ws_row[kb];
-  };
-
-  int kb = wave;
-  if (kb < KB) load(kb, a_cur, b_cur, s_cur, sw_cur);
-  for (; kb < KB; kb += NW) {
-    v8i a_nxt[RT], b_nxt[CT];
-    float s_nxt[CT], sw_nxt = 0.f;
-    const bool more = kb + NW < KB;
-    if (more) load(kb + NW, a_nxt, b_nxt, s_nxt, sw_nxt);
-#pragma unroll
-    for (int c = 0; c < CT; c++) {
-      const float scl = s_cur[c] * sw_cur;
-#pragma unroll
-      for (int r = 0; r < RT; r++) {
-        const v4f p = mfma_16x16x128_fp8(a_cur[r], b_cur[c], v4f{0.f, 0.f, 0.f, 0.f});
-        acc[r][c] += scl * p;
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int r = 0; r < RT; r++) a_cur[r] = a_nxt[r];
-#pragma unroll
-      for (int c = 0; c < CT; c++) {
-        b_cur[c] = b_nxt[c];
-        s_cur[c] = s_nxt[c];
-      }
-      sw_cur = sw_nxt;
-    }
+  __device__ __forceinline__ v4f mma(const Frag &a, const v8i &b) const {
+    return mfma_16x16x128_fp8(a, b, v4f{0.f, 0.f, 0.f, 0.f});
   }
-
-  if (NW > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int r = 0; r < RT; r++)
-#pragma unroll
-        for (int c = 0; c < CT; c++) red[wave - 1][r * CT + c][lane] = acc[r][c];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < NW - 1; w++)
-#pragma unroll
-      for (int r = 0; r < RT; r++)
-#pragma unroll
-        for (int c = 0; c < CT; c++) acc[r][c] += red[w][r * CT + c][lane];
-  }
-#pragma unroll
-  for (int c = 0; c < CT; c++) {
-    const int m = 16 * c + lr;
-    if (m >= M) continue;
-#pragma unroll
-    for (int r = 0; r < RT; r++) {
-      const int n = n0 + 16 * r + 4 * g;
-      *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = pack_bf16x4(acc[r][c]);
-    }
-  }
-}
+};
 
 // ================================================================ dispatch ==
 
@@ -315,20 +225,35 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
   return hipGetLastError();
 }
 
-template <int RT, int CT, int NW>
+template <int RT, int CT, int NW, int D>
 static hipError_t launch_decode(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int M, int N,
                                 int K, uint16_t *y, hipStream_t stream) {
-  hipLaunchKernelGGL((dense_decode_kernel<RT, CT, NW>), dim3(N / (16 * RT)), dim3(NW * 64), 0, stream, xq, xs, wq,
-                     ws, M, N, K, y);
+  hipLaunchKernelGGL((decode_kernel<DenseWeight, RT, CT, NW, D>), dim3(N / (16 * RT)), dim3(NW * 64), 0, stream,
+                     DenseWeight{wq, K}, xq, xs, ws, M, N, K, y);
   return hipGetLastError();
+}
+
+
+// Decode configuration (measured on MI355X over the Llama-3-8B shapes): more
+// rows per workgroup when N is large enough to keep every CU busy, since each
+// workgroup re-reads the M x K activations from L2.
+template <int CT>
+static hipError_t launch_decode_for(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int M,
+                                    int N, int K, uint16_t *y, hipStream_t stream) {
+  if constexpr (CT == 1)
+    if (M <= 4) return launch_decode<1, CT, 16, 2>(xq, xs, wq, ws, M, N, K, y, stream);
+  if constexpr (CT <= 2)
+    if (N >= 16384) return launch_decode<4, CT, 8, 2>(xq, xs, wq, ws, M, N, K, y, stream);
+  if (N >= 6144) return launch_decode<2, CT, 8, 2>(xq, xs, wq, ws, M, N, K, y, stream);
+  return launch_decode<1, CT, 8, 1>(xq, xs, wq, ws, M, N, K, y, stream);
 }
 
 hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
                              int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (m <= 16) return launch_decode<1, 1, 8>(xq, xs, wq, ws, m, n, k, y, stream);
-  if (m <= 32) return launch_decode<1, 2, 8>(xq, xs, wq, ws, m, n, k, y, stream);
-  if (m <= 64) return launch_decode<1, 4, 8>(xq, xs, wq, ws, m, n, k, y, stream);
+  if (m <= 16) return launch_decode_for<1>(xq, xs, wq, ws, m, n, k, y, stream);
+  if (m <= 32) return launch_decode_for<2>(xq, xs, wq, ws, m, n, k, y, stream);
+  if (m <= 64) return launch_decode_for<4>(xq, xs, wq, ws, m, n, k, y, stream);
   return launch_tile<256, 256, 2, 4>(xq, xs, wq, ws, m, n, k, y, stream);
 }
 

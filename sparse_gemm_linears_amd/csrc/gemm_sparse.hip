@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "gemm_common.hpp"
+#include "gemm_decode.hpp"
 #include "launch.hpp"
 
 namespace fp8lin {
@@ -49,7 +50,8 @@ struct SparseTile {
 };
 
 // SB: K blocks per token-scale load (4 when K/128 is a multiple of 4, else 1).
-template <int BN, int BM, int WN, int WM, int SB>
+// CR: the next K block's copies are issued across the first CR row tiles.
+template <int BN, int BM, int WN, int WM, int SB, int CR>
 __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t *__restrict__ xq,
                                                                  const float *__restrict__ xs,
                                                                  const uint8_t *__restrict__ wv,
@@ -94,24 +96,32 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
   TokenScales<BM, SB> scales;
   scales.init(lds_s, xs, M, KB, m_base, tid);
 
-  auto issue_copies = [&](int kb, int st) {
-#pragma unroll
-    for (int i = 0; i < C::kVCopies; i++) {
-      const int r0 = (i * C::kWaves + wave) * 16;
+  // copy j of a K block: 0 .. kVCopies-1 values, kVCopies the index words
+  // (waves below kMCopyWaves), then the token panel
+  auto issue_copy = [&](int kb, int st, int j) {
+    if (j < C::kVCopies) {
+      const int r0 = (j * C::kWaves + wave) * 16;
       const uint8_t *base = wv + (int64_t)min(n_base + r0, N - 16) * vrow_bytes + (int64_t)kb * 64;
       copy16_global_to_lds(base + v_lane, (st ? lds_v1 : lds_v0) + r0 * 64);
-    }
-    if (wave < C::kMCopyWaves) {
-      const int r0 = wave * 64;
-      const uint8_t *base = wm + (int64_t)min(n_base + r0, N - 64) * mrow_bytes + (int64_t)kb * 16;
-      copy16_global_to_lds(base + m_lane, (st ? lds_m1 : lds_m0) + r0 * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < C::kBCopies; i++) {
+    } else if (j == C::kVCopies) {
+      if (wave < C::kMCopyWaves) {
+        const int r0 = wave * 64;
+        const uint8_t *base = wm + (int64_t)min(n_base + r0, N - 64) * mrow_bytes + (int64_t)kb * 16;
+        copy16_global_to_lds(base + m_lane, (st ? lds_m1 : lds_m0) + r0 * 16);
+      }
+    } else {
+      const int i = j - C::kVCopies - 1;
       const int r0 = (i * C::kWaves + wave) * 8;
       const uint8_t *base = xq + (int64_t)min(m_base + r0, M - 1) * K + (int64_t)kb * kGroup;
       copy16_global_to_lds(base + b_lane[i], (st ? lds_b1 : lds_b0) + r0 * 128);
     }
+  };
+  constexpr int kCopies = C::kVCopies + 1 + C::kBCopies;
+  constexpr int kCopyRows = CR < C::RT ? CR : C::RT;  // copies are spread over the first kCopyRows row tiles
+  constexpr int kCopiesPerRow = (kCopies + kCopyRows - 1) / kCopyRows;
+  auto issue_copies = [&](int kb, int st) {
+#pragma unroll
+    for (int j = 0; j < kCopies; j++) issue_copy(kb, st, j);
   };
 
   const int fr_lo = lr * 128 + ((g ^ swz(lr)) << 4);
@@ -133,7 +143,6 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
     constexpr int ST = decltype(st_tag)::value;
     const bool more = kb + 1 < KB;
     const bool scale_load = (kb % SB == 0) && (kb + SB < KB);
-    if (more) issue_copies(kb + 1, ST ^ 1);
     if (scale_load) scales.load(kb / SB + 1);
     const float sw = ws_row[kb];
     v8i bf[C::CT];
@@ -150,6 +159,10 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
     v4f p_prev[C::CT];
 #pragma unroll
     for (int r = 0; r < C::RT; r++) {
+      if (more && r < kCopyRows) {
+#pragma unroll
+        for (int j = r * kCopiesPerRow; j < (r + 1) * kCopiesPerRow && j < kCopies; j++) issue_copy(kb + 1, ST ^ 1, j);
+      }
       const v4i af = af_next;
       const int ix = ix_next;
       if (r + 1 < C::RT) {
@@ -203,122 +216,24 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
 
 // ============================================================ decode kernel ==
 
-template <int RT, int CT, int NW>
-__global__ __launch_bounds__(NW * 64) void sparse_decode_kernel(const uint8_t *__restrict__ xq,
-                                                                const float *__restrict__ xs,
-                                                                const uint8_t *__restrict__ wv,
-                                                                const uint8_t *__restrict__ wm,
-                                                                const float *__restrict__ ws, int M, int N, int K,
-                                                                uint16_t *__restrict__ y) {
-  static_assert(128 % (16 * RT) == 0, "a workgroup's rows must sit in one 128-row scale block");
-  __shared__ v4f red[NW > 1 ? NW - 1 : 1][RT * CT][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, lr = lane & 15;
-  const int KB = K / kGroup;
-  const int n0 = blockIdx.x * 16 * RT;
-  const float *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
-
-  const uint8_t *vrow[RT];
-  const uint8_t *mrow[RT];
-#pragma unroll
-  for (int r = 0; r < RT; r++) {
-    const int64_t n = n0 + 16 * r + lr;
-    vrow[r] = wv + n * (K / 2) + 16 * g;
-    mrow[r] = wm + n * (K / 8) + 4 * g;
+// Weight operand of the decode kernel: 16 value bytes and one index word of
+// one row's K block per lane.
+struct SparseFrag {
+  v4i v;
+  int idx;
+};
+struct SparseWeight {
+  typedef SparseFrag Frag;
+  const uint8_t *wv, *wm;
+  int K;
+  __device__ __forceinline__ Frag load(int64_t row, int kb, int g) const {
+    SparseFrag f;
+    f.v = make_v4i(ldg16(wv + row * (K / 2) + (int64_t)kb * 64 + 16 * g));
+    f.idx = *reinterpret_cast<const int *>(wm + row * (K / 8) + (int64_t)kb * 16 + 4 * g);
+    return f;
   }
-  const uint8_t *xrow[CT];
-  const float *srow[CT];
-#pragma unroll
-  for (int c = 0; c < CT; c++) {
-    const int m = min(16 * c + lr, M - 1);
-    xrow[c] = xq + (int64_t)m * K;
-    srow[c] = xs + (int64_t)m * KB;
-  }
-
-  v4f acc[RT][CT];
-#pragma unroll
-  for (int r = 0; r < RT; r++)
-#pragma unroll
-    for (int c = 0; c < CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  v4i a_cur[RT];
-  int i_cur[RT];
-  v8i b_cur[CT];
-  float s_cur[CT], sw_cur = 0.f;
-  auto load = [&](int kb, v4i(&a)[RT], int(&ix)[RT], v8i(&b)[CT], float(&s)[CT], float &sw) {
-#pragma unroll
-    for (int r = 0; r < RT; r++) {
-      a[r] = make_v4i(ldg16(vrow[r] + (int64_t)kb * 64));
-      ix[r] = *reinterpret_cast<const int *>(mrow[r] + (int64_t)kb * 16);
-    }
-#pragma unroll
-    for (int c = 0; c < CT; c++) {
-      b[c] = load_frag_global(xrow[c] + (int64_t)kb * kGroup, g);
-      s[c] = srow[c][kb];
-    }
-    sw = ws_row[kb];
-  };
-
-  int kb = wave;
-  if (kb < KB) load(kb, a_cur, i_cur, b_cur, s_cur, sw_cur);
-  for (; kb < KB; kb += NW) {
-    v4i a_nxt[RT];
-    int i_nxt[RT];
-    v8i b_nxt[CT];
-    float s_nxt[CT], sw_nxt = 0.f;
-    const bool more = kb + NW < KB;
-    if (more) load(kb + NW, a_nxt, i_nxt, b_nxt, s_nxt, sw_nxt);
-#pragma unroll
-    for (int c = 0; c < CT; c++) {
-      const float scl = s_cur[c] * sw_cur;
-#pragma unroll
-      for (int r = 0; r < RT; r++) {
-        const v4f p = smfmac_16x16x128_fp8(a_cur[r], b_cur[c], i_cur[r]);
-        acc[r][c] += scl * p;
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int r = 0; r < RT; r++) {
-        a_cur[r] = a_nxt[r];
-        i_cur[r] = i_nxt[r];
-      }
-#pragma unroll
-      for (int c = 0; c < CT; c++) {
-        b_cur[c] = b_nxt[c];
-        s_cur[c] = s_nxt[c];
-      }
-      sw_cur = sw_nxt;
-    }
-  }
-
-  if (NW > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int r = 0; r < RT; r++)
-#pragma unroll
-        for (int c = 0; c < CT; c++) red[wave - 1][r * CT + c][lane] = acc[r][c];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < NW - 1; w++)
-#pragma unroll
-      for (int r = 0; r < RT; r++)
-#pragma unroll
-        for (int c = 0; c < CT; c++) acc[r][c] += red[w][r * CT + c][lane];
-  }
-#pragma unroll
-  for (int c = 0; c < CT; c++) {
-    const int m = 16 * c + lr;
-    if (m >= M) continue;
-#pragma unroll
-    for (int r = 0; r < RT; r++) {
-      const int n = n0 + 16 * r + 4 * g;
-      *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = pack_bf16x4(acc[r][c]);
-    }
-  }
-}
+  __device__ __forceinline__ v4f mma(const Frag &a, const v8i &b) const { return smfmac_16x16x128_fp8(a.v, b, a.idx); }
+};
 
 // ================================================================ dispatch ==
 
@@ -328,28 +243,43 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
   using C = SparseTile<BN, BM, WN, WM>;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   if ((K / kGroup) % 4 == 0)
-    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 4, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
                        stream, xq, xs, wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4);
   else
-    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 1>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 1, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
                        stream, xq, xs, wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4);
   return hipGetLastError();
 }
 
-template <int RT, int CT, int NW>
+template <int RT, int CT, int NW, int D>
 static hipError_t launch_decode(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
                                 const float *ws, int M, int N, int K, uint16_t *y, hipStream_t stream) {
-  hipLaunchKernelGGL((sparse_decode_kernel<RT, CT, NW>), dim3(N / (16 * RT)), dim3(NW * 64), 0, stream, xq, xs, wv,
-                     wm, ws, M, N, K, y);
+  hipLaunchKernelGGL((decode_kernel<SparseWeight, RT, CT, NW, D>), dim3(N / (16 * RT)), dim3(NW * 64), 0, stream,
+                     SparseWeight{wv, wm, K}, xq, xs, ws, M, N, K, y);
   return hipGetLastError();
+}
+
+
+// Decode configuration (measured on MI355X over the Llama-3-8B shapes): more
+// rows per workgroup when N is large enough to keep every CU busy, since each
+// workgroup re-reads the M x K activations from L2.
+template <int CT>
+static hipError_t launch_decode_for(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
+                                    const float *ws, int M, int N, int K, uint16_t *y, hipStream_t stream) {
+  if constexpr (CT == 1)
+    if (M <= 4) return launch_decode<1, CT, 16, 2>(xq, xs, wv, wm, ws, M, N, K, y, stream);
+  if constexpr (CT <= 2)
+    if (N >= 16384) return launch_decode<4, CT, 8, 2>(xq, xs, wv, wm, ws, M, N, K, y, stream);
+  if (N >= 6144) return launch_decode<2, CT, 8, 2>(xq, xs, wv, wm, ws, M, N, K, y, stream);
+  return launch_decode<1, CT, 8, 1>(xq, xs, wv, wm, ws, M, N, K, y, stream);
 }
 
 hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
                               const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (m <= 16) return launch_decode<1, 1, 8>(xq, xs, wv, wm, ws, m, n, k, y, stream);
-  if (m <= 32) return launch_decode<1, 2, 8>(xq, xs, wv, wm, ws, m, n, k, y, stream);
-  if (m <= 64) return launch_decode<1, 4, 8>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+  if (m <= 16) return launch_decode_for<1>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+  if (m <= 32) return launch_decode_for<2>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+  if (m <= 64) return launch_decode_for<4>(xq, xs, wv, wm, ws, m, n, k, y, stream);
   return launch_tile<256, 256, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, stream);
 }
 
