@@ -33,6 +33,32 @@ if ROOT not in sys.path:
 METRIC = "FP8 block-scaled GEMM TFLOP/s & % MFMA peak (dense, 2:4); decode-M HBM GB/s"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+CALIB_BYTES = 256 << 20    # size of the traffic-calibration copy
+
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
+# of this script (FETCH_SIZE, then WRITE_SIZE; profiles/
+# fp8_block_gemm_gate_up_m4096_traffic.md has the commands and the readings),
+# each scaled by the same counter's reading for the calibration copy.  It is
+# reported only while the kernel's sources hash to the value it was taken on.
+TRAFFIC = {"bytes_per_launch": 948957387,
+           "sources_sha256": "b48f896a844b5ef2536db3a61294e0f49b6a11e808661ad5cd1381b54803552c"}
+TRAFFIC_SOURCES = ("sparse_gemm_linears_amd/csrc/gemm_dense.hip", "sparse_gemm_linears_amd/csrc/gemm_common.hpp",
+                   "sparse_gemm_linears_amd/csrc/device_common.hpp")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    if TRAFFIC is None or TRAFFIC["sources_sha256"] != kernel_sources_sha256():
+        return None
+    return TRAFFIC["bytes_per_launch"]
 
 
 def parse_args():
@@ -89,7 +115,7 @@ def main():
 
     kernels = ("quant_act", "quant_wblock", "prune24", "dense_gemm", "sparse_gemm")
 
-    def step(events=None):
+    def step(events=None, dominant=None):
         for li, L in enumerate(layers):
             calls = (
                 lambda: sgl.fp8_quant_act(L["x"], L["xq"], L["xs"]),
@@ -101,21 +127,41 @@ def main():
             for ki, f in enumerate(calls):
                 if events is not None:
                     events[li][ki][0].record()
-                f()
+                if dominant is not None and li == dominant[0] and ki == 3:
+                    dominant[1][0].record()
+                    f()
+                    dominant[1][1].record()
+                else:
+                    f()
                 if events is not None:
                     events[li][ki][1].record()
+
+    # Calibration copy for the HBM traffic counters: a plain device-to-device
+    # copy of CALIB_BYTES, whose FETCH_SIZE / WRITE_SIZE readings under
+    # rocprofv3 --pmc give the scale from counter KiB to bytes moved.
+    calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # ------------------------------------------------- timed whole steps ----
+    # The dominant kernel (dense gate/up GEMM) is bracketed by events inside
+    # the timed steps, on the stream the library launches on.
+    gi = [L["name"] for L in layers].index("gate_up")
+    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(dominant=(gi, dom_ev[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    dom_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in dom_ev]))
 
     # ----------------------------------- per-kernel times (HIP events) ------
     durations = {(li, ki): [] for li in range(len(layers)) for ki in range(len(kernels))}
@@ -163,16 +209,16 @@ def main():
     gemm_flops = dense_flops + sparse_flops
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the dense gate/up GEMM
-    gi = [L["name"] for L in layers].index("gate_up")
+    # dominant kernel: the dense gate/up GEMM, timed inside the timed steps
     Lg = layers[gi]
-    dom_us = float(np.mean(durations[(gi, kernels.index("dense_gemm"))]))
     dom_flops = 2 * M * Lg["N"] * Lg["K"]
     achieved = dom_flops / dom_us / 1e6
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
                 "kernel": "fp8_block_gemm dense tile kernel, gate_up 4096x28672x4096",
-                "avg_launch_us": round(dom_us, 2), "flops_per_launch": dom_flops}
+                "avg_launch_us": round(dom_us, 2), "flops_per_launch": dom_flops,
+                "algorithmic_bytes_per_launch": M * Lg["K"] + Lg["N"] * Lg["K"] + 4 * M * (Lg["K"] // 128)
+                + 4 * (Lg["N"] // 128) * (Lg["K"] // 128) + 2 * M * Lg["N"]}
 
     # free the prefill working set before the decode measurements
     del layers

@@ -38,7 +38,7 @@ PREFILL_M = 4096
 SPARSE_M = (16, 4096)
 DSV3_M = 8192
 
-# The five workloads, numbered as in the task description.
+# The five workloads: the single small linear, Llama-3-8B decode, prefill and 2:4, DeepSeek-V3 FFN.
 WORKLOADS = {
     "single_linear_16x512x512": dict(shapes=[("linear", 512, 512)], M=(16,), dist="normal", outliers=False,
                                      w_std=0.02, sparse=False),
