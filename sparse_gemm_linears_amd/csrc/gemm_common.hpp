@@ -64,9 +64,33 @@ __device__ __forceinline__ void copy16_global_to_lds(const void *src, void *lds_
   __builtin_amdgcn_global_load_lds((glb_void *)const_cast<void *>(src), (lds_void *)lds_wave_base, 16, 0, 0);
 }
 
+// Raw buffer resources (byte-addressed, no stride).  A load whose offset lies
+// at or past `bytes` returns zeros.  Offsets are a per-lane 32-bit VGPR plus a
+// wave-uniform 32-bit SGPR, so walking K costs scalar adds only.  The dword-3
+// value 0x00020000 is the gfx9 raw-buffer format (32-bit data, no swizzle).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer into registers.
+__device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+// 16 bytes per lane from a buffer into LDS (buffer_load_dwordx4 ... lds): the
+// 64 lanes write 1 KB at `lds_wave_base` in lane order.
+__device__ __forceinline__ void buffer_copy16_to_lds(rsrc_t r, uint32_t voff, uint32_t soff, void *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
 // Wait until this wave's outstanding global loads (the LDS copies included)
-// have landed.
-__device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// have landed: s_waitcnt vmcnt(0) (expcnt and lgkmcnt at their maxima, 7 and
+// 15).  Issued through the builtin so that the compiler's own wait insertion
+// knows the counter is drained and adds no later waits for these loads.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Pins a value in VGPRs at this point of the program: the computation that
 // produces it cannot be sunk below the pin (keeps the partial-product scaling

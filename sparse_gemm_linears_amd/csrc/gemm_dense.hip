@@ -98,10 +98,6 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
   constexpr int kCopies = C::kACopies + C::kBCopies;
   constexpr int kCopyRows = CR < C::RT ? CR : C::RT;  // copies are spread over the first kCopyRows row tiles
   constexpr int kCopiesPerRow = (kCopies + kCopyRows - 1) / kCopyRows;
-  auto issue_copies = [&](int kb, int st) {
-#pragma unroll
-    for (int j = 0; j < kCopies; j++) issue_copy(kb, st, j);
-  };
 
   // per-lane fragment read offsets (row lr of a 16-row slab, chunks g and g+4)
   const int fr_lo = lr * 128 + ((g ^ swz(lr)) << 4);
@@ -118,42 +114,53 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
   const int nb_wave = min((n_base + wn0) / kGroup, NB - 1);
   const float *ws_row = ws + (int64_t)nb_wave * KB;
 
-  // One K step on stage ST: the next block's copies (and, once per scale
-  // group, the next group's token scales) are in flight while the MFMAs of
-  // this one run.  The partial of each 16x16 tile is scaled into its
-  // accumulator while the MFMA of the following tile executes.
+  // Token fragments live in registers one K step ahead: bx[ST] holds this
+  // step's, and the next step's are read from LDS during row tiles
+  // kBReadRow.. of this step.  Token copies therefore run two steps ahead (the
+  // stage they overwrite was drained into registers a step earlier) and the
+  // weight copies one step ahead; every copy still has a whole step to land.
+  v8i bx[2][C::CT];
+  constexpr int kBReadRow = C::RT - C::CT;
+  auto read_b = [&](const uint8_t *Bt, v8i (&dst)[C::CT], int c) {
+    dst[c] = load_frag_at(Bt, b_lo, b_hi, c * 2048);
+  };
+
+  // One K step: A stage ST, B fragments in bx[ST].  The copies issued here
+  // (weights of kb+1 into A stage ST^1, tokens of kb+2 into B stage ST) and,
+  // once per scale group, the next token scales are in flight while the MFMAs
+  // run.  The partial of each 16x16 tile is scaled into its accumulator while
+  // the MFMA of the following tile executes.
   auto step = [&](int kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
-    const bool more = kb + 1 < KB;
+    const bool more_a = kb + 1 < KB, more_b = kb + 2 < KB;
     const bool scale_load = (kb % SB == 0) && (kb + SB < KB);
     if (scale_load) scales.load(kb / SB + 1);
     const float sw = ws_row[kb];
-    // Only the first A and B fragments are read up front; the other B
-    // fragments are read between the MFMAs of row tile 0 and each next A
-    // fragment during the MFMAs of the current row tile, so the waves leaving
-    // the barrier do not all queue on the LDS before their first MFMA.
     const uint8_t *At = ST ? lds_a1 : lds_a0;
-    const uint8_t *Bt = ST ? lds_b1 : lds_b0;
-    v8i bf[C::CT];
+    const uint8_t *Bn = ST ? lds_b0 : lds_b1;  // tokens of kb+1
     float scl[C::CT];
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
     v8i an = load_frag_at(At, a_lo, a_hi, 0);
-    bf[0] = load_frag_at(Bt, b_lo, b_hi, 0);
     v4f p_prev;
 #pragma unroll
     for (int r = 0; r < C::RT; r++) {
-      if (more && r < kCopyRows) {
+      if (r < kCopyRows) {
 #pragma unroll
-        for (int j = r * kCopiesPerRow; j < (r + 1) * kCopiesPerRow && j < kCopies; j++) issue_copy(kb + 1, ST ^ 1, j);
+        for (int j = r * kCopiesPerRow; j < (r + 1) * kCopiesPerRow && j < kCopies; j++) {
+          if (j < C::kACopies) {
+            if (more_a) issue_copy(kb + 1, ST ^ 1, j);
+          } else if (more_b) {
+            issue_copy(kb + 2, ST, j);
+          }
+        }
       }
       const v8i af = an;
       if (r + 1 < C::RT) an = load_frag_at(At, a_lo, a_hi, (r + 1) * 2048);
+      if (r >= kBReadRow && more_a) read_b(Bn, bx[ST ^ 1], r - kBReadRow);
 #pragma unroll
       for (int c = 0; c < C::CT; c++) {
-        if (r == 0) {
-          if (c + 1 < C::CT) bf[c + 1] = load_frag_at(Bt, b_lo, b_hi, (c + 1) * 2048);
-          scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
-        }
-        const v4f p = mfma_16x16x128_fp8(af, bf[c], v4f{0.f, 0.f, 0.f, 0.f});
+        const v4f p = mfma_16x16x128_fp8(af, bx[ST][c], v4f{0.f, 0.f, 0.f, 0.f});
         const int t = r * C::CT + c;
         if (t > 0) {
           const int pr = (t - 1) / C::CT, pc = (t - 1) % C::CT;
@@ -161,22 +168,30 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
           pin(acc[pr][pc]);
         }
         p_prev = p;
-        if (r == 0) __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     acc[C::RT - 1][C::CT - 1] += scl[C::CT - 1] * p_prev;
     pin(acc[C::RT - 1][C::CT - 1]);
-    if (more || scale_load) wait_global_loads();
+    if (more_a || scale_load) wait_global_loads();
     if (scale_load) scales.store(kb / SB + 1);
     __syncthreads();
   };
 
-  issue_copies(0, 0);
+  // prologue: weights of K block 0, tokens of K blocks 0 and 1
+#pragma unroll
+  for (int j = 0; j < kCopies; j++) issue_copy(0, 0, j);
+  if (KB > 1) {
+#pragma unroll
+    for (int j = C::kACopies; j < kCopies; j++) issue_copy(1, 1, j);
+  }
   scales.load(0);
   wait_global_loads();
   scales.store(0);
   __syncthreads();
+#pragma unroll
+  for (int c = 0; c < C::CT; c++) read_b(lds_b0, bx[0], c);
+  __syncthreads();  // B stage 0 is refilled by step 0
   for (int kb = 0; kb < KB; kb += 2) {
     step(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{});
