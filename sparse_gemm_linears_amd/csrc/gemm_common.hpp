@@ -74,6 +74,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Buffer resource over rows [row0, row0 + 128) of a panel of `row_bytes`-byte
+// rows starting at `panel`, clipped to the `rows_left` rows that exist: rows
+// past the matrix edge read as zeros (their results are never stored).  128
+// rows of at most 2^24 bytes keep every offset below 2^31.  The clamp goes
+// through readfirstlane so the resource stays in SGPRs (a VGPR resource
+// would make every load a loop over lanes).
+__device__ __forceinline__ rsrc_t panel_rows128(const uint8_t *panel, int rows_left, int row0, int row_bytes) {
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(128, rows_left - row0)));
+  return make_rsrc(panel + (int64_t)row0 * row_bytes, (uint32_t)rows * (uint32_t)row_bytes);
+}
+
 // 16 bytes per lane from a buffer into registers.
 __device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
   const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);

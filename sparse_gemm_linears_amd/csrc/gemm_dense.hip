@@ -30,7 +30,8 @@ struct DenseTile {
   static constexpr int RT = kWaveN / 16, CT = kWaveM / 16;
   static constexpr int kACopies = BN / 8 / kWaves, kBCopies = BM / 8 / kWaves;  // 1 KB = 8 rows per copy
   static constexpr int kATile = BN * 128, kBTile = BM * 128;
-  static_assert(BN % (8 * kWaves) == 0 && BM % (8 * kWaves) == 0, "tile / wave mismatch");
+  static_assert(BN == 256 && BM == 256, "panels are addressed as two 128-row halves");
+  static_assert(128 % (8 * kWaves) == 0, "copy slabs tile the 128-row halves");
   static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
   static_assert(kWaveN == 128, "a wave covers one 128-row weight scale block (and 256-byte epilogue rows)");
   static_assert(BM <= kThreads, "one thread per token scale");
@@ -66,34 +67,29 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
   const int m_base = tm * BM, n_base = tn * BN;
   const int wn0 = (wave / WM) * C::kWaveN, wm0 = (wave % WM) * C::kWaveM;
 
-  // Copy slab i of this wave covers tile rows r0 = (i*kWaves + wave)*8 .. +7;
+  // Copy slab i of this wave covers panel rows r0 = (i*kWaves + wave)*8 .. +7;
   // lane (cj, cp) writes LDS chunk position cp of row r0+cj, i.e. logical
-  // chunk cp ^ swz(r0+cj); r0 % 16 = 8*(wave % 2) for every i.
-  const int copy_chunk = 16 * (cp ^ swz(cj + 8 * (wave & 1)));
-  const uint32_t a_lane = (uint32_t)(cj * K + copy_chunk);
-  uint32_t b_lane[C::kBCopies];
-#pragma unroll
-  for (int i = 0; i < C::kBCopies; i++) {
-    const int r0 = m_base + (i * C::kWaves + wave) * 8;
-    b_lane[i] = (uint32_t)((min(r0 + cj, M - 1) - min(r0, M - 1)) * K + copy_chunk);
-  }
+  // chunk cp ^ swz(r0+cj); r0 % 16 = 8*(wave % 2) for every i.  Both panels
+  // have K-byte rows, so one per-lane offset serves every copy; the slab and
+  // the K block go into the scalar offset.
+  const uint32_t copy_voff = (uint32_t)((wave * 8 + cj) * K + 16 * (cp ^ swz(cj + 8 * (wave & 1))));
+  const uint8_t *wpanel = wq + (int64_t)n_base * K, *xpanel = xq + (int64_t)m_base * K;
+  const rsrc_t rw0 = panel_rows128(wpanel, N - n_base, 0, K), rw1 = panel_rows128(wpanel, N - n_base, 128, K);
+  const rsrc_t rx0 = panel_rows128(xpanel, M - m_base, 0, K), rx1 = panel_rows128(xpanel, M - m_base, 128, K);
   TokenScales<BM, SB> scales;
   scales.init(lds_s, xs, M, KB, m_base, tid);
 
   // One 128-wide K block of the weight and token panels into LDS stage `st`.
-  // Rows past the matrix edge re-read valid rows; their results are never stored.
   auto issue_copy = [&](int kb, int st, int j) {
-    const int64_t koff = (int64_t)kb * kGroup;
-    if (j < C::kACopies) {
-      const int r0 = (j * C::kWaves + wave) * 8;
-      const uint8_t *base = wq + (int64_t)min(n_base + r0, N - 8) * K + koff;
-      copy16_global_to_lds(base + a_lane, (st ? lds_a1 : lds_a0) + r0 * 128);
-    } else {
-      const int i = j - C::kACopies;
-      const int r0 = (i * C::kWaves + wave) * 8;
-      const uint8_t *base = xq + (int64_t)min(m_base + r0, M - 1) * K + koff;
-      copy16_global_to_lds(base + b_lane[i], (st ? lds_b1 : lds_b0) + r0 * 128);
-    }
+    constexpr int kSlab = 8 * C::kWaves;  // panel rows covered by one copy of every wave
+    const bool is_a = j < C::kACopies;
+    const int first = (is_a ? j : j - C::kACopies) * kSlab;  // panel row of wave 0's slab
+    const uint32_t soff = (uint32_t)kb * 128u + (uint32_t)(first % 128) * (uint32_t)K;
+    const int lds_off = (first + wave * 8) * 128;
+    if (is_a)
+      buffer_copy16_to_lds(first < 128 ? rw0 : rw1, copy_voff, soff, (st ? lds_a1 : lds_a0) + lds_off);
+    else
+      buffer_copy16_to_lds(first < 128 ? rx0 : rx1, copy_voff, soff, (st ? lds_b1 : lds_b0) + lds_off);
   };
   constexpr int kCopies = C::kACopies + C::kBCopies;
   constexpr int kCopyRows = CR < C::RT ? CR : C::RT;  // copies are spread over the first kCopyRows row tiles
