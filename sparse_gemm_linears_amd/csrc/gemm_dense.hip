@@ -138,7 +138,7 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
 #pragma unroll
     for (int c = 0; c < C::CT; c++) scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
     v8i an = load_frag_at(At, a_lo, a_hi, 0);
-    v4f p_prev;
+    v4f p_prev, p_prev2;
 #pragma unroll
     for (int r = 0; r < C::RT; r++) {
       if (r < kCopyRows) {
@@ -157,16 +157,21 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
 #pragma unroll
       for (int c = 0; c < C::CT; c++) {
         const v4f p = mfma_16x16x128_fp8(af, bx[ST][c], v4f{0.f, 0.f, 0.f, 0.f});
+        // scale the partial of two MFMAs back: its result is ready, so the
+        // FMAs issue without hazard waits while this MFMA runs
         const int t = r * C::CT + c;
-        if (t > 0) {
-          const int pr = (t - 1) / C::CT, pc = (t - 1) % C::CT;
-          acc[pr][pc] += scl[pc] * p_prev;
+        if (t > 1) {
+          const int pr = (t - 2) / C::CT, pc = (t - 2) % C::CT;
+          acc[pr][pc] += scl[pc] * p_prev2;
           pin(acc[pr][pc]);
         }
+        p_prev2 = p_prev;
         p_prev = p;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    acc[C::RT - 1][C::CT - 2] += scl[C::CT - 2] * p_prev2;
+    pin(acc[C::RT - 1][C::CT - 2]);
     acc[C::RT - 1][C::CT - 1] += scl[C::CT - 1] * p_prev;
     pin(acc[C::RT - 1][C::CT - 1]);
     if (more_a || scale_load) wait_global_loads();
