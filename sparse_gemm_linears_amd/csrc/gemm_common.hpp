@@ -158,6 +158,9 @@ struct TokenScales {
 // by row), reads it back as whole rows and stores 256 contiguous bytes per
 // row.  `acc_c` holds the RT 16x16 accumulators of token tile c (lane: token
 // l%16, rows 4*(l/16)..+3 of each row tile).  Requires 16*RT*2 == 256.
+// The stores are non-temporal: Y is written once and not read back by this
+// kernel, and streaming it past the L2 keeps the end-of-tile write burst from
+// stalling the next tile's operand loads.
 template <int RT>
 __device__ __forceinline__ void store_token_tile(uint8_t *scratch, const v4f (&acc_c)[RT], uint16_t *y, int M,
                                                  int N, int m0, int n0, int lane) {
@@ -171,9 +174,9 @@ __device__ __forceinline__ void store_token_tile(uint8_t *scratch, const v4f (&a
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int row = 4 * j + g;  // lane l reads row 4j + l/16, chunk l%16
-    const uint4 v = *reinterpret_cast<const uint4 *>(scratch + row * 256 + ((lr ^ row) << 4));
+    const v4i v = *reinterpret_cast<const v4i *>(scratch + row * 256 + ((lr ^ row) << 4));
     const int m = m0 + row, n = n0 + 8 * lr;
-    if (m < M && n < N) *reinterpret_cast<uint4 *>(y + (int64_t)m * N + n) = v;
+    if (m < M && n < N) __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(y + (int64_t)m * N + n));
   }
 }
 

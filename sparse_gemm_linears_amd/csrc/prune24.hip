@@ -21,13 +21,15 @@ struct Kept2 {
 };
 
 // SC: score type (uint32 |w| bit patterns for magnitude, exact fp64 products
-// for activation-aware).  ge[i][j] (i < j) says position i ranks before
-// position j (ties go to the lower index); a position is kept when fewer than
-// two positions rank before it.
+// for activation-aware).  gij (i < j) says position i ranks before position j
+// (ties go to the lower index); a position is kept when fewer than two
+// positions rank before it.  The values come in as four scalars and are picked
+// with selects: from an array, the compiler turns the pick into an indexed load
+// from scratch memory.
 template <typename SC>
-__device__ __forceinline__ Kept2 select_two(const float (&v)[4], const SC (&sc)[4]) {
-  const uint32_t g01 = sc[0] >= sc[1], g02 = sc[0] >= sc[2], g03 = sc[0] >= sc[3];
-  const uint32_t g12 = sc[1] >= sc[2], g13 = sc[1] >= sc[3], g23 = sc[2] >= sc[3];
+__device__ __forceinline__ Kept2 select_two(float v0, float v1, float v2, float v3, SC s0, SC s1, SC s2, SC s3) {
+  const uint32_t g01 = s0 >= s1, g02 = s0 >= s2, g03 = s0 >= s3;
+  const uint32_t g12 = s1 >= s2, g13 = s1 >= s3, g23 = s2 >= s3;
   // number of positions ranking before each position
   const uint32_t a0 = 3u - (g01 + g02 + g03);
   const uint32_t a1 = g01 + 2u - (g12 + g13);
@@ -35,8 +37,8 @@ __device__ __forceinline__ Kept2 select_two(const float (&v)[4], const SC (&sc)[
   const uint32_t a3 = g03 + g13 + g23;
   const bool k0 = a0 < 2u, k1 = a1 < 2u, k2 = a2 < 2u, k3 = a3 < 2u;
   Kept2 r;
-  r.first = k0 ? v[0] : (k1 ? v[1] : v[2]);
-  r.second = k3 ? v[3] : (k2 ? v[2] : v[1]);
+  r.first = k0 ? v0 : (k1 ? v1 : v2);
+  r.second = k3 ? v3 : (k2 ? v2 : v1);
   const uint32_t i0 = k0 ? 0u : (k1 ? 1u : 2u);
   const uint32_t i1 = k3 ? 3u : (k2 ? 2u : 1u);
   r.nib = i0 | (i1 << 2);
@@ -72,16 +74,14 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       const uint32_t lo = r[2 * h], hi = r[2 * h + 1];
-      const float v[4] = {bf16_to_f32(lo & 0xFFFFu), __uint_as_float(lo & 0xFFFF0000u), bf16_to_f32(hi & 0xFFFFu),
-                          __uint_as_float(hi & 0xFFFF0000u)};
+      const float v0 = bf16_to_f32(lo & 0xFFFFu), v1 = __uint_as_float(lo & 0xFFFF0000u);
+      const float v2 = bf16_to_f32(hi & 0xFFFFu), v3 = __uint_as_float(hi & 0xFFFF0000u);
       if constexpr (AWARE) {
-        double sc[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) sc[j] = fabs((double)v[j]) * c[4 * h + j];  // exact in fp64
-        kept[i][h] = select_two(v, sc);
+        // |w| * c is exact in fp64 (8 + 24 significant bits)
+        kept[i][h] = select_two(v0, v1, v2, v3, fabs((double)v0) * c[4 * h], fabs((double)v1) * c[4 * h + 1],
+                                fabs((double)v2) * c[4 * h + 2], fabs((double)v3) * c[4 * h + 3]);
       } else {
-        const uint32_t sc[4] = {lo & 0x7FFFu, (lo >> 16) & 0x7FFFu, hi & 0x7FFFu, (hi >> 16) & 0x7FFFu};
-        kept[i][h] = select_two(v, sc);
+        kept[i][h] = select_two(v0, v1, v2, v3, lo & 0x7FFFu, (lo >> 16) & 0x7FFFu, hi & 0x7FFFu, (hi >> 16) & 0x7FFFu);
       }
       amax_bits = max(amax_bits, max(__float_as_uint(kept[i][h].first) & 0x7FFFFFFFu,
                                      __float_as_uint(kept[i][h].second) & 0x7FFFFFFFu));
