@@ -105,7 +105,12 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
     uint32_t word = quantize4_fast(kv, rs, need);
     if (__builtin_expect(need != 0u, 0)) word = quantize4_exact(kv, sc);
     *reinterpret_cast<uint32_t*>(vals + n * (K / 2) + kcol / 2) = word;
-    meta[n * (K / 8) + kcol / 8] = (uint8_t)(kept[i][0].nib | (kept[i][1].nib << 4));
+    // the 16 lanes of a row segment hold its 16 consecutive meta bytes: every
+    // fourth lane gathers four of them for one 4-byte store
+    const uint32_t mb = kept[i][0].nib | (kept[i][1].nib << 4);
+    const uint32_t m4 = mb | ((uint32_t)__shfl_down((int)mb, 1, 16) << 8) |
+                        ((uint32_t)__shfl_down((int)mb, 2, 16) << 16) | ((uint32_t)__shfl_down((int)mb, 3, 16) << 24);
+    if ((t & 3) == 0) *reinterpret_cast<uint32_t*>(meta + n * (K / 8) + kcol / 8) = m4;
   }
 }
 
