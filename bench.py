@@ -245,9 +245,10 @@ def main():
 
 
 def bench_decode(sgl, si, torch, np, dev, bf16):
-    """Decode-M GEMMs: dense at M in {1,8,32,64}, 2:4 at M=16, each shape with
+    """Decode-M GEMMs: dense at M in {1,8,16,32,64}, 2:4 at M=16, each shape with
     enough weight copies (>= 1 GiB in total) that every call reads its weight
-    from HBM.  Each call is timed as a HIP-graph replay of back-to-back calls."""
+    from HBM; beside each, the fused-quantization call and the two-call path it
+    replaces.  Each call is timed as a HIP-graph replay of back-to-back calls."""
     res = {}
     for name, K, N in si.LLAMA3_8B:
         wq_bytes = N * K
@@ -263,16 +264,23 @@ def bench_decode(sgl, si, torch, np, dev, bf16):
             x = bf16(si.activations(M, K))
             xq, xs = sgl.fp8_quant_act(x)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            runs = {"dense": lambda i: sgl.fp8_block_gemm(xq, xs, dense_w[i][0], dense_w[i][1], y)}
+            # "dense"/"sparse": the GEMM on codes already quantized; "*_linear": the fused call on
+            # bf16 activations; "*_two_call": fp8_quant_act then the GEMM, the path the fused call replaces
+            runs = {"dense": lambda i: sgl.fp8_block_gemm(xq, xs, dense_w[i][0], dense_w[i][1], y),
+                    "dense_linear": lambda i: sgl.fp8_block_linear(x, dense_w[i][0], dense_w[i][1], y),
+                    "dense_two_call": lambda i: (sgl.fp8_quant_act(x, xq, xs),
+                                                 sgl.fp8_block_gemm(xq, xs, dense_w[i][0], dense_w[i][1], y))}
             if M == 16:
                 runs["sparse"] = lambda i: sgl.fp8_sparse24_gemm(xq, xs, *sparse_w[i], y)
+                runs["sparse_linear"] = lambda i: sgl.fp8_sparse24_linear(x, *sparse_w[i], y)
+                runs["sparse_two_call"] = lambda i: (sgl.fp8_quant_act(x, xq, xs),
+                                                     sgl.fp8_sparse24_gemm(xq, xs, *sparse_w[i], y))
             for kind, f in runs.items():
                 us = time_graph(torch, f, copies)
-                if kind == "dense":
-                    nbytes = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
-                else:
-                    nbytes = N * K // 2 + N * K // 8 + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) \
-                        + 2 * M * N
+                wbytes = N * K if kind.startswith("dense") else N * K // 2 + N * K // 8
+                # activation bytes: fp8 codes + scales for the GEMM, bf16 for the fused call
+                xbytes = 2 * M * K if kind.endswith("linear") else M * K + 4 * M * (K // 128)
+                nbytes = wbytes + 4 * (N // 128) * (K // 128) + xbytes + 2 * M * N
                 gbs = nbytes / us / 1e3
                 res[f"{name}.M{M}.{kind}"] = {"us": round(us, 2), "gbs": round(gbs, 1),
                                               "frac_hbm": round(gbs / 8000.0, 4)}

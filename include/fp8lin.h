@@ -21,7 +21,8 @@
  * Errors: on any error nothing is enqueued and every output is left untouched.
  *   FP8L_ERR_NULL    a required pointer is NULL;
  *   FP8L_ERR_SHAPE   M < 0, N <= 0, K <= 0, K % 128 != 0, N % 128 != 0, or a
- *                    dimension above 2^24, or a matrix above 2^36 elements;
+ *                    dimension above 2^24, or a matrix above 2^36 elements
+ *                    (and M > 64 for the two *_linear calls);
  *   FP8L_ERR_ALIGN   a pointer is not 16-byte aligned;
  *   FP8L_ERR_ALIAS   an output overlaps an input or another output;
  *   FP8L_ERR_DEVICE  the current HIP device is missing or is not gfx950;
@@ -130,6 +131,39 @@ fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq
 fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t *wvals,
                               const uint8_t *wmeta, const float *ws, int64_t M, int64_t N,
                               int64_t K, uint16_t *y, hipStream_t stream);
+
+/*
+ * Decode-sized linear layer on bf16 activations: fp8_quant_act and
+ * fp8_block_gemm in one kernel ("FP8 a granularite fine", intro bullets and
+ * section "Chemin rapide de DeepGEMM": the activations are quantized per token
+ * and group of 128 channels, dynamically, right before the block-scaled FP8
+ * GEMM; "FP8 Quantization" (TensorRT-LLM), section "Low Latency GEMM Plugin":
+ * small-batch FP8 GEMMs are latency-bound, and one launch less matters there).
+ *
+ *   x [M,K] bf16, M <= 64
+ *   wq [N,K] e4m3, ws [N/128,K/128] fp32   from fp8_quant_weight_block
+ *   y [M,N] bf16
+ * y is bit-identical to fp8_quant_act(x) followed by fp8_block_gemm on the
+ * resulting codes and scales: each workgroup quantizes the activations it
+ * reads with the same arithmetic, and the codes are never written out.
+ * M > 64 is FP8L_ERR_SHAPE: for a larger batch, quantize it once with
+ * fp8_quant_act and call fp8_block_gemm.
+ * Performance: every workgroup quantizes the activations it needs, so the
+ * fused call is faster than the two calls only while that work is small.
+ * Measured on MI355X (Llama-3-8B shapes, HIP graphs), one or two tokens save
+ * 0.2-2.5 us per call; from three tokens on the two-call path is faster.
+ */
+fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
+                             int64_t K, uint16_t *y, hipStream_t stream);
+
+/*
+ * The same fused decode-sized linear with a 2:4-compressed weight from
+ * prune24_compress; bit-identical to fp8_quant_act then fp8_sparse24_gemm.
+ *
+ *   x [M,K] bf16, M <= 64; wvals [N,K/2], wmeta [N,K/8], ws [N/128,K/128]; y [M,N] bf16
+ */
+fp8l_status fp8_sparse24_linear(const uint16_t *x, const uint8_t *wvals, const uint8_t *wmeta, const float *ws,
+                                int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
 
 /* Static, never NULL, English text for a status code. */
 const char *fp8lin_status_str(fp8l_status status);

@@ -28,7 +28,8 @@ FP8L_ERR_DEVICE = 5
 FP8L_ERR_LAUNCH = 6
 
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
-           "fp8_sparse24_gemm", "fp8lin_status_str")
+           "fp8_sparse24_gemm", "fp8_block_linear", "fp8_sparse24_linear", "fp8lin_status_str")
+MAX_LINEAR_M = 64  # the fused-quantization calls take decode-sized batches
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +60,8 @@ def load_library():
             "prune24_compress": [P, P, I, I, P, P, P, P],
             "fp8_block_gemm": [P, P, P, P, I, I, I, P, P],
             "fp8_sparse24_gemm": [P, P, P, P, P, I, I, I, P, P],
+            "fp8_block_linear": [P, P, P, I, I, I, P, P],
+            "fp8_sparse24_linear": [P, P, P, P, I, I, I, P, P],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -178,4 +181,35 @@ def fp8_sparse24_gemm(xq, xs, wvals, wmeta, ws, y: torch.Tensor | None = None):
     y = _out(y, "y", (M, N), torch.bfloat16, xq)
     _check("fp8_sparse24_gemm", load_library().fp8_sparse24_gemm(
         _ptr(xq), _ptr(xs), _ptr(wvals), _ptr(wmeta), _ptr(ws), M, N, K, _ptr(y), _stream(xq)))
+    return y
+
+
+def fp8_block_linear(x, wq, ws, y: torch.Tensor | None = None):
+    """(x [M,K] bf16 with M <= 64, wq [N,K], ws [N/128,K/128]) -> y [M,N] bf16; the activations are
+    quantized inside the kernel (bit-identical to fp8_quant_act followed by fp8_block_gemm)."""
+    wq = _codes(wq)
+    _want(x, "x", torch.bfloat16)
+    _want(wq, "wq", torch.uint8)
+    M, K = x.shape
+    N = wq.shape[0]
+    _want(wq, "wq", torch.uint8, (N, K))
+    _want(ws, "ws", torch.float32, (N // GROUP, K // GROUP))
+    y = _out(y, "y", (M, N), torch.bfloat16, x)
+    _check("fp8_block_linear", load_library().fp8_block_linear(
+        _ptr(x), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _stream(x)))
+    return y
+
+
+def fp8_sparse24_linear(x, wvals, wmeta, ws, y: torch.Tensor | None = None):
+    """(x [M,K] bf16 with M <= 64, wvals [N,K/2], wmeta [N,K/8], ws) -> y [M,N] bf16 (fused quantization)."""
+    wvals = _codes(wvals)
+    _want(x, "x", torch.bfloat16)
+    M, K = x.shape
+    N = wvals.shape[0]
+    _want(wvals, "wvals", torch.uint8, (N, K // 2))
+    _want(wmeta, "wmeta", torch.uint8, (N, K // 8))
+    _want(ws, "ws", torch.float32, (N // GROUP, K // GROUP))
+    y = _out(y, "y", (M, N), torch.bfloat16, x)
+    _check("fp8_sparse24_linear", load_library().fp8_sparse24_linear(
+        _ptr(x), _ptr(wvals), _ptr(wmeta), _ptr(ws), M, N, K, _ptr(y), _stream(x)))
     return y

@@ -67,6 +67,8 @@ bool bad_nk(int64_t N, int64_t K) {
 }
 bool bad_mn(int64_t M, int64_t N) { return M * N > kMaxElems; }
 
+constexpr int64_t kMaxLinearM = 64;  // the fused-quantization calls are the decode form
+
 fp8l_status launched(hipError_t e) {
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -146,11 +148,40 @@ fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   return launched(fp8lin::launch_sparse_gemm(xq, xs, wvals, wmeta, ws, M, N, K, y, stream));
 }
 
+fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N, int64_t K,
+                             uint16_t *y, hipStream_t stream) {
+  if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N) || M > kMaxLinearM) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!x || !wq || !ws || !y) return FP8L_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(ws) || !aligned16(y)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{x, M * K * 2}, {wq, N * K}, {ws, (N / 128) * (K / 128) * 4}};
+  const Range outs[] = {{y, M * N * 2}};
+  if (any_alias(outs, 1, ins, 3)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_dense_linear(x, wq, ws, M, N, K, y, stream));
+}
+
+fp8l_status fp8_sparse24_linear(const uint16_t *x, const uint8_t *wvals, const uint8_t *wmeta, const float *ws,
+                                int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N) || M > kMaxLinearM) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!x || !wvals || !wmeta || !ws || !y) return FP8L_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wvals) || !aligned16(wmeta) || !aligned16(ws) || !aligned16(y))
+    return FP8L_ERR_ALIGN;
+  const Range ins[] = {{x, M * K * 2}, {wvals, N * K / 2}, {wmeta, N * K / 8}, {ws, (N / 128) * (K / 128) * 4}};
+  const Range outs[] = {{y, M * N * 2}};
+  if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_sparse_linear(x, wvals, wmeta, ws, M, N, K, y, stream));
+}
+
 const char *fp8lin_status_str(fp8l_status status) {
   switch (status) {
     case FP8L_OK: return "ok";
     case FP8L_ERR_NULL: return "a required pointer is NULL";
-    case FP8L_ERR_SHAPE: return "unsupported shape (K and N must be positive multiples of 128, M >= 0, each <= 2^24)";
+    case FP8L_ERR_SHAPE:
+      return "unsupported shape (K and N must be positive multiples of 128, M >= 0, each <= 2^24; M <= 64 for the "
+             "*_linear calls)";
     case FP8L_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FP8L_ERR_ALIAS: return "an output overlaps an input or another output";
     case FP8L_ERR_DEVICE: return "no gfx950 (MI355X) device is current";

@@ -78,6 +78,43 @@ __device__ __forceinline__ bool scale_fast_ok(float s) {
 // |bf16| as an integer: ordering of non-NaN magnitudes is the integer ordering.
 __device__ __forceinline__ uint32_t bf16_abs_bits(uint32_t b16) { return b16 & 0x7FFFu; }
 
+// One 1x128 activation group held by 16 consecutive lanes, 8 bf16 values
+// (16 bytes) per lane: returns this lane's 8 codes and the group scale.  The
+// group amax is an integer max over |bf16| bit patterns, shuffled across the
+// 16 lanes (all 16 must be active); s = amax / 448 as an IEEE division; codes
+// by the fast quotient with the exact-division fallback.
+__device__ __forceinline__ uint2 quantize_group16(const uint4 &raw, float &s_out) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    amax_bits = max(amax_bits, bf16_abs_bits(w[i] & 0xFFFFu));
+    amax_bits = max(amax_bits, bf16_abs_bits(w[i] >> 16));
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 16));
+  const float sc = bf16_to_f32(amax_bits) / 448.0f;
+  const float rs = __builtin_amdgcn_rcpf(sc);
+  float v[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    v[i][0] = bf16_to_f32(w[2 * i] & 0xFFFFu);
+    v[i][1] = __uint_as_float(w[2 * i] & 0xFFFF0000u);
+    v[i][2] = bf16_to_f32(w[2 * i + 1] & 0xFFFFu);
+    v[i][3] = __uint_as_float(w[2 * i + 1] & 0xFFFF0000u);
+  }
+  uint32_t need = scale_fast_ok(sc) ? 0u : 1u;
+  uint32_t packed[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) packed[i] = quantize4_fast(v[i], rs, need);
+  if (__builtin_expect(need != 0u, 0)) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) packed[i] = quantize4_exact(v[i], sc);
+  }
+  s_out = sc;
+  return make_uint2(packed[0], packed[1]);
+}
+
 // v_mfma_f32_16x16x128_f8f6f4 with both operands e4m3 and no block scale.
 // A: 16 rows x 128 K, B: 128 K x 16 columns; lane l holds row / column l%16 and
 // 32 K-bytes; D: lane l holds column l%16, rows 4*(l/16) .. +3.

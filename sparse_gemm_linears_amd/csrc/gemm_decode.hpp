@@ -15,16 +15,178 @@
 //   typename W::Frag;                                  operand registers
 //   Frag W::load(int64_t row, int kb, int g) const;    row's K block kb, lane group g
 //   v4f  W::mma(const Frag &a, const v8i &b) const;    16x16 partial for one K block
+// and so is the token operand X:
+//   typename X::Raw;                                   what a load leaves in registers
+//   Raw  X::load(int m, int kb, int g) const;          token m's K block kb, lane group g
+//   void X::make(const Raw &r, v8i &frag, float &s);   e4m3 fragment and the token's scale
+//   kStaged                                            true: X::stage fills LDS first
+// X::make runs with all 64 lanes active (it may reduce across lane groups).
 #pragma once
 
 #include "gemm_common.hpp"
 
 namespace fp8lin {
 
-template <class W, int RT, int CT, int NW, int D>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, const uint8_t *__restrict__ xq,
-                                                         const float *__restrict__ xs, const float *__restrict__ ws,
-                                                         int M, int N, int K, uint16_t *__restrict__ y) {
+// Tokens already quantized by fp8_quant_act: codes and one scale per K block.
+struct QuantTokens {
+  const uint8_t *xq;
+  const float *xs;
+  int K;
+  static constexpr bool kStaged = false;
+  static constexpr int kRawRegs = 9;  // VGPRs per loaded K block
+  struct Raw {
+    v8i q;
+    float s;
+  };
+  __device__ __forceinline__ void stage(uint8_t *, int, int, int) {}
+  __device__ __forceinline__ Raw load(int m, int kb, int g) const {
+    Raw r;
+    r.q = load_frag_global(xq + (int64_t)m * K + (int64_t)kb * kGroup, g);
+    r.s = xs[(int64_t)m * (K / kGroup) + kb];
+    return r;
+  }
+  __device__ __forceinline__ void make(const Raw &r, v8i &frag, float &s) const {
+    frag = r.q;
+    s = r.s;
+  }
+};
+
+// bf16 tokens quantized on the fly, with the arithmetic of fp8_quant_act (so
+// the codes and scales are the same bits): group amax of |x| over the 128
+// channels of the K block (the four lane groups of a token hold 32 channels
+// each: two xor-shuffles), s = amax / 448 as an IEEE division, codes from
+// x * rcp(s) with the exact-division fallback near rounding midpoints.  Lane
+// group g holds channels [16g, 16g+16) and [64+16g, 64+16g+16), the fragment
+// layout of the MFMA operand.
+struct Bf16Tokens {
+  const uint16_t *x;
+  int K;
+  static constexpr bool kStaged = false;
+  static constexpr int kRawRegs = 16;  // VGPRs per loaded K block
+  struct Raw {
+    uint4 v[4];
+  };
+  __device__ __forceinline__ void stage(uint8_t *, int, int, int) {}
+  __device__ __forceinline__ Raw load(int m, int kb, int g) const {
+    const uint16_t *row = x + (int64_t)m * K + (int64_t)kb * kGroup;
+    Raw r;
+    r.v[0] = *reinterpret_cast<const uint4 *>(row + 16 * g);
+    r.v[1] = *reinterpret_cast<const uint4 *>(row + 16 * g + 8);
+    r.v[2] = *reinterpret_cast<const uint4 *>(row + 64 + 16 * g);
+    r.v[3] = *reinterpret_cast<const uint4 *>(row + 64 + 16 * g + 8);
+    return r;
+  }
+  __device__ __forceinline__ void make(const Raw &r, v8i &frag, float &s_out) const {
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      w[4 * i] = r.v[i].x;
+      w[4 * i + 1] = r.v[i].y;
+      w[4 * i + 2] = r.v[i].z;
+      w[4 * i + 3] = r.v[i].w;
+    }
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+      amax_bits = max(amax_bits, max(bf16_abs_bits(w[i] & 0xFFFFu), bf16_abs_bits(w[i] >> 16)));
+    amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 16, 64));
+    amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 32, 64));
+    const float s = bf16_to_f32(amax_bits) / 448.0f;
+    const float rs = __builtin_amdgcn_rcpf(s);
+    uint32_t need = scale_fast_ok(s) ? 0u : 1u;
+    uint32_t packed[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float v[4] = {bf16_to_f32(w[2 * i] & 0xFFFFu), __uint_as_float(w[2 * i] & 0xFFFF0000u),
+                          bf16_to_f32(w[2 * i + 1] & 0xFFFFu), __uint_as_float(w[2 * i + 1] & 0xFFFF0000u)};
+      packed[i] = quantize4_fast(v, rs, need);
+    }
+    if (__builtin_expect(need != 0u, 0)) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float v[4] = {bf16_to_f32(w[2 * i] & 0xFFFFu), __uint_as_float(w[2 * i] & 0xFFFF0000u),
+                            bf16_to_f32(w[2 * i + 1] & 0xFFFFu), __uint_as_float(w[2 * i + 1] & 0xFFFF0000u)};
+        packed[i] = quantize4_exact(v, s);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) frag[i] = (int)packed[i];
+    s_out = s;
+  }
+};
+
+// bf16 tokens quantized once per workgroup into LDS before the GEMM loop (for
+// small M, where M x K codes fit in LDS): 16 lanes per 1x128 group, the
+// arithmetic of fp8_quant_act (quantize_group16), codes [M][K] and scales
+// [M][K/128] in dynamically sized LDS.  Fragments then come from LDS.
+struct StagedTokens {
+  const uint16_t *x;
+  int K;
+  uint8_t *codes;
+  float *scales;
+  static constexpr bool kStaged = true;
+  static constexpr int kRawRegs = 9;
+  struct Raw {
+    v8i q;
+    float s;
+  };
+  static size_t lds_bytes(int M, int K) { return (size_t)M * K + (size_t)4 * M * (K / kGroup); }
+  static constexpr int kMaxPasses = 4;  // groups per 16-lane team
+  // All threads of the workgroup take part (every 16-lane team stays active).
+  // Every load is issued before any arithmetic, so the staging costs one
+  // memory latency rather than one per pass.
+  __device__ __forceinline__ void stage(uint8_t *lds, int M, int tid, int nthreads) {
+    codes = lds;
+    scales = reinterpret_cast<float *>(lds + (size_t)M * K);
+    const int groups = M * (K / kGroup), teams = nthreads / 16, lane16 = tid & 15;
+    const int passes = (groups + teams - 1) / teams;
+    uint4 raw[kMaxPasses];
+#pragma unroll
+    for (int p = 0; p < kMaxPasses; p++) {
+      // groups past the end repeat the last one and store nothing
+      const int gc = min(p * teams + tid / 16, groups - 1);
+      if (p < passes) raw[p] = *reinterpret_cast<const uint4 *>(x + (int64_t)gc * kGroup + lane16 * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < kMaxPasses; p++) {
+      if (p < passes) {
+        const int grp = p * teams + tid / 16, gc = min(grp, groups - 1);
+        float s;
+        const uint2 q = quantize_group16(raw[p], s);
+        if (grp < groups) {
+          *reinterpret_cast<uint2 *>(codes + (size_t)gc * kGroup + lane16 * 8) = q;
+          if (lane16 == 0) scales[gc] = s;
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ Raw load(int m, int kb, int g) const {
+    const uint8_t *row = codes + (size_t)m * K + (size_t)kb * kGroup;
+    Raw r;
+    r.q = make_v8i(*reinterpret_cast<const uint4 *>(row + 16 * g), *reinterpret_cast<const uint4 *>(row + 64 + 16 * g));
+    r.s = scales[m * (K / kGroup) + kb];
+    return r;
+  }
+  __device__ __forceinline__ void make(const Raw &r, v8i &frag, float &s) const {
+    frag = r.q;
+    s = r.s;
+  }
+};
+
+// Staging pays while the per-workgroup quantization (M x K elements, redone by
+// every workgroup) stays small next to the weight stream: measured on MI355X,
+// the staged call beats fp8_quant_act + GEMM for one or two tokens and loses
+// from three on.  The codes (plus the largest reduction buffer, 28 KB) must
+// fit the default 64 KB of LDS per workgroup, and each 16-lane team stages at
+// most kMaxPasses groups (64 teams in the 16-wave workgroup used for M <= 4).
+inline bool staged_tokens_fit(int64_t M, int64_t K) {
+  return M <= 2 && StagedTokens::lds_bytes((int)M, (int)K) <= 36 * 1024 &&
+         M * (K / kGroup) <= StagedTokens::kMaxPasses * 64;
+}
+
+template <class W, class X, int RT, int CT, int NW, int D>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const float *__restrict__ ws, int M, int N,
+                                                         int K, uint16_t *__restrict__ y) {
   static_assert(128 % (16 * RT) == 0, "a workgroup's rows must sit in one 128-row scale block");
   __shared__ v4f red[NW > 1 ? NW - 1 : 1][RT * CT][64];
   const int lane = threadIdx.x & 63;
@@ -35,28 +197,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, const uint8_t *_
   const float *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
   const int n_w = wave < KB ? (KB - wave + NW - 1) / NW : 0;  // K blocks of this wave
 
-  const uint8_t *xrow[CT];
-  const float *srow[CT];
+  int mrow[CT];
 #pragma unroll
-  for (int c = 0; c < CT; c++) {
-    const int m = min(16 * c + lr, M - 1);
-    xrow[c] = xq + (int64_t)m * K;
-    srow[c] = xs + (int64_t)m * KB;
-  }
+  for (int c = 0; c < CT; c++) mrow[c] = min(16 * c + lr, M - 1);
 
   typename W::Frag a[D][RT];
-  v8i b[D][CT];
-  float sx[D][CT], sw[D];
-  auto load = [&](int slot, int i) {
+  typename X::Raw b[D][CT];
+  float sw[D];
+  auto load_w = [&](int slot, int i) {
     const int kb = wave + i * NW;
 #pragma unroll
     for (int r = 0; r < RT; r++) a[slot][r] = wop.load(n0 + 16 * r + lr, kb, g);
-#pragma unroll
-    for (int c = 0; c < CT; c++) {
-      b[slot][c] = load_frag_global(xrow[c] + (int64_t)kb * kGroup, g);
-      sx[slot][c] = srow[c][kb];
-    }
     sw[slot] = ws_row[kb];
+  };
+  auto load_x = [&](int slot, int i) {
+    const int kb = wave + i * NW;
+#pragma unroll
+    for (int c = 0; c < CT; c++) b[slot][c] = xop.load(mrow[c], kb, g);
   };
 
   v4f acc[RT][CT];
@@ -65,9 +222,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, const uint8_t *_
 #pragma unroll
     for (int c = 0; c < CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // the first weight loads go out before the tokens are staged, so their HBM
+  // latency overlaps the staging
 #pragma unroll
   for (int d = 0; d < D; d++)
-    if (d < n_w) load(d, d);
+    if (d < n_w) load_w(d, d);
+  if constexpr (X::kStaged) {
+    extern __shared__ __align__(16) uint8_t staged_lds[];
+    xop.stage(staged_lds, M, threadIdx.x, NW * 64);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int d = 0; d < D; d++)
+    if (d < n_w) load_x(d, d);
   for (int i0 = 0; i0 < n_w; i0 += D) {
 #pragma unroll
     for (int d = 0; d < D; d++) {
@@ -75,11 +242,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, const uint8_t *_
       if (i < n_w) {
 #pragma unroll
         for (int c = 0; c < CT; c++) {
-          const float scl = sx[d][c] * sw[d];
+          v8i bf;
+          float sx;
+          xop.make(b[d][c], bf, sx);
+          const float scl = sx * sw[d];
 #pragma unroll
-          for (int r = 0; r < RT; r++) acc[r][c] += scl * wop.mma(a[d][r], b[d][c]);
+          for (int r = 0; r < RT; r++) acc[r][c] += scl * wop.mma(a[d][r], bf);
         }
-        if (i + D < n_w) load(d, i + D);
+        if (i + D < n_w) {
+          load_w(d, i + D);
+          load_x(d, i + D);
+        }
       }
     }
   }

@@ -251,11 +251,12 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
   return hipGetLastError();
 }
 
-template <int RT, int CT, int NW, int D>
-static hipError_t launch_decode(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
-                                const float *ws, int M, int N, int K, uint16_t *y, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<SparseWeight, RT, CT, NW, D>), dim3(N / (16 * RT)), dim3(NW * 64), 0, stream,
-                     SparseWeight{wv, wm, K}, xq, xs, ws, M, N, K, y);
+template <class X, int RT, int CT, int NW, int D>
+static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, const float *ws, int M, int N, int K,
+                                uint16_t *y, hipStream_t stream) {
+  const size_t lds = X::kStaged ? StagedTokens::lds_bytes(M, K) : 0;
+  hipLaunchKernelGGL((decode_kernel<SparseWeight, X, RT, CT, NW, D>), dim3(N / (16 * RT)), dim3(NW * 64), lds,
+                     stream, SparseWeight{wv, wm, K}, xop, ws, M, N, K, y);
   return hipGetLastError();
 }
 
@@ -263,24 +264,45 @@ static hipError_t launch_decode(const uint8_t *xq, const float *xs, const uint8_
 // Decode configuration (measured on MI355X over the Llama-3-8B shapes): more
 // rows per workgroup when N is large enough to keep every CU busy, since each
 // workgroup re-reads the M x K activations from L2.
-template <int CT>
-static hipError_t launch_decode_for(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
-                                    const float *ws, int M, int N, int K, uint16_t *y, hipStream_t stream) {
+template <class X, int CT>
+static hipError_t launch_decode_for(X xop, const uint8_t *wv, const uint8_t *wm, const float *ws, int M, int N,
+                                    int K, uint16_t *y, hipStream_t stream) {
   if constexpr (CT == 1)
-    if (M <= 4) return launch_decode<1, CT, 16, 2>(xq, xs, wv, wm, ws, M, N, K, y, stream);
+    if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wv, wm, ws, M, N, K, y, stream);
   if constexpr (CT <= 2)
-    if (N >= 16384) return launch_decode<4, CT, 8, 2>(xq, xs, wv, wm, ws, M, N, K, y, stream);
-  if (N >= 6144) return launch_decode<2, CT, 8, 2>(xq, xs, wv, wm, ws, M, N, K, y, stream);
-  return launch_decode<1, CT, 8, 1>(xq, xs, wv, wm, ws, M, N, K, y, stream);
+    if (N >= 16384) return launch_decode<X, 4, CT, 8, 2>(xop, wv, wm, ws, M, N, K, y, stream);
+  // bf16 tokens take 16 registers per K block and token tile: one block in
+  // flight for the widest tile
+  constexpr int D2 = (CT == 4 && X::kRawRegs > 9) ? 1 : 2;
+  if (N >= 6144) return launch_decode<X, 2, CT, 8, D2>(xop, wv, wm, ws, M, N, K, y, stream);
+  return launch_decode<X, 1, CT, 8, 1>(xop, wv, wm, ws, M, N, K, y, stream);
+}
+
+template <class X>
+static hipError_t launch_sparse_decode(X xop, const uint8_t *wv, const uint8_t *wm, const float *ws, int M, int N,
+                                       int K, uint16_t *y, hipStream_t stream) {
+  if constexpr (X::kStaged) {
+    return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, stream);  // M <= 8
+  } else {
+    if (M <= 16) return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, stream);
+    if (M <= 32) return launch_decode_for<X, 2>(xop, wv, wm, ws, M, N, K, y, stream);
+    return launch_decode_for<X, 4>(xop, wv, wm, ws, M, N, K, y, stream);
+  }
 }
 
 hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
                               const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (m <= 16) return launch_decode_for<1>(xq, xs, wv, wm, ws, m, n, k, y, stream);
-  if (m <= 32) return launch_decode_for<2>(xq, xs, wv, wm, ws, m, n, k, y, stream);
-  if (m <= 64) return launch_decode_for<4>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+  if (m <= 64) return launch_sparse_decode(QuantTokens{xq, xs, k}, wv, wm, ws, m, n, k, y, stream);
   return launch_tile<256, 256, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+}
+
+hipError_t launch_sparse_linear(const uint16_t *x, const uint8_t *wv, const uint8_t *wm, const float *ws, int64_t M,
+                                int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  if (staged_tokens_fit(M, K))
+    return launch_sparse_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wv, wm, ws, (int)M, (int)N, (int)K, y,
+                                stream);
+  return launch_sparse_decode(Bf16Tokens{x, (int)K}, wv, wm, ws, (int)M, (int)N, (int)K, y, stream);
 }
 
 }  // namespace fp8lin

@@ -23,35 +23,10 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   // group grp covers elements [grp*128, grp*128+128) of the flattened [M,K] array
   uint4 raw = make_uint4(0, 0, 0, 0);
   if (live) raw = *reinterpret_cast<const uint4*>(x + grp * kGroup + lane16 * 8);
-  uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t amax_bits = 0;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    amax_bits = max(amax_bits, bf16_abs_bits(w[i] & 0xFFFFu));
-    amax_bits = max(amax_bits, bf16_abs_bits(w[i] >> 16));
-  }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 16));
-  const float sc = bf16_to_f32(amax_bits) / 448.0f;
-  const float rs = __builtin_amdgcn_rcpf(sc);
-  float v[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    v[i][0] = bf16_to_f32(w[2 * i] & 0xFFFFu);
-    v[i][1] = __uint_as_float(w[2 * i] & 0xFFFF0000u);
-    v[i][2] = bf16_to_f32(w[2 * i + 1] & 0xFFFFu);
-    v[i][3] = __uint_as_float(w[2 * i + 1] & 0xFFFF0000u);
-  }
-  uint32_t need = scale_fast_ok(sc) ? 0u : 1u;
-  uint32_t packed[2];
-#pragma unroll
-  for (int i = 0; i < 2; i++) packed[i] = quantize4_fast(v[i], rs, need);
-  if (__builtin_expect(need != 0u, 0)) {
-#pragma unroll
-    for (int i = 0; i < 2; i++) packed[i] = quantize4_exact(v[i], sc);
-  }
+  float sc;
+  const uint2 packed = quantize_group16(raw, sc);
   if (live) {
-    *reinterpret_cast<uint2*>(q + grp * kGroup + lane16 * 8) = make_uint2(packed[0], packed[1]);
+    *reinterpret_cast<uint2*>(q + grp * kGroup + lane16 * 8) = packed;
     if (lane16 == 0) s[grp] = sc;
   }
 }

@@ -25,7 +25,7 @@ def lib():
     return sgl.load_library()
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_every_exported_call():
     names = header_functions()
     assert set(names) == set(sgl.EXPORTS)
     assert len(names) == len(set(names))
@@ -108,6 +108,24 @@ def test_gemm_validation(lib):
     assert h(P(A), P(B), P(C), P(D), P(E), 16, 128, 128, P(D), None) == sgl.FP8L_ERR_ALIAS
 
 
+def test_linear_validation(lib):
+    """The fused-quantization calls: same checks as the GEMMs, plus M <= 64."""
+    f = lib.fp8_block_linear
+    assert f(P(A), P(C), P(D), 65, 128, 128, P(E), None) == sgl.FP8L_ERR_SHAPE
+    assert f(P(A), P(C), P(D), 16, 100, 128, P(E), None) == sgl.FP8L_ERR_SHAPE
+    assert f(P(A), P(C), P(D), 16, 128, 96, P(E), None) == sgl.FP8L_ERR_SHAPE
+    assert f(P(A), None, P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_NULL
+    assert f(P(A), P(C), P(D), 16, 128, 128, P(E + 8), None) == sgl.FP8L_ERR_ALIGN
+    assert f(P(A), P(C), P(D), 16, 128, 128, P(A + 1024), None) == sgl.FP8L_ERR_ALIAS  # y over x
+    assert f(None, P(C), P(D), 0, 128, 128, None, None) == sgl.FP8L_OK
+    h = lib.fp8_sparse24_linear
+    assert h(P(A), P(B), P(C), P(D), 65, 128, 128, P(E), None) == sgl.FP8L_ERR_SHAPE
+    assert h(P(A), P(B), None, P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_NULL
+    assert h(P(A), P(B), P(C + 4), P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_ALIGN
+    assert h(P(A), P(B), P(C), P(D), 16, 128, 128, P(C), None) == sgl.FP8L_ERR_ALIAS
+    assert h(None, P(B), P(C), P(D), 0, 128, 128, None, None) == sgl.FP8L_OK
+
+
 def test_valid_call_without_gpu_reports_device(lib):
     """With valid arguments and no gfx950 device the call stops at the device check."""
     import torch
@@ -115,6 +133,7 @@ def test_valid_call_without_gpu_reports_device(lib):
         pytest.skip("a GPU is present")
     assert lib.fp8_quant_act(P(A), 4, 128, P(B), P(C), None) == sgl.FP8L_ERR_DEVICE
     assert lib.fp8_block_gemm(P(A), P(B), P(C), P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_DEVICE
+    assert lib.fp8_block_linear(P(A), P(C), P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_DEVICE
 
 
 def test_binding_rejects_host_tensors():
