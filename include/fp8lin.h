@@ -23,6 +23,7 @@
  *   FP8L_ERR_SHAPE   M < 0, N <= 0, K <= 0, K % 128 != 0, N % 128 != 0, or a
  *                    dimension above 2^24, or a matrix above 2^36 elements
  *                    (and M > 64 for the two *_linear calls);
+ *                    for fp8_block_gemm_swiglu I plays the part of N;
  *   FP8L_ERR_ALIGN   a pointer is not 16-byte aligned;
  *   FP8L_ERR_ALIAS   an output overlaps an input or another output;
  *   FP8L_ERR_DEVICE  the current HIP device is missing or is not gfx950;
@@ -131,6 +132,28 @@ fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq
 fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t *wvals,
                               const uint8_t *wmeta, const float *ws, int64_t M, int64_t N,
                               int64_t K, uint16_t *y, hipStream_t stream);
+
+/*
+ * Gated-MLP up projection with the SwiGLU activation in the GEMM epilogue
+ * ("FP8 Quantization" (TensorRT-LLM), section "GEMM + SwiGLU Fusion in
+ * Gated-MLP": the gate and up matmuls and the SwiGLU run as one kernel).  With
+ * block scales every scale of both GEMMs is kept; the fused result differs
+ * from two GEMMs and an elementwise pass only in skipping the bf16 rounding of
+ * the gate and up sums.
+ *
+ *   xq [M,K], xs [M,K/128]          from fp8_quant_act
+ *   wq [2I,K], ws [2I/128,K/128]    rows 0..I-1 the gate projection, I..2I-1 the
+ *                                   up projection (nn.Linear weights stacked)
+ *   h  [M,I] bf16                   h = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)),
+ *                                   g, u the fp32 block-scaled sums of fp8_block_gemm
+ *   hq [M,I] e4m3, hs [M,I/128]     fp8_quant_act(h), the next layer's input
+ *                                   (both NULL: not produced)
+ * I must be a positive multiple of 128.  Meant for prefill-sized M: every
+ * call runs 256-token tiles.
+ */
+fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                                  int64_t M, int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs,
+                                  hipStream_t stream);
 
 /*
  * Decode-sized linear layer on bf16 activations: fp8_quant_act and

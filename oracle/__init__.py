@@ -15,7 +15,10 @@ follows are cited in ``oracle.c``:
   and practical example 1: groups of 4 along K, keep the top two scores,
   recalibrate scales after pruning, export values + masks;
 * "Combiner elagage et quantification", section "La cle": keep the two
-  largest of every four.
+  largest of every four;
+* "FP8 Quantization" (TensorRT-LLM docs), section "GEMM + SwiGLU Fusion in
+  Gated-MLP": the gate and up GEMMs of a gated MLP combined by SwiGLU
+  (``swiglu`` / ``gemm_swiglu`` below, in numpy fp64).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, brute force and exact rational arithmetic; none is "parity
@@ -217,6 +220,24 @@ def gemm(xq, xs, wq, ws, rows: np.ndarray | None = None) -> np.ndarray:
 def sparse24_gemm(xq, xs, vals, meta, ws, rows: np.ndarray | None = None) -> np.ndarray:
     """The GEMM on the decompressed 2:4 weight (pruned places contribute zero)."""
     return gemm(xq, xs, decompress24(vals, meta), ws, rows=rows)
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """SwiGLU of gate and up values in fp64: silu(g) * u with silu(g) = g / (1 + exp(-g))."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * np.asarray(u, dtype=np.float64)
+
+
+def gemm_swiglu(xq, xs, wq, ws, rows: np.ndarray | None = None) -> np.ndarray:
+    """Gated-MLP up projection: wq [2I,K] stacks the gate (rows 0..I-1) and up
+    (rows I..2I-1) projections; returns swiglu(gate GEMM, up GEMM) [M or rows, I]
+    in fp64, each GEMM as in ``gemm``."""
+    I = wq.shape[0] // 2
+    nb = I // GROUP
+    g = gemm(xq, xs, wq[:I], ws[:nb], rows=rows)
+    u = gemm(xq, xs, wq[I:], ws[nb:], rows=rows)
+    return swiglu(g, u)
 
 
 def num_threads() -> int:

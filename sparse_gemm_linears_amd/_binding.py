@@ -28,7 +28,8 @@ FP8L_ERR_DEVICE = 5
 FP8L_ERR_LAUNCH = 6
 
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
-           "fp8_sparse24_gemm", "fp8_block_linear", "fp8_sparse24_linear", "fp8lin_status_str")
+           "fp8_sparse24_gemm", "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear",
+           "fp8lin_status_str")
 MAX_LINEAR_M = 64  # the fused-quantization calls take decode-sized batches
 
 _lock = threading.Lock()
@@ -60,6 +61,7 @@ def load_library():
             "prune24_compress": [P, P, I, I, P, P, P, P],
             "fp8_block_gemm": [P, P, P, P, I, I, I, P, P],
             "fp8_sparse24_gemm": [P, P, P, P, P, I, I, I, P, P],
+            "fp8_block_gemm_swiglu": [P, P, P, P, I, I, I, P, P, P, P],
             "fp8_block_linear": [P, P, P, I, I, I, P, P],
             "fp8_sparse24_linear": [P, P, P, P, I, I, I, P, P],
         }
@@ -213,3 +215,26 @@ def fp8_sparse24_linear(x, wvals, wmeta, ws, y: torch.Tensor | None = None):
     _check("fp8_sparse24_linear", load_library().fp8_sparse24_linear(
         _ptr(x), _ptr(wvals), _ptr(wmeta), _ptr(ws), M, N, K, _ptr(y), _stream(x)))
     return y
+
+
+def fp8_block_gemm_swiglu(xq, xs, wq, ws, h: torch.Tensor | None = None, quantize: bool = True,
+                          hq: torch.Tensor | None = None, hs: torch.Tensor | None = None):
+    """(xq [M,K], xs, wq [2I,K] = [gate; up], ws [2I/128,K/128]) -> h [M,I] bf16 = silu(gate) * up, and, when
+    ``quantize``, (hq [M,I] e4m3 codes, hs [M,I/128]) = fp8_quant_act(h).  Returns (h, hq, hs)."""
+    xq, wq = _codes(xq), _codes(wq)
+    _want(xq, "xq", torch.uint8)
+    _want(wq, "wq", torch.uint8)
+    M, K = xq.shape
+    I = wq.shape[0] // 2
+    _want(wq, "wq", torch.uint8, (2 * I, K))
+    _want(xs, "xs", torch.float32, (M, K // GROUP))
+    _want(ws, "ws", torch.float32, (2 * I // GROUP, K // GROUP))
+    h = _out(h, "h", (M, I), torch.bfloat16, xq)
+    if quantize:
+        hq = _out(hq, "hq", (M, I), torch.uint8, xq)
+        hs = _out(hs, "hs", (M, I // GROUP), torch.float32, xq)
+    else:
+        hq = hs = None
+    _check("fp8_block_gemm_swiglu", load_library().fp8_block_gemm_swiglu(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, I, K, _ptr(h), _ptr(hq), _ptr(hs), _stream(xq)))
+    return h, hq, hs

@@ -148,6 +148,21 @@ fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   return launched(fp8lin::launch_sparse_gemm(xq, xs, wvals, wmeta, ws, M, N, K, y, stream));
 }
 
+fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
+                                  int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs, hipStream_t stream) {
+  if (I <= 0 || bad_mk(M, K) || bad_nk(2 * I, K) || bad_mn(M, I)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!xq || !xs || !wq || !ws || !h || (!hq != !hs)) return FP8L_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(h) ||
+      (hq && (!aligned16(hq) || !aligned16(hs))))
+    return FP8L_ERR_ALIGN;
+  const Range ins[] = {{xq, M * K}, {xs, M * (K / 128) * 4}, {wq, 2 * I * K}, {ws, (2 * I / 128) * (K / 128) * 4}};
+  const Range outs[] = {{h, M * I * 2}, {hq, hq ? M * I : 0}, {hs, hs ? M * (I / 128) * 4 : 0}};
+  if (any_alias(outs, 3, ins, 4)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_dense_gemm_swiglu(xq, xs, wq, ws, M, I, K, h, hq, hs, stream));
+}
+
 fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N, int64_t K,
                              uint16_t *y, hipStream_t stream) {
   if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N) || M > kMaxLinearM) return FP8L_ERR_SHAPE;

@@ -30,6 +30,7 @@ struct DenseTile {
   static constexpr int RT = kWaveN / 16, CT = kWaveM / 16;
   static constexpr int kACopies = BN / 8 / kWaves, kBCopies = BM / 8 / kWaves;  // 1 KB = 8 rows per copy
   static constexpr int kATile = BN * 128, kBTile = BM * 128;
+  static constexpr int kWavesPerSlice = WM;  // waves sharing a weight slice (one per token slice)
   static_assert(BN == 256 && BM == 256, "panels are addressed as two 128-row halves");
   static_assert(128 % (8 * kWaves) == 0, "copy slabs tile the 128-row halves");
   static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
@@ -38,15 +39,98 @@ struct DenseTile {
   static_assert(kWaves * 4096 <= kATile, "epilogue scratch fits in one weight stage");
 };
 
+// Output of the SwiGLU epilogue: h [M,I] bf16 (the kernel's y) and, when hq
+// is not NULL, its per-token 1x128 e4m3 codes hq [M,I] and scales hs [M,I/128].
+struct SwigluOut {
+  uint8_t *hq;
+  float *hs;
+  int I;
+};
+
+// SwiGLU epilogue.  The two waves with the same token slice hold the gate
+// (wn0 = 0) and up (wn0 = 128) sums of the same 128 outputs in the same
+// register layout; per token tile the up wave hands its fp32 sums to the gate
+// wave through LDS, and the gate wave forms h = silu(g) * u = g * u / (1 +
+// exp(-g)) in fp32, stores bf16(h) and, if asked, quantizes bf16(h) as
+// fp8_quant_act would: the tile's 128 outputs are exactly one 1x128 group of a
+// token, held by the four lane groups of the token's lanes (two xor-shuffles
+// give the group amax).
+template <class C>
+__device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *xch, uint8_t *scratch, uint16_t *h,
+                                                const SwigluOut &so, int M, int m_wave, int tn, int wave, int wn0,
+                                                int lane) {
+  const int lr = lane & 15, g = lane >> 4, slot = wave % C::kWavesPerSlice;
+  const bool gate = wn0 == 0;
+#pragma unroll
+  for (int c = 0; c < C::CT; c++) {
+    if (!gate) {
+#pragma unroll
+      for (int r = 0; r < C::RT; r++) xch[(slot * C::RT + r) * 64 + lane] = acc[r][c];
+    }
+    __syncthreads();
+    if (gate) {
+      v4f hv[C::RT];
+#pragma unroll
+      for (int r = 0; r < C::RT; r++) {
+        const v4f u = xch[(slot * C::RT + r) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float gv = acc[r][c][e];
+          // bf16 rounding here is the value h takes in memory
+          hv[r][e] = bf16_to_f32(f32_to_bf16_rne(gv * u[e] / (1.0f + expf(-gv))));
+        }
+      }
+      const int m0 = m_wave + 16 * c;
+      store_token_tile<C::RT>(scratch, hv, h, M, so.I, m0, 128 * tn, lane);
+      if (so.hq) {
+        uint32_t amax_bits = 0;
+#pragma unroll
+        for (int r = 0; r < C::RT; r++)
+#pragma unroll
+          for (int e = 0; e < 4; e++) amax_bits = max(amax_bits, __float_as_uint(hv[r][e]) & 0x7FFFFFFFu);
+        amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 16, 64));
+        amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 32, 64));
+        const float sc = __uint_as_float(amax_bits) / 448.0f;
+        const float rs = __builtin_amdgcn_rcpf(sc);
+        uint32_t need = scale_fast_ok(sc) ? 0u : 1u;
+        uint32_t words[C::RT];
+#pragma unroll
+        for (int r = 0; r < C::RT; r++) {
+          const float v[4] = {hv[r][0], hv[r][1], hv[r][2], hv[r][3]};
+          words[r] = quantize4_fast(v, rs, need);
+        }
+        if (__builtin_expect(need != 0u, 0)) {
+#pragma unroll
+          for (int r = 0; r < C::RT; r++) {
+            const float v[4] = {hv[r][0], hv[r][1], hv[r][2], hv[r][3]};
+            words[r] = quantize4_exact(v, sc);
+          }
+        }
+        const int m = m0 + lr;
+        if (m < M) {
+          uint8_t *qrow = so.hq + (int64_t)m * so.I + 128 * tn;
+#pragma unroll
+          for (int r = 0; r < C::RT; r++) *reinterpret_cast<uint32_t *>(qrow + 16 * r + 4 * g) = words[r];
+          if (g == 0) so.hs[(int64_t)m * (so.I / kGroup) + tn] = sc;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // SB: K blocks per token-scale load (4 when K/128 is a multiple of 4, else 1).
 // CR: the next K block's copies are issued across the first CR row tiles.
-template <int BN, int BM, int WN, int WM, int SB, int CR>
+// SWIGLU: the weight is [gate; up] (2I rows); tile tn covers outputs
+// [128 tn, 128 tn + 128) and reads gate rows there into the first panel half
+// and up rows I + 128 tn .. into the second; y is h [M,I].
+template <int BN, int BM, int WN, int WM, int SB, int CR, bool SWIGLU>
 __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *__restrict__ xq,
                                                                 const float *__restrict__ xs,
                                                                 const uint8_t *__restrict__ wq,
                                                                 const float *__restrict__ ws, int M, int N,
                                                                 int K, uint16_t *__restrict__ y, int tiles_m,
-                                                                int tiles_n, int group_m) {
+                                                                int tiles_n, int group_m, SwigluOut so) {
   using C = DenseTile<BN, BM, WN, WM>;
   // One LDS object per stage and panel: copies into one stage and fragment
   // reads of the other are then known not to overlap, so reads never wait for
@@ -73,8 +157,12 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
   // have K-byte rows, so one per-lane offset serves every copy; the slab and
   // the K block go into the scalar offset.
   const uint32_t copy_voff = (uint32_t)((wave * 8 + cj) * K + 16 * (cp ^ swz(cj + 8 * (wave & 1))));
-  const uint8_t *wpanel = wq + (int64_t)n_base * K, *xpanel = xq + (int64_t)m_base * K;
-  const rsrc_t rw0 = panel_rows128(wpanel, N - n_base, 0, K), rw1 = panel_rows128(wpanel, N - n_base, 128, K);
+  // first weight row of each 128-row panel half
+  const int w_half0 = SWIGLU ? 128 * tn : n_base;
+  const int w_half1 = SWIGLU ? so.I + 128 * tn : n_base + 128;
+  const uint8_t *xpanel = xq + (int64_t)m_base * K;
+  const rsrc_t rw0 = panel_rows128(wq + (int64_t)w_half0 * K, N - w_half0, 0, K);
+  const rsrc_t rw1 = panel_rows128(wq + (int64_t)w_half1 * K, N - w_half1, 0, K);
   const rsrc_t rx0 = panel_rows128(xpanel, M - m_base, 0, K), rx1 = panel_rows128(xpanel, M - m_base, 128, K);
   TokenScales<BM, SB> scales;
   scales.init(lds_s, xs, M, KB, m_base, tid);
@@ -107,7 +195,7 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
 #pragma unroll
     for (int c = 0; c < C::CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int nb_wave = min((n_base + wn0) / kGroup, NB - 1);
+  const int nb_wave = min((wn0 == 0 ? w_half0 : w_half1) / kGroup, NB - 1);
   const float *ws_row = ws + (int64_t)nb_wave * KB;
 
   // Token fragments live in registers one K step ahead: bx[ST] holds this
@@ -200,12 +288,17 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
 
   // epilogue through a wave-private 4 KB slice of the (now idle) weight stage 0
   uint8_t *scratch = lds_a0 + wave * 4096;
+  if constexpr (!SWIGLU) {
 #pragma unroll
-  for (int c = 0; c < C::CT; c++) {
-    v4f col[C::RT];
+    for (int c = 0; c < C::CT; c++) {
+      v4f col[C::RT];
 #pragma unroll
-    for (int r = 0; r < C::RT; r++) col[r] = acc[r][c];
-    store_token_tile<C::RT>(scratch, col, y, M, N, m_base + wm0 + 16 * c, n_base + wn0, lane);
+      for (int r = 0; r < C::RT; r++) col[r] = acc[r][c];
+      store_token_tile<C::RT>(scratch, col, y, M, N, m_base + wm0 + 16 * c, n_base + wn0, lane);
+    }
+  } else {
+    swiglu_epilogue<C>(acc, reinterpret_cast<v4f *>(lds_b0), scratch, y, so, M, m_base + wm0, tn, wave, wn0,
+                       lane);
   }
 }
 
@@ -232,12 +325,13 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
                               int K, uint16_t *y, hipStream_t stream) {
   using C = DenseTile<BN, BM, WN, WM>;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const SwigluOut none{nullptr, nullptr, 0};
   if ((K / kGroup) % 4 == 0)
-    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
-                       stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4);
+    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false>), dim3(tiles_m * tiles_n),
+                       dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, none);
   else
-    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
-                       stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4);
+    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4, false>), dim3(tiles_m * tiles_n),
+                       dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, none);
   return hipGetLastError();
 }
 
@@ -285,6 +379,22 @@ hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *
   const int m = (int)M, n = (int)N, k = (int)K;
   if (m <= 64) return launch_dense_decode(QuantTokens{xq, xs, k}, wq, ws, m, n, k, y, stream);
   return launch_tile<256, 256, 2, 4>(xq, xs, wq, ws, m, n, k, y, stream);
+}
+
+hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                                   int64_t M, int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs,
+                                   hipStream_t stream) {
+  using C = DenseTile<256, 256, 2, 4>;
+  const int m = (int)M, k = (int)K;
+  const int tiles_m = (m + 255) / 256, tiles_n = (int)(I / 128);
+  const SwigluOut so{hq, hs, (int)I};
+  if ((k / kGroup) % 4 == 0)
+    hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 4, 4, true>), dim3(tiles_m * tiles_n), dim3(C::kThreads),
+                       0, stream, xq, xs, wq, ws, m, (int)(2 * I), k, h, tiles_m, tiles_n, 4, so);
+  else
+    hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 1, 4, true>), dim3(tiles_m * tiles_n), dim3(C::kThreads),
+                       0, stream, xq, xs, wq, ws, m, (int)(2 * I), k, h, tiles_m, tiles_n, 4, so);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,

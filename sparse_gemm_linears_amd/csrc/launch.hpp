@@ -16,6 +16,12 @@ hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *
 hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
                               const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
 
+// Dense GEMM on a [gate; up] weight (2I rows) with the SwiGLU epilogue:
+// h = bf16(silu(g) * u), plus fp8_quant_act(h) when hq is not NULL.
+hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                                   int64_t M, int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs,
+                                   hipStream_t stream);
+
 // Decode-sized (M <= 64) GEMMs on bf16 activations, quantized inside the kernel
 // with the arithmetic of fp8_quant_act.
 hipError_t launch_dense_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,

@@ -122,3 +122,40 @@ def test_linear_deterministic(gpu_lib):
     a = gpu_lib.fp8_block_linear(x, dev(wq), dev(ws))
     b = gpu_lib.fp8_block_linear(x, dev(wq), dev(ws))
     assert same_bits(a, b)
+
+
+# ------------------------------------------------- GEMM + SwiGLU epilogue ---
+
+@functools.lru_cache(maxsize=None)
+def gate_up_weight(K: int, I: int):
+    """[gate; up] stacked weight (the Llama-3-8B gate/up shape when I = 14336)."""
+    return oracle.quant_wblock(si.weights(2 * I, K))
+
+
+@pytest.mark.parametrize("M,I,K", [(4096, 14336, 4096), (300, 256, 640), (16, 128, 128), (513, 384, 1152)])
+def test_gemm_swiglu(gpu_lib, M, I, K):
+    x = si.activations(M, K, outliers=(K == 4096))
+    xq, xs = oracle.quant_act(x)
+    wq, ws = gate_up_weight(K, I)
+    h, hq, hs = gpu_lib.fp8_block_gemm_swiglu(dev(xq), dev(xs), dev(wq), dev(ws))
+    rows = np.unique(np.concatenate([[0, M - 1, min(255, M - 1), min(256, M - 1)], si.sample_rows(M, 8, seed=9)]))
+    assert_gemm_close(h[torch.from_numpy(rows).to("cuda")], oracle.gemm_swiglu(xq, xs, wq, ws, rows=rows),
+                      f"h {M}x{I}x{K}")
+    # the fused quantization equals fp8_quant_act of the stored h, bit for bit (oracle and library quantizer)
+    h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    rq, rs = oracle.quant_act(h_bits[rows])
+    assert np.array_equal(hq.cpu().numpy()[rows], rq)
+    assert np.array_equal(hs.cpu().numpy()[rows].view(np.uint32), rs.view(np.uint32))
+    lq, ls = gpu_lib.fp8_quant_act(h)
+    assert torch.equal(lq, hq) and torch.equal(ls.view(torch.int32), hs.view(torch.int32))
+
+
+def test_gemm_swiglu_without_quantization(gpu_lib):
+    M, I, K = 256, 256, 512
+    xq, xs = oracle.quant_act(si.activations(M, K, outliers=False))
+    wq, ws = gate_up_weight(K, I)
+    h, hq, hs = gpu_lib.fp8_block_gemm_swiglu(dev(xq), dev(xs), dev(wq), dev(ws), quantize=False)
+    assert hq is None and hs is None
+    h2, _, _ = gpu_lib.fp8_block_gemm_swiglu(dev(xq), dev(xs), dev(wq), dev(ws))
+    assert same_bits(h, h2)
+    assert_gemm_close(h, oracle.gemm_swiglu(xq, xs, wq, ws), "h")

@@ -443,3 +443,34 @@ def test_sparse_gemm_equals_dense_on_decompressed():
     keep = oracle.prune24_mask(w)
     wq, ws = oracle.quant_wblock(np.where(keep, w, np.uint16(0)).astype(np.uint16))
     assert np.array_equal(y, oracle.gemm(xq, xs, wq, ws))
+
+
+# ----------------------------------------------------------------- SwiGLU ---
+
+def test_swiglu_against_library_sigmoid_and_identities():
+    """silu(g) * u against scipy's logistic function, and silu(x) - silu(-x) = x."""
+    from scipy.special import expit
+    g = np.concatenate([np.linspace(-60, 60, 2001), [0.0, 1e-30, -1e-30, 700.0, -700.0, -1e4]])
+    u = np.cos(np.arange(g.size))
+    assert np.allclose(oracle.swiglu(g, u), g * expit(g) * u, rtol=1e-14, atol=1e-300)
+    assert np.allclose(oracle.swiglu(g, 1.0) - oracle.swiglu(-g, 1.0), g, rtol=1e-13, atol=1e-13)
+    assert oracle.swiglu(0.0, 5.0) == 0.0
+    assert oracle.swiglu(-1e4, 3.0) == 0.0 and oracle.swiglu(1e4, 3.0) == 3e4
+
+
+def test_gemm_swiglu_uses_gate_then_up_halves():
+    """Swapping the gate and up halves changes the result as silu's asymmetry says
+    (a transposed stacking fails); each half is the dense GEMM of its rows."""
+    rng = np.random.default_rng(11)
+    M, K, I = 3, 256, 128
+    xq, xs = oracle.quant_act(si.to_bf16_bits(torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))))
+    w = si.to_bf16_bits(torch.from_numpy((rng.standard_normal((2 * I, K)) * 0.05).astype(np.float32)))
+    wq, ws = oracle.quant_wblock(w)
+    h = oracle.gemm_swiglu(xq, xs, wq, ws)
+    g = oracle.gemm(xq, xs, wq[:I], ws[:1])
+    u = oracle.gemm(xq, xs, wq[I:], ws[1:])
+    assert np.array_equal(h, oracle.swiglu(g, u))
+    swapped = oracle.gemm_swiglu(xq, xs, np.concatenate([wq[I:], wq[:I]]), np.concatenate([ws[1:], ws[:1]]))
+    assert not np.allclose(h, swapped)
+    rows = np.array([2, 0])
+    assert np.array_equal(oracle.gemm_swiglu(xq, xs, wq, ws, rows=rows), h[rows])
