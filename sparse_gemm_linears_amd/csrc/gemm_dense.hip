@@ -76,8 +76,10 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *x
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const float gv = acc[r][c][e];
-          // bf16 rounding here is the value h takes in memory
-          hv[r][e] = bf16_to_f32(f32_to_bf16_rne(gv * u[e] / (1.0f + expf(-gv))));
+          // silu with the hardware exp2 and reciprocal (a few ulp in fp32,
+          // far below the bf16 rounding that follows); the bf16 value is
+          // what h holds in memory and what the codes are made from
+          hv[r][e] = bf16_to_f32(f32_to_bf16_rne(gv * u[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv))));
         }
       }
       const int m0 = m_wave + 16 * c;
@@ -106,12 +108,19 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *x
             words[r] = quantize4_exact(v, sc);
           }
         }
-        const int m = m0 + lr;
-        if (m < M) {
-          uint8_t *qrow = so.hq + (int64_t)m * so.I + 128 * tn;
+        // codes through the wave's LDS scratch (16 rows x 128 bytes, 16-byte
+        // chunks XOR-swizzled by row) so that each row goes out as 128
+        // contiguous bytes
 #pragma unroll
-          for (int r = 0; r < C::RT; r++) *reinterpret_cast<uint32_t *>(qrow + 16 * r + 4 * g) = words[r];
-          if (g == 0) so.hs[(int64_t)m * (so.I / kGroup) + tn] = sc;
+        for (int r = 0; r < C::RT; r++)
+          *reinterpret_cast<uint32_t *>(scratch + lr * 128 + ((r ^ (lr & 7)) << 4) + 4 * g) = words[r];
+        if (g == 0 && m0 + lr < M) so.hs[(int64_t)(m0 + lr) * (so.I / kGroup) + tn] = sc;
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+          const int row = 8 * p + (lane >> 3), chunk = lane & 7;
+          const v4i v = *reinterpret_cast<const v4i *>(scratch + row * 128 + ((chunk ^ (row & 7)) << 4));
+          if (m0 + row < M)
+            *reinterpret_cast<v4i *>(so.hq + (int64_t)(m0 + row) * so.I + 128 * tn + 16 * chunk) = v;
         }
       }
     }
