@@ -225,6 +225,7 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
+    swiglu = bench_swiglu(sgl, si, torch, np, dev, bf16, args.steps)
     decode = None if args.no_decode else bench_decode(sgl, si, torch, np, dev, bf16)
     cpu = None if args.no_cpu else cpu_baseline(si, np, args.cpu_rows)
 
@@ -239,9 +240,48 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": per_kernel,
+        "swiglu": swiglu,
         "decode": decode,
     }
     print(json.dumps(out))
+
+
+def bench_swiglu(sgl, si, torch, np, dev, bf16, steps):
+    """The gated-MLP up projection at M=4096 (gate/up 4096 -> 2 x 14336): the fused
+    GEMM + SwiGLU call, with and without the e4m3 output for the down projection,
+    beside the plain GEMM of the same weight and fp8_quant_act of h."""
+    M, K, I = si.PREFILL_M, 4096, 14336
+    xq, xs = sgl.fp8_quant_act(bf16(si.activations(M, K)))
+    wq, ws = sgl.fp8_quant_weight_block(bf16(si.weights(2 * I, K)))
+    y = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    hq = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    hs = torch.empty((M, I // 128), dtype=torch.float32, device=dev)
+    runs = {
+        "gemm_swiglu_quant": lambda: sgl.fp8_block_gemm_swiglu(xq, xs, wq, ws, h, True, hq, hs),
+        "gemm_swiglu": lambda: sgl.fp8_block_gemm_swiglu(xq, xs, wq, ws, h, False),
+        "gemm_only": lambda: sgl.fp8_block_gemm(xq, xs, wq, ws, y),
+        "quant_act_of_h": lambda: sgl.fp8_quant_act(h, hq, hs),
+    }
+    res = {}
+    for name, f in runs.items():
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        entry = {"us": round(us, 2)}
+        if name != "quant_act_of_h":
+            entry["tflops"] = round(2 * M * 2 * I * K / us / 1e6, 1)
+        res[name] = entry
+    del y, h, hq, hs, wq, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(sgl, si, torch, np, dev, bf16):
