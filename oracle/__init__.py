@@ -67,13 +67,16 @@ def _load():
             lib.oracle_e4m3_encode.restype = ctypes.c_uint8
             lib.oracle_quant_act.argtypes = [P, I, I, P, P]
             lib.oracle_quant_wblock.argtypes = [P, I, I, P, P]
+            lib.oracle_quant_act_ue8m0.argtypes = [P, I, I, P, P]
+            lib.oracle_quant_wblock_ue8m0.argtypes = [P, I, I, P, P]
             lib.oracle_prune24_mask.argtypes = [P, P, I, I, P]
             lib.oracle_prune24_compress.argtypes = [P, P, I, I, P, P, P]
             lib.oracle_decompress24.argtypes = [P, P, I, I, P]
             lib.oracle_gemm.argtypes = [P, P, P, P, I, I, I, P]
             lib.oracle_gemm_rows.argtypes = [P, P, P, P, I, I, I, P, I, P]
             lib.oracle_num_threads.restype = ctypes.c_int
-            for f in ("oracle_quant_act", "oracle_quant_wblock", "oracle_prune24_mask",
+            for f in ("oracle_quant_act", "oracle_quant_wblock", "oracle_quant_act_ue8m0",
+                      "oracle_quant_wblock_ue8m0", "oracle_prune24_mask",
                       "oracle_prune24_compress", "oracle_decompress24", "oracle_gemm",
                       "oracle_gemm_rows"):
                 getattr(lib, f).restype = None
@@ -220,6 +223,38 @@ def gemm(xq, xs, wq, ws, rows: np.ndarray | None = None) -> np.ndarray:
 def sparse24_gemm(xq, xs, vals, meta, ws, rows: np.ndarray | None = None) -> np.ndarray:
     """The GEMM on the decompressed 2:4 weight (pruned places contribute zero)."""
     return gemm(xq, xs, decompress24(vals, meta), ws, rows=rows)
+
+
+def quant_act_ue8m0(x_bf16: np.ndarray):
+    """x [M,K] bf16 bits -> (codes [M,K] uint8, UE8M0 exponents [M,K/128] uint8); scale = 2^(e-127)."""
+    _check_bf16(x_bf16, "x")
+    M, K = x_bf16.shape
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    q = np.empty((M, K), np.uint8)
+    e = np.empty((M, K // GROUP), np.uint8)
+    _load().oracle_quant_act_ue8m0(_ptr(x), M, K, _ptr(q), _ptr(e))
+    return q, e
+
+
+def quant_wblock_ue8m0(w_bf16: np.ndarray):
+    """w [N,K] bf16 bits -> (codes [N,K] uint8, UE8M0 exponents [N/128,K/128] uint8)."""
+    _check_bf16(w_bf16, "w")
+    N, K = w_bf16.shape
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    q = np.empty((N, K), np.uint8)
+    e = np.empty((N // GROUP, K // GROUP), np.uint8)
+    _load().oracle_quant_wblock_ue8m0(_ptr(w), N, K, _ptr(q), _ptr(e))
+    return q, e
+
+
+def ue8m0_to_f32(e: np.ndarray) -> np.ndarray:
+    """UE8M0 bytes -> their values 2^(e-127) as fp32 (exact: 2^-127 is an fp32 subnormal)."""
+    return np.ldexp(np.float32(1.0), np.asarray(e, dtype=np.int32) - 127).astype(np.float32)
+
+
+def gemm_ue8m0(xq, xe, wq, we, rows: np.ndarray | None = None) -> np.ndarray:
+    """Block-scaled GEMM with UE8M0 scales: ``gemm`` with scales 2^(e-127)."""
+    return gemm(xq, ue8m0_to_f32(xe), wq, ue8m0_to_f32(we), rows=rows)
 
 
 def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:

@@ -278,6 +278,67 @@ void oracle_gemm_rows(const uint8_t *xq, const float *xs, const uint8_t *wq, con
 }
 
 /* Threads OpenMP will use for the GEMM (reported with CPU timings). */
+/* ------------------------------------------------------ UE8M0 scales ---- */
+
+/*
+ * Power-of-two scales stored as UE8M0 bytes ("FP8 a granularite fine", section
+ * "Format d'echelle UE8M0": scales kept as float8_e8m0fnu).  A byte e stands
+ * for 2^(e - 127).  The pages do not say how amax/448 becomes a power of two;
+ * this oracle takes the smallest power of two that is not below amax/448, so
+ * no value saturates: e is the smallest integer in [0, 254] with
+ * 448 * 2^(e - 127) >= amax (e = 0 when amax is 0 or tiny).  Found here by a
+ * plain upward search in double precision (448 * 2^(e - 127) is exact).
+ */
+static int ue8m0_exponent(double amax) {
+    int e = 0;
+    while (e < 254 && ldexp(448.0, e - 127) < amax) e++;
+    return e;
+}
+
+/* code of x with scale 2^(e - 127): x * 2^(127 - e) is exact in double; one
+ * rounding to e4m3 (never saturating, since |x| <= amax) */
+static uint8_t quantize_one_ue8m0(float x, int e) {
+    return oracle_e4m3_encode(ldexp((double)x, 127 - e));
+}
+
+void oracle_quant_act_ue8m0(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, uint8_t *e_out) {
+    int64_t KB = K / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t kb = 0; kb < KB; kb++) {
+            double amax = 0.0;
+            for (int64_t k = kb * G; k < (kb + 1) * G; k++) {
+                double a = fabs((double)bf16_to_f32(x[m * K + k]));
+                if (a > amax) amax = a;
+            }
+            int e = ue8m0_exponent(amax);
+            e_out[m * KB + kb] = (uint8_t)e;
+            for (int64_t k = kb * G; k < (kb + 1) * G; k++)
+                q[m * K + k] = quantize_one_ue8m0(bf16_to_f32(x[m * K + k]), e);
+        }
+    }
+}
+
+void oracle_quant_wblock_ue8m0(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, uint8_t *e_out) {
+    int64_t NB = N / G, KB = K / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t nb = 0; nb < NB; nb++) {
+        for (int64_t kb = 0; kb < KB; kb++) {
+            double amax = 0.0;
+            for (int64_t n = nb * G; n < (nb + 1) * G; n++)
+                for (int64_t k = kb * G; k < (kb + 1) * G; k++) {
+                    double a = fabs((double)bf16_to_f32(w[n * K + k]));
+                    if (a > amax) amax = a;
+                }
+            int e = ue8m0_exponent(amax);
+            e_out[nb * KB + kb] = (uint8_t)e;
+            for (int64_t n = nb * G; n < (nb + 1) * G; n++)
+                for (int64_t k = kb * G; k < (kb + 1) * G; k++)
+                    q[n * K + k] = quantize_one_ue8m0(bf16_to_f32(w[n * K + k]), e);
+        }
+    }
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);

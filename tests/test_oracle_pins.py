@@ -474,3 +474,117 @@ def test_gemm_swiglu_uses_gate_then_up_halves():
     assert not np.allclose(h, swapped)
     rows = np.array([2, 0])
     assert np.array_equal(oracle.gemm_swiglu(xq, xs, wq, ws, rows=rows), h[rows])
+
+
+# ----------------------------------------------------------- UE8M0 scales ---
+
+def _ue8m0_groups():
+    """[8, 1024] bf16 groups of 128: exact powers of two times 448, just above them,
+    zero, bf16 subnormals, the bf16 maximum, random normals and heavy tails."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((8, 1024)).astype(np.float32)
+    x[0, :128] = 0.0
+    x[0, 128:256] = np.float32(448.0) * np.linspace(-1, 1, 128, dtype=np.float32)   # amax = 448 exactly
+    x[0, 256:384] = np.float32(448.0 * 2 ** -20) * np.sign(rng.standard_normal(128)).astype(np.float32)
+    x[0, 384:512] = rng.standard_normal(128).astype(np.float32) * 1e-39            # bf16 subnormals
+    x[1, :128] = np.float32(3.3895314e38) * np.linspace(-1, 1, 128, dtype=np.float32)  # near the bf16 max
+    x[1, 128:256] = np.float32(450.0)                                               # next bf16 above 448
+    x[1, 256:384] = np.float32(448.0 * (1 + 2 ** -7)) * np.linspace(-1, 1, 128, dtype=np.float32)
+    z = rng.standard_normal((4, 2, 1024))
+    x[2:4] = (z[0] / np.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3)).astype(np.float32)
+    return si.to_bf16_bits(torch.from_numpy(x))
+
+
+def test_ue8m0_exponent_is_the_smallest_covering_power_of_two():
+    xb = _ue8m0_groups()
+    q, e = oracle.quant_act_ue8m0(xb)
+    vals = si.bf16_bits_to_f32(xb)
+    for m in range(vals.shape[0]):
+        for kb in range(vals.shape[1] // 128):
+            amax = Fraction(float(np.abs(vals[m, 128 * kb:128 * kb + 128]).max()))
+            ek = int(e[m, kb])
+            assert Fraction(448) * Fraction(2) ** (ek - 127) >= amax
+            assert ek == 0 or Fraction(448) * Fraction(2) ** (ek - 128) < amax
+    assert e[0, 0] == 0 and e[0, 1] == 127 and e[0, 2] == 107 and e[0, 3] == 0
+    assert e[1, 1] == 128 and e[1, 2] == 128
+
+
+def test_ue8m0_codes_are_the_nearest_of_the_exact_quotient():
+    """Exhaustive nearest-value search on x / 2^(e-127) (an exact rational), independent
+    of the oracle's bisection encoder."""
+    xb = _ue8m0_groups()
+    q, e = oracle.quant_act_ue8m0(xb)
+    vals = si.bf16_bits_to_f32(xb)
+    rng = np.random.default_rng(3)
+    for m in range(vals.shape[0]):
+        for k in rng.choice(vals.shape[1], 48, replace=False):
+            x = float(vals[m, k])
+            neg = math.copysign(1.0, x) < 0
+            ek = int(e[m, k // 128])
+            want = nearest_e4m3(Fraction(x) / Fraction(2) ** (ek - 127), negative=neg)
+            assert q[m, k] == want, (m, k, x, ek)
+
+
+def test_ue8m0_matches_fp32_scales_when_amax_over_448_is_a_power_of_two():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    for m in range(4):
+        for kb in range(4):
+            g = x[m, 128 * kb:128 * kb + 128]
+            g[np.argmax(np.abs(g))] = np.float32(448.0 * 2.0 ** (kb - m * 3))   # amax = 448 * 2^k
+            g[:] = np.clip(g, -448.0 * 2.0 ** (kb - m * 3), 448.0 * 2.0 ** (kb - m * 3))
+    xb = si.to_bf16_bits(torch.from_numpy(x))
+    q8, e = oracle.quant_act_ue8m0(xb)
+    q32, s = oracle.quant_act(xb)
+    assert np.array_equal(q8, q32)
+    assert np.array_equal(oracle.ue8m0_to_f32(e), s)
+
+
+def test_ue8m0_scale_invariance_and_values():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    q0, e0 = oracle.quant_act_ue8m0(si.to_bf16_bits(torch.from_numpy(x)))
+    for j in (-30, -1, 5, 40):
+        qj, ej = oracle.quant_act_ue8m0(si.to_bf16_bits(torch.from_numpy(x * np.float32(2.0 ** j))))
+        assert np.array_equal(qj, q0) and np.array_equal(ej.astype(int), e0.astype(int) + j)
+    v = oracle.ue8m0_to_f32(np.array([0, 1, 126, 127, 128, 254], np.uint8))
+    assert v[3] == 1.0 and v[4] == 2.0 and v[2] == 0.5 and v[5] == 2.0 ** 127
+    assert v[0] == np.float32(2.0 ** -127) and 0 < v[0] < np.finfo(np.float32).tiny
+
+
+def test_ue8m0_weight_blocks_exact():
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((256, 384)) * 0.02).astype(np.float32)
+    w[:128, 128:256] *= 1e4
+    w[128:, :128] = 0.0
+    wb = si.to_bf16_bits(torch.from_numpy(w))
+    q, e = oracle.quant_wblock_ue8m0(wb)
+    vals = si.bf16_bits_to_f32(wb)
+    for nb in range(2):
+        for kb in range(3):
+            blk = vals[128 * nb:128 * nb + 128, 128 * kb:128 * kb + 128]
+            amax = Fraction(float(np.abs(blk).max()))
+            ek = int(e[nb, kb])
+            assert Fraction(448) * Fraction(2) ** (ek - 127) >= amax
+            assert ek == 0 or Fraction(448) * Fraction(2) ** (ek - 128) < amax
+            for (i, j) in [(0, 0), (5, 77), (127, 127), (64, 3)]:
+                x = float(blk[i, j])
+                want = nearest_e4m3(Fraction(x) / Fraction(2) ** (ek - 127), negative=math.copysign(1.0, x) < 0)
+                assert q[128 * nb + i, 128 * kb + j] == want
+    assert e[1, 0] == 0 and np.all(q[128:, :128] == 0)
+
+
+def test_gemm_ue8m0_is_the_gemm_with_power_of_two_scales():
+    rng = np.random.default_rng(10)
+    x = si.to_bf16_bits(torch.from_numpy(rng.standard_normal((8, 256)).astype(np.float32)))
+    w = si.to_bf16_bits(torch.from_numpy((rng.standard_normal((128, 256)) * 0.02).astype(np.float32)))
+    xq, xe = oracle.quant_act_ue8m0(x)
+    wq, we = oracle.quant_wblock_ue8m0(w)
+    y = oracle.gemm_ue8m0(xq, xe, wq, we)
+    # exact: every product is a multiple of 2^-18 times 2^(ex+ew-254); sum exactly with Fractions
+    for m, n in [(0, 0), (3, 77), (7, 127)]:
+        acc = Fraction(0)
+        for kb in range(2):
+            blk = sum(decode_exact(int(xq[m, k])) * decode_exact(int(wq[n, k])) for k in range(128 * kb, 128 * kb + 128))
+            acc += blk * Fraction(2) ** (int(xe[m, kb]) - 127) * Fraction(2) ** (int(we[0, kb]) - 127)
+        assert y[m, n] == float(acc)
