@@ -134,6 +134,32 @@ fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t 
                               int64_t K, uint16_t *y, hipStream_t stream);
 
 /*
+ * Power-of-two (UE8M0) scales ("FP8 a granularite fine", section "Format
+ * d'echelle UE8M0": scales stored as float8_e8m0fnu bytes, as some
+ * checkpoints do and some kernels require).  A byte e stands for 2^(e - 127).
+ * The group / block exponent is the smallest e >= 0 with 448 * 2^(e - 127) >=
+ * amax, the smallest power of two not below amax / 448, so no value
+ * saturates; amax == 0 gives e = 0.  Codes are enc(x * 2^(127 - e)), one
+ * rounding of an exact quotient.  Layouts are those of the fp32-scale calls
+ * with one byte per scale: e [M,K/128] for activations, [N/128,K/128] for
+ * weights.
+ */
+fp8l_status fp8_quant_act_ue8m0(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, uint8_t *e,
+                                hipStream_t stream);
+fp8l_status fp8_quant_weight_block_ue8m0(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, uint8_t *e,
+                                         hipStream_t stream);
+
+/*
+ * Block-scaled FP8 GEMM with UE8M0 scales, applied by the gfx950 MFMA's own
+ * block scaling (no per-block multiply in the kernel):
+ *   y[m,n] = bf16_rne( sum_kb 2^(xe[m,kb] - 127) * 2^(we[n/128,kb] - 127) *
+ *                      sum_{k in kb} dec(xq[m,k]) * dec(wq[n,k]) ), fp32 accumulation.
+ * Dense weights only: the 2:4 sparse MFMA of gfx950 has no block-scaled form.
+ */
+fp8l_status fp8_block_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uint8_t *wq, const uint8_t *we,
+                                 int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+
+/*
  * Gated-MLP up projection with the SwiGLU activation in the GEMM epilogue
  * ("FP8 Quantization" (TensorRT-LLM), section "GEMM + SwiGLU Fusion in
  * Gated-MLP": the gate and up matmuls and the SwiGLU run as one kernel).  With

@@ -28,8 +28,8 @@ FP8L_ERR_DEVICE = 5
 FP8L_ERR_LAUNCH = 6
 
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
-           "fp8_sparse24_gemm", "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear",
-           "fp8lin_status_str")
+           "fp8_sparse24_gemm", "fp8_quant_act_ue8m0", "fp8_quant_weight_block_ue8m0", "fp8_block_gemm_ue8m0",
+           "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear", "fp8lin_status_str")
 MAX_LINEAR_M = 64  # the fused-quantization calls take decode-sized batches
 
 _lock = threading.Lock()
@@ -61,6 +61,9 @@ def load_library():
             "prune24_compress": [P, P, I, I, P, P, P, P],
             "fp8_block_gemm": [P, P, P, P, I, I, I, P, P],
             "fp8_sparse24_gemm": [P, P, P, P, P, I, I, I, P, P],
+            "fp8_quant_act_ue8m0": [P, I, I, P, P, P],
+            "fp8_quant_weight_block_ue8m0": [P, I, I, P, P, P],
+            "fp8_block_gemm_ue8m0": [P, P, P, P, I, I, I, P, P],
             "fp8_block_gemm_swiglu": [P, P, P, P, I, I, I, P, P, P, P],
             "fp8_block_linear": [P, P, P, I, I, I, P, P],
             "fp8_sparse24_linear": [P, P, P, P, I, I, I, P, P],
@@ -238,3 +241,47 @@ def fp8_block_gemm_swiglu(xq, xs, wq, ws, h: torch.Tensor | None = None, quantiz
     _check("fp8_block_gemm_swiglu", load_library().fp8_block_gemm_swiglu(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, I, K, _ptr(h), _ptr(hq), _ptr(hs), _stream(xq)))
     return h, hq, hs
+
+
+def _exps(t: torch.Tensor) -> torch.Tensor:
+    """Accept UE8M0 scales as uint8 or float8_e8m0fnu; returns a uint8 view."""
+    if t.dtype == getattr(torch, "float8_e8m0fnu", None):
+        return t.view(torch.uint8)
+    return t
+
+
+def fp8_quant_act_ue8m0(x: torch.Tensor, q: torch.Tensor | None = None, e: torch.Tensor | None = None):
+    """x [M,K] bf16 -> (q [M,K] e4m3 codes, e [M,K/128] UE8M0 exponent bytes; scale 2^(e-127))."""
+    _want(x, "x", torch.bfloat16)
+    M, K = x.shape
+    q = _out(q, "q", (M, K), torch.uint8, x)
+    e = _out(e, "e", (M, K // GROUP), torch.uint8, x)
+    _check("fp8_quant_act_ue8m0", load_library().fp8_quant_act_ue8m0(_ptr(x), M, K, _ptr(q), _ptr(e), _stream(x)))
+    return q, e
+
+
+def fp8_quant_weight_block_ue8m0(w: torch.Tensor, q: torch.Tensor | None = None, e: torch.Tensor | None = None):
+    """w [N,K] bf16 -> (q [N,K] e4m3 codes, e [N/128,K/128] UE8M0 exponent bytes)."""
+    _want(w, "w", torch.bfloat16)
+    N, K = w.shape
+    q = _out(q, "q", (N, K), torch.uint8, w)
+    e = _out(e, "e", (N // GROUP, K // GROUP), torch.uint8, w)
+    _check("fp8_quant_weight_block_ue8m0",
+           load_library().fp8_quant_weight_block_ue8m0(_ptr(w), N, K, _ptr(q), _ptr(e), _stream(w)))
+    return q, e
+
+
+def fp8_block_gemm_ue8m0(xq, xe, wq, we, y: torch.Tensor | None = None):
+    """(xq [M,K], xe [M,K/128], wq [N,K], we [N/128,K/128], UE8M0 exponents) -> y [M,N] bf16."""
+    xq, wq, xe, we = _codes(xq), _codes(wq), _exps(xe), _exps(we)
+    _want(xq, "xq", torch.uint8)
+    _want(wq, "wq", torch.uint8)
+    M, K = xq.shape
+    N = wq.shape[0]
+    _want(wq, "wq", torch.uint8, (N, K))
+    _want(xe, "xe", torch.uint8, (M, K // GROUP))
+    _want(we, "we", torch.uint8, (N // GROUP, K // GROUP))
+    y = _out(y, "y", (M, N), torch.bfloat16, xq)
+    _check("fp8_block_gemm_ue8m0", load_library().fp8_block_gemm_ue8m0(
+        _ptr(xq), _ptr(xe), _ptr(wq), _ptr(we), M, N, K, _ptr(y), _stream(xq)))
+    return y

@@ -148,6 +148,43 @@ fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   return launched(fp8lin::launch_sparse_gemm(xq, xs, wvals, wmeta, ws, M, N, K, y, stream));
 }
 
+fp8l_status fp8_quant_act_ue8m0(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, uint8_t *e, hipStream_t stream) {
+  if (bad_mk(M, K)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!x || !q || !e) return FP8L_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(e)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{x, M * K * 2}};
+  const Range outs[] = {{q, M * K}, {e, M * (K / 128)}};
+  if (any_alias(outs, 2, ins, 1)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_quant_act_ue8m0(x, M, K, q, e, stream));
+}
+
+fp8l_status fp8_quant_weight_block_ue8m0(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, uint8_t *e,
+                                         hipStream_t stream) {
+  if (bad_nk(N, K)) return FP8L_ERR_SHAPE;
+  if (!w || !q || !e) return FP8L_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(e)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{w, N * K * 2}};
+  const Range outs[] = {{q, N * K}, {e, (N / 128) * (K / 128)}};
+  if (any_alias(outs, 2, ins, 1)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_quant_wblock_ue8m0(w, N, K, q, e, stream));
+}
+
+fp8l_status fp8_block_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uint8_t *wq, const uint8_t *we,
+                                 int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!xq || !xe || !wq || !we || !y) return FP8L_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xe) || !aligned16(wq) || !aligned16(we) || !aligned16(y)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{xq, M * K}, {xe, M * (K / 128)}, {wq, N * K}, {we, (N / 128) * (K / 128)}};
+  const Range outs[] = {{y, M * N * 2}};
+  if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_dense_gemm_ue8m0(xq, xe, wq, we, M, N, K, y, stream));
+}
+
 fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
                                   int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs, hipStream_t stream) {
   if (I <= 0 || bad_mk(M, K) || bad_nk(2 * I, K) || bad_mn(M, I)) return FP8L_ERR_SHAPE;

@@ -75,6 +75,25 @@ __device__ __forceinline__ bool scale_fast_ok(float s) {
   return b >= 0x0D800000u && b < 0x7F800000u;
 }
 
+// UE8M0 (power-of-two) scales: byte e stands for 2^(e - 127).  The exponent of
+// a group is the smallest e >= 0 with 448 * 2^(e - 127) >= amax.  With amax =
+// (1 + f) 2^(E - 127) (fp32 fields E, f; 448 = 1.75 * 2^8) that is E - 8, plus
+// one when f > 0.75, clamped at 0 (zero, subnormal and tiny groups).
+__device__ __forceinline__ uint32_t ue8m0_exponent(uint32_t amax_f32_bits) {
+  const int e = (int)(amax_f32_bits >> 23) - 8 + ((amax_f32_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < 0 ? 0u : (uint32_t)e;
+}
+
+// 2^(127 - e) as an fp32 normal (e <= 253, which every bf16 amax gives).
+__device__ __forceinline__ float ue8m0_inverse(uint32_t e) { return __uint_as_float((254u - e) << 23); }
+
+// Codes of four values with a power-of-two scale: x * 2^(127 - e) is exact
+// (or so small that it rounds to a zero code either way), so one hardware RNE
+// conversion gives the code of the exact quotient; |x| <= amax never saturates.
+__device__ __forceinline__ uint32_t quantize4_pow2(const float (&x)[4], float inv) {
+  return e4m3_pack4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+}
+
 // |bf16| as an integer: ordering of non-NaN magnitudes is the integer ordering.
 __device__ __forceinline__ uint32_t bf16_abs_bits(uint32_t b16) { return b16 & 0x7FFFu; }
 

@@ -153,6 +153,53 @@ struct TokenScales {
   }
 };
 
+// Token exponents (UE8M0 scales, one byte per token and K block) staged like
+// TokenScales: registers <- SB exponent bytes of this thread's token (one
+// 4-byte load when SB = 4), LDS [2][SB][BM] one word per exponent.
+template <int BM, int SB>
+struct TokenExps {
+  uint32_t *lds;
+  const uint8_t *src;
+  uint32_t reg;
+  int tid;
+
+  __device__ __forceinline__ void init(float *lds_, const uint8_t *xe, int M, int KB, int m_base, int tid_) {
+    lds = reinterpret_cast<uint32_t *>(lds_);
+    tid = tid_;
+    src = xe + (int64_t)min(m_base + min(tid, BM - 1), M - 1) * KB;
+  }
+  __device__ __forceinline__ void load(int grp) {
+    if (tid < BM) {
+      if (SB == 4) reg = *reinterpret_cast<const uint32_t *>(src + 4 * grp);
+      else reg = src[grp];
+    }
+  }
+  __device__ __forceinline__ void store(int grp) {
+    if (tid < BM) {
+      uint32_t *d = lds + (grp & 1) * SB * BM + tid;
+      d[0] = reg & 0xFFu;
+      if (SB == 4) {
+        d[BM] = (reg >> 8) & 0xFFu;
+        d[2 * BM] = (reg >> 16) & 0xFFu;
+        d[3 * BM] = reg >> 24;
+      }
+    }
+  }
+  __device__ __forceinline__ uint32_t get(int kb, int row) const {
+    return lds[((kb / SB) & 1) * SB * BM + (kb % SB) * BM + row];
+  }
+};
+
+// v_mfma_scale_f32_16x16x128_f8f6f4, both operands e4m3, accumulating into c:
+// products of A row i scaled by 2^(sa - 127) and of B column j by 2^(sb - 127),
+// where sa / sb are byte 0 of the lane's scale operand (each lane covers its
+// row / column and one 32-wide K quarter; all four quarters carry the same
+// exponent here).
+__device__ __forceinline__ v4f mfma_16x16x128_fp8_e8(const v8i &a, const v8i &b, const v4f &c, uint32_t sa,
+                                                    uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
+}
+
 // Coalesced epilogue: a wave writes its 16 x (16*RT) bf16 sub-tile for token
 // tile c into a private 16 x 256-byte LDS scratch (16-byte chunks XOR-swizzled
 // by row), reads it back as whole rows and stores 256 contiguous bytes per

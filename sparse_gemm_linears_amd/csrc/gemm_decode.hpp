@@ -32,8 +32,9 @@ struct QuantTokens {
   const uint8_t *xq;
   const float *xs;
   int K;
-  static constexpr bool kStaged = false;
+  static constexpr bool kStaged = false, kE8 = false;
   static constexpr int kRawRegs = 9;  // VGPRs per loaded K block
+  typedef float Scale;
   struct Raw {
     v8i q;
     float s;
@@ -51,6 +52,32 @@ struct QuantTokens {
   }
 };
 
+// Tokens quantized by fp8_quant_act_ue8m0: codes and one exponent byte per K
+// block; the MFMA applies 2^(e - 127) itself.
+struct QuantTokensE8 {
+  const uint8_t *xq;
+  const uint8_t *xe;
+  int K;
+  static constexpr bool kStaged = false, kE8 = true;
+  static constexpr int kRawRegs = 9;
+  typedef uint8_t Scale;
+  struct Raw {
+    v8i q;
+    uint32_t e;
+  };
+  __device__ __forceinline__ void stage(uint8_t *, int, int, int) {}
+  __device__ __forceinline__ Raw load(int m, int kb, int g) const {
+    Raw r;
+    r.q = load_frag_global(xq + (int64_t)m * K + (int64_t)kb * kGroup, g);
+    r.e = xe[(int64_t)m * (K / kGroup) + kb];
+    return r;
+  }
+  __device__ __forceinline__ void make(const Raw &r, v8i &frag, uint32_t &e) const {
+    frag = r.q;
+    e = r.e;
+  }
+};
+
 // bf16 tokens quantized on the fly, with the arithmetic of fp8_quant_act (so
 // the codes and scales are the same bits): group amax of |x| over the 128
 // channels of the K block (the four lane groups of a token hold 32 channels
@@ -61,8 +88,9 @@ struct QuantTokens {
 struct Bf16Tokens {
   const uint16_t *x;
   int K;
-  static constexpr bool kStaged = false;
+  static constexpr bool kStaged = false, kE8 = false;
   static constexpr int kRawRegs = 16;  // VGPRs per loaded K block
+  typedef float Scale;
   struct Raw {
     uint4 v[4];
   };
@@ -124,8 +152,9 @@ struct StagedTokens {
   int K;
   uint8_t *codes;
   float *scales;
-  static constexpr bool kStaged = true;
+  static constexpr bool kStaged = true, kE8 = false;
   static constexpr int kRawRegs = 9;
+  typedef float Scale;
   struct Raw {
     v8i q;
     float s;
@@ -185,8 +214,8 @@ inline bool staged_tokens_fit(int64_t M, int64_t K) {
 }
 
 template <class W, class X, int RT, int CT, int NW, int D>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const float *__restrict__ ws, int M, int N,
-                                                         int K, uint16_t *__restrict__ y) {
+__global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typename X::Scale *__restrict__ ws,
+                                                         int M, int N, int K, uint16_t *__restrict__ y) {
   static_assert(128 % (16 * RT) == 0, "a workgroup's rows must sit in one 128-row scale block");
   __shared__ v4f red[NW > 1 ? NW - 1 : 1][RT * CT][64];
   const int lane = threadIdx.x & 63;
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const flo
   const int g = lane >> 4, lr = lane & 15;
   const int KB = K / kGroup;
   const int n0 = blockIdx.x * 16 * RT;
-  const float *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
+  const typename X::Scale *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
   const int n_w = wave < KB ? (KB - wave + NW - 1) / NW : 0;  // K blocks of this wave
 
   int mrow[CT];
@@ -203,7 +232,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const flo
 
   typename W::Frag a[D][RT];
   typename X::Raw b[D][CT];
-  float sw[D];
+  typename X::Scale sw[D];
   auto load_w = [&](int slot, int i) {
     const int kb = wave + i * NW;
 #pragma unroll
@@ -243,11 +272,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const flo
 #pragma unroll
         for (int c = 0; c < CT; c++) {
           v8i bf;
-          float sx;
-          xop.make(b[d][c], bf, sx);
-          const float scl = sx * sw[d];
+          if constexpr (X::kE8) {
+            uint32_t ex;
+            xop.make(b[d][c], bf, ex);
 #pragma unroll
-          for (int r = 0; r < RT; r++) acc[r][c] += scl * wop.mma(a[d][r], bf);
+            for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(a[d][r], bf, acc[r][c], sw[d], ex);
+          } else {
+            float sx;
+            xop.make(b[d][c], bf, sx);
+            const float scl = sx * sw[d];
+#pragma unroll
+            for (int r = 0; r < RT; r++) acc[r][c] += scl * wop.mma(a[d][r], bf);
+          }
         }
         if (i + D < n_w) {
           load_w(d, i + D);

@@ -133,13 +133,13 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *x
 // SWIGLU: the weight is [gate; up] (2I rows); tile tn covers outputs
 // [128 tn, 128 tn + 128) and reads gate rows there into the first panel half
 // and up rows I + 128 tn .. into the second; y is h [M,I].
-template <int BN, int BM, int WN, int WM, int SB, int CR, bool SWIGLU>
-__global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *__restrict__ xq,
-                                                                const float *__restrict__ xs,
-                                                                const uint8_t *__restrict__ wq,
-                                                                const float *__restrict__ ws, int M, int N,
-                                                                int K, uint16_t *__restrict__ y, int tiles_m,
-                                                                int tiles_n, int group_m, SwigluOut so) {
+// E8: UE8M0 scales (xs, ws are exponent bytes) applied by the MFMA's block
+// scaling, accumulating straight into the accumulators with no VALU work.
+template <int BN, int BM, int WN, int WM, int SB, int CR, bool SWIGLU, bool E8 = false>
+__global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
+    const uint8_t *__restrict__ xq, const std::conditional_t<E8, uint8_t, float> *__restrict__ xs,
+    const uint8_t *__restrict__ wq, const std::conditional_t<E8, uint8_t, float> *__restrict__ ws, int M, int N,
+    int K, uint16_t *__restrict__ y, int tiles_m, int tiles_n, int group_m, SwigluOut so) {
   using C = DenseTile<BN, BM, WN, WM>;
   // One LDS object per stage and panel: copies into one stage and fragment
   // reads of the other are then known not to overlap, so reads never wait for
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
   const rsrc_t rw0 = panel_rows128(wq + (int64_t)w_half0 * K, N - w_half0, 0, K);
   const rsrc_t rw1 = panel_rows128(wq + (int64_t)w_half1 * K, N - w_half1, 0, K);
   const rsrc_t rx0 = panel_rows128(xpanel, M - m_base, 0, K), rx1 = panel_rows128(xpanel, M - m_base, 128, K);
-  TokenScales<BM, SB> scales;
+  std::conditional_t<E8, TokenExps<BM, SB>, TokenScales<BM, SB>> scales;
   scales.init(lds_s, xs, M, KB, m_base, tid);
 
   // One 128-wide K block of the weight and token panels into LDS stage `st`.
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
     for (int c = 0; c < C::CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int nb_wave = min((wn0 == 0 ? w_half0 : w_half1) / kGroup, NB - 1);
-  const float *ws_row = ws + (int64_t)nb_wave * KB;
+  const auto *ws_row = ws + (int64_t)nb_wave * KB;
 
   // Token fragments live in registers one K step ahead: bx[ST] holds this
   // step's, and the next step's are read from LDS during row tiles
@@ -228,12 +228,17 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
     const bool more_a = kb + 1 < KB, more_b = kb + 2 < KB;
     const bool scale_load = (kb % SB == 0) && (kb + SB < KB);
     if (scale_load) scales.load(kb / SB + 1);
-    const float sw = ws_row[kb];
     const uint8_t *At = ST ? lds_a1 : lds_a0;
     const uint8_t *Bn = ST ? lds_b0 : lds_b1;  // tokens of kb+1
-    float scl[C::CT];
+    // fp32 scales: scl = xs * ws per token, applied by FMAs; UE8M0: the two
+    // exponents go to the MFMA
+    std::conditional_t<E8, uint32_t, float> scl[C::CT];
+    const auto sw = ws_row[kb];
 #pragma unroll
-    for (int c = 0; c < C::CT; c++) scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
+    for (int c = 0; c < C::CT; c++) {
+      if constexpr (E8) scl[c] = scales.get(kb, wm0 + 16 * c + lr);
+      else scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
+    }
     v8i an = load_frag_at(At, a_lo, a_hi, 0);
     v4f p_prev, p_prev2;
 #pragma unroll
@@ -249,28 +254,39 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(const uint8_t *
         }
       }
       const v8i af = an;
+      // a compiler-only fence: the next row's fragment reads are not hoisted
+      // above this row (with no VALU work between the MFMAs, the compiler
+      // would read every fragment of the step up front and spill)
+      if constexpr (E8) asm volatile("" ::: "memory");
       if (r + 1 < C::RT) an = load_frag_at(At, a_lo, a_hi, (r + 1) * 2048);
       if (r >= kBReadRow && more_a) read_b(Bn, bx[ST ^ 1], r - kBReadRow);
 #pragma unroll
       for (int c = 0; c < C::CT; c++) {
-        const v4f p = mfma_16x16x128_fp8(af, bx[ST][c], v4f{0.f, 0.f, 0.f, 0.f});
-        // scale the partial of two MFMAs back: its result is ready, so the
-        // FMAs issue without hazard waits while this MFMA runs
-        const int t = r * C::CT + c;
-        if (t > 1) {
-          const int pr = (t - 2) / C::CT, pc = (t - 2) % C::CT;
-          acc[pr][pc] += scl[pc] * p_prev2;
-          pin(acc[pr][pc]);
+        if constexpr (E8) {
+          acc[r][c] = mfma_16x16x128_fp8_e8(af, bx[ST][c], acc[r][c], (uint32_t)sw, scl[c]);
+          pin(acc[r][c]);  // keeps the MFMA in its row (nothing else reads acc until the epilogue)
+        } else {
+          const v4f p = mfma_16x16x128_fp8(af, bx[ST][c], v4f{0.f, 0.f, 0.f, 0.f});
+          // scale the partial of two MFMAs back: its result is ready, so the
+          // FMAs issue without hazard waits while this MFMA runs
+          const int t = r * C::CT + c;
+          if (t > 1) {
+            const int pr = (t - 2) / C::CT, pc = (t - 2) % C::CT;
+            acc[pr][pc] += scl[pc] * p_prev2;
+            pin(acc[pr][pc]);
+          }
+          p_prev2 = p_prev;
+          p_prev = p;
         }
-        p_prev2 = p_prev;
-        p_prev = p;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    acc[C::RT - 1][C::CT - 2] += scl[C::CT - 2] * p_prev2;
-    pin(acc[C::RT - 1][C::CT - 2]);
-    acc[C::RT - 1][C::CT - 1] += scl[C::CT - 1] * p_prev;
-    pin(acc[C::RT - 1][C::CT - 1]);
+    if constexpr (!E8) {
+      acc[C::RT - 1][C::CT - 2] += scl[C::CT - 2] * p_prev2;
+      pin(acc[C::RT - 1][C::CT - 2]);
+      acc[C::RT - 1][C::CT - 1] += scl[C::CT - 1] * p_prev;
+      pin(acc[C::RT - 1][C::CT - 1]);
+    }
     if (more_a || scale_load) wait_global_loads();
     if (scale_load) scales.store(kb / SB + 1);
     __syncthreads();
@@ -325,6 +341,9 @@ struct DenseWeight {
   __device__ __forceinline__ v4f mma(const Frag &a, const v8i &b) const {
     return mfma_16x16x128_fp8(a, b, v4f{0.f, 0.f, 0.f, 0.f});
   }
+  __device__ __forceinline__ v4f mma_e8(const Frag &a, const v8i &b, const v4f &c, uint32_t ea, uint32_t eb) const {
+    return mfma_16x16x128_fp8_e8(a, b, c, ea, eb);
+  }
 };
 
 // ================================================================ dispatch ==
@@ -345,8 +364,8 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
 }
 
 template <class X, int RT, int CT, int NW, int D>
-static hipError_t launch_decode(X xop, const uint8_t *wq, const float *ws, int M, int N, int K, uint16_t *y,
-                                hipStream_t stream) {
+static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
+                                uint16_t *y, hipStream_t stream) {
   const size_t lds = X::kStaged ? StagedTokens::lds_bytes(M, K) : 0;
   hipLaunchKernelGGL((decode_kernel<DenseWeight, X, RT, CT, NW, D>), dim3(N / (16 * RT)), dim3(NW * 64), lds, stream,
                      DenseWeight{wq, K}, xop, ws, M, N, K, y);
@@ -358,8 +377,8 @@ static hipError_t launch_decode(X xop, const uint8_t *wq, const float *ws, int M
 // rows per workgroup when N is large enough to keep every CU busy, since each
 // workgroup re-reads the M x K activations from L2.
 template <class X, int CT>
-static hipError_t launch_decode_for(X xop, const uint8_t *wq, const float *ws, int M, int N, int K, uint16_t *y,
-                                    hipStream_t stream) {
+static hipError_t launch_decode_for(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
+                                    uint16_t *y, hipStream_t stream) {
   if constexpr (CT == 1)
     if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wq, ws, M, N, K, y, stream);
   if constexpr (CT <= 2)
@@ -372,8 +391,8 @@ static hipError_t launch_decode_for(X xop, const uint8_t *wq, const float *ws, i
 }
 
 template <class X>
-static hipError_t launch_dense_decode(X xop, const uint8_t *wq, const float *ws, int M, int N, int K, uint16_t *y,
-                                      hipStream_t stream) {
+static hipError_t launch_dense_decode(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
+                                      uint16_t *y, hipStream_t stream) {
   if constexpr (X::kStaged) {
     return launch_decode_for<X, 1>(xop, wq, ws, M, N, K, y, stream);  // M <= 8
   } else {
@@ -403,6 +422,22 @@ hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const ui
   else
     hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 1, 4, true>), dim3(tiles_m * tiles_n), dim3(C::kThreads),
                        0, stream, xq, xs, wq, ws, m, (int)(2 * I), k, h, tiles_m, tiles_n, 4, so);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uint8_t *wq, const uint8_t *we,
+                                   int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  using C = DenseTile<256, 256, 2, 4>;
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (m <= 64) return launch_dense_decode(QuantTokensE8{xq, xe, k}, wq, we, m, n, k, y, stream);
+  const int tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
+  const SwigluOut none{nullptr, nullptr, 0};
+  if ((k / kGroup) % 4 == 0)
+    hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 4, 4, false, true>), dim3(tiles_m * tiles_n),
+                       dim3(C::kThreads), 0, stream, xq, xe, wq, we, m, n, k, y, tiles_m, tiles_n, 4, none);
+  else
+    hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 1, 4, false, true>), dim3(tiles_m * tiles_n),
+                       dim3(C::kThreads), 0, stream, xq, xe, wq, we, m, n, k, y, tiles_m, tiles_n, 4, none);
   return hipGetLastError();
 }
 

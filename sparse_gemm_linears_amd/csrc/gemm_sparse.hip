@@ -252,8 +252,8 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
 }
 
 template <class X, int RT, int CT, int NW, int D>
-static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, const float *ws, int M, int N, int K,
-                                uint16_t *y, hipStream_t stream) {
+static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, const typename X::Scale *ws, int M,
+                                int N, int K, uint16_t *y, hipStream_t stream) {
   const size_t lds = X::kStaged ? StagedTokens::lds_bytes(M, K) : 0;
   hipLaunchKernelGGL((decode_kernel<SparseWeight, X, RT, CT, NW, D>), dim3(N / (16 * RT)), dim3(NW * 64), lds,
                      stream, SparseWeight{wv, wm, K}, xop, ws, M, N, K, y);

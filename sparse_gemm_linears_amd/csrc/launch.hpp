@@ -9,6 +9,12 @@ namespace fp8lin {
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, hipStream_t stream);
 hipError_t launch_quant_wblock(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, hipStream_t stream);
+// UE8M0 (power-of-two) scale variants: one exponent byte per group / block.
+hipError_t launch_quant_act_ue8m0(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, uint8_t *e, hipStream_t stream);
+hipError_t launch_quant_wblock_ue8m0(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, uint8_t *e,
+                                     hipStream_t stream);
+hipError_t launch_dense_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uint8_t *wq, const uint8_t *we,
+                                   int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
 hipError_t launch_prune24(const uint16_t *w, const float *col_norm, int64_t N, int64_t K, uint8_t *vals,
                           uint8_t *meta, float *s, hipStream_t stream);
 hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
