@@ -226,6 +226,7 @@ def main():
     torch.cuda.empty_cache()
 
     swiglu = bench_swiglu(sgl, si, torch, np, dev, bf16, args.steps)
+    ue8m0 = bench_ue8m0(sgl, si, torch, np, dev, bf16, args.steps)
     decode = None if args.no_decode else bench_decode(sgl, si, torch, np, dev, bf16)
     cpu = None if args.no_cpu else cpu_baseline(si, np, args.cpu_rows)
 
@@ -241,9 +242,45 @@ def main():
         "cpu_baseline": cpu,
         "kernels": per_kernel,
         "swiglu": swiglu,
+        "ue8m0": ue8m0,
         "decode": decode,
     }
     print(json.dumps(out))
+
+
+def time_calls(torch, f, reps):
+    """Mean time of back-to-back calls of f, from HIP events on the current stream."""
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def bench_ue8m0(sgl, si, torch, np, dev, bf16, steps):
+    """UE8M0 (power-of-two) scales on the four Llama-3-8B shapes at M=4096: the two
+    quantizers and the GEMM whose scales the MFMA applies."""
+    M = si.PREFILL_M
+    res = {}
+    for name, K, N in si.LLAMA3_8B:
+        x, w = bf16(si.activations(M, K)), bf16(si.weights(N, K))
+        xq, xe = sgl.fp8_quant_act_ue8m0(x)
+        wq, we = sgl.fp8_quant_weight_block_ue8m0(w)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t_qa = time_calls(torch, lambda: sgl.fp8_quant_act_ue8m0(x, xq, xe), steps)
+        t_qw = time_calls(torch, lambda: sgl.fp8_quant_weight_block_ue8m0(w, wq, we), steps)
+        t_g = time_calls(torch, lambda: sgl.fp8_block_gemm_ue8m0(xq, xe, wq, we, y), steps)
+        tf = 2 * M * N * K / t_g / 1e6
+        res[name] = {"quant_act_us": round(t_qa, 2), "quant_wblock_us": round(t_qw, 2), "gemm_us": round(t_g, 2),
+                     "gemm_tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        del x, w, xq, xe, wq, we, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_swiglu(sgl, si, torch, np, dev, bf16, steps):

@@ -134,6 +134,28 @@ fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t 
                               int64_t K, uint16_t *y, hipStream_t stream);
 
 /*
+ * Grouped (mixture-of-experts) block-scaled FP8 GEMM, contiguous layout ("FP8
+ * a granularite fine", section "Chemin rapide de DeepGEMM": the expert layers
+ * of MoE models run as grouped FP8 GEMMs).  The tokens routed to expert g are
+ * the rows offsets[g] .. offsets[g+1]-1 of X and Y; each group is
+ * fp8_block_gemm with that expert's weight.
+ *
+ *   xq [M,K] e4m3, xs [M,K/128] fp32          tokens, sorted by expert
+ *   wq [G,N,K] e4m3, ws [G,N/128,K/128] fp32  one 128x128-block-scaled weight per expert
+ *   offsets [G+1] int32, device memory        offsets[0] = 0, nondecreasing,
+ *                                             offsets[G] = M (empty groups allowed)
+ *   y [M,N] bf16
+ * The group sizes stay on the device: the launch covers the worst case
+ * (ceil(M/256) + G token tiles) and surplus workgroups exit at once, so no
+ * host synchronisation is needed.  Offsets that break the rules give
+ * unspecified rows but never an access outside X, Y or the weights.
+ * 1 <= G <= 4096, G*N*K <= 2^36.
+ */
+fp8l_status fp8_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                             const int32_t *offsets, int64_t G, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                             hipStream_t stream);
+
+/*
  * Power-of-two (UE8M0) scales ("FP8 a granularite fine", section "Format
  * d'echelle UE8M0": scales stored as float8_e8m0fnu bytes, as some
  * checkpoints do and some kernels require).  A byte e stands for 2^(e - 127).

@@ -257,6 +257,20 @@ def gemm_ue8m0(xq, xe, wq, we, rows: np.ndarray | None = None) -> np.ndarray:
     return gemm(xq, ue8m0_to_f32(xe), wq, ue8m0_to_f32(we), rows=rows)
 
 
+def grouped_gemm(xq, xs, wq, ws, offsets, rows: np.ndarray | None = None) -> np.ndarray:
+    """Grouped GEMM: row m of the result is ``gemm`` of row m with expert g's weight
+    wq[g], ws[g], where offsets[g] <= m < offsets[g+1]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    M = xq.shape[0]
+    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, wq.shape[1]), np.float64)
+    group = np.searchsorted(offsets, rows, side="right") - 1
+    for g in np.unique(group):
+        sel = np.nonzero(group == g)[0]
+        out[sel] = gemm(xq, xs, wq[g], ws[g], rows=rows[sel])
+    return out
+
+
 def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     """SwiGLU of gate and up values in fp64: silu(g) * u with silu(g) = g / (1 + exp(-g))."""
     g = np.asarray(g, dtype=np.float64)

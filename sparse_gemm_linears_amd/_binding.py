@@ -29,7 +29,7 @@ FP8L_ERR_LAUNCH = 6
 
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
            "fp8_sparse24_gemm", "fp8_quant_act_ue8m0", "fp8_quant_weight_block_ue8m0", "fp8_block_gemm_ue8m0",
-           "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear", "fp8lin_status_str")
+           "fp8_grouped_gemm", "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear", "fp8lin_status_str")
 MAX_LINEAR_M = 64  # the fused-quantization calls take decode-sized batches
 
 _lock = threading.Lock()
@@ -65,6 +65,7 @@ def load_library():
             "fp8_quant_weight_block_ue8m0": [P, I, I, P, P, P],
             "fp8_block_gemm_ue8m0": [P, P, P, P, I, I, I, P, P],
             "fp8_block_gemm_swiglu": [P, P, P, P, I, I, I, P, P, P, P],
+            "fp8_grouped_gemm": [P, P, P, P, P, I, I, I, I, P, P],
             "fp8_block_linear": [P, P, P, I, I, I, P, P],
             "fp8_sparse24_linear": [P, P, P, P, I, I, I, P, P],
         }
@@ -284,4 +285,22 @@ def fp8_block_gemm_ue8m0(xq, xe, wq, we, y: torch.Tensor | None = None):
     y = _out(y, "y", (M, N), torch.bfloat16, xq)
     _check("fp8_block_gemm_ue8m0", load_library().fp8_block_gemm_ue8m0(
         _ptr(xq), _ptr(xe), _ptr(wq), _ptr(we), M, N, K, _ptr(y), _stream(xq)))
+    return y
+
+
+def fp8_grouped_gemm(xq, xs, wq, ws, offsets: torch.Tensor, y: torch.Tensor | None = None):
+    """Grouped (MoE) GEMM: rows offsets[g] .. offsets[g+1]-1 of (xq [M,K], xs) times expert g of
+    (wq [G,N,K], ws [G,N/128,K/128]); offsets is a device int32 tensor [G+1].  -> y [M,N] bf16."""
+    xq, wq = _codes(xq), _codes(wq)
+    _want(xq, "xq", torch.uint8)
+    _want(wq, "wq", torch.uint8)
+    M, K = xq.shape
+    G, N = wq.shape[0], wq.shape[1]
+    _want(wq, "wq", torch.uint8, (G, N, K))
+    _want(xs, "xs", torch.float32, (M, K // GROUP))
+    _want(ws, "ws", torch.float32, (G, N // GROUP, K // GROUP))
+    _want(offsets, "offsets", torch.int32, (G + 1,))
+    y = _out(y, "y", (M, N), torch.bfloat16, xq)
+    _check("fp8_grouped_gemm", load_library().fp8_grouped_gemm(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offsets), G, M, N, K, _ptr(y), _stream(xq)))
     return y

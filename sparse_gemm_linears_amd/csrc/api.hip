@@ -68,6 +68,7 @@ bool bad_nk(int64_t N, int64_t K) {
 bool bad_mn(int64_t M, int64_t N) { return M * N > kMaxElems; }
 
 constexpr int64_t kMaxLinearM = 64;  // the fused-quantization calls are the decode form
+constexpr int64_t kMaxGroups = 4096;   // experts of one grouped GEMM
 
 fp8l_status launched(hipError_t e) {
   if (e != hipSuccess) {
@@ -183,6 +184,26 @@ fp8l_status fp8_block_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uin
   if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
   return launched(fp8lin::launch_dense_gemm_ue8m0(xq, xe, wq, we, M, N, K, y, stream));
+}
+
+fp8l_status fp8_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                             const int32_t *offsets, int64_t G, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                             hipStream_t stream) {
+  if (G <= 0 || G > kMaxGroups || bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N) || G * N * K > kMaxElems)
+    return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!xq || !xs || !wq || !ws || !offsets || !y) return FP8L_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(offsets) || !aligned16(y))
+    return FP8L_ERR_ALIGN;
+  const Range ins[] = {{xq, M * K},
+                       {xs, M * (K / 128) * 4},
+                       {wq, G * N * K},
+                       {ws, G * (N / 128) * (K / 128) * 4},
+                       {offsets, (G + 1) * 4}};
+  const Range outs[] = {{y, M * N * 2}};
+  if (any_alias(outs, 1, ins, 5)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_dense_grouped_gemm(xq, xs, wq, ws, offsets, G, M, N, K, y, stream));
 }
 
 fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,

@@ -39,12 +39,17 @@ struct DenseTile {
   static_assert(kWaves * 4096 <= kATile, "epilogue scratch fits in one weight stage");
 };
 
-// Output of the SwiGLU epilogue: h [M,I] bf16 (the kernel's y) and, when hq
-// is not NULL, its per-token 1x128 e4m3 codes hq [M,I] and scales hs [M,I/128].
-struct SwigluOut {
+// Arguments of the optional tile-kernel modes.
+//  SwiGLU epilogue: h [M,I] bf16 is the kernel's y; when hq is not NULL, its
+//  per-token 1x128 e4m3 codes hq [M,I] and scales hs [M,I/128] as well.
+//  Grouped GEMM: G expert weights [G][N][K] (scales [G][N/128][K/128]); the
+//  tokens of expert g are rows offsets[g] .. offsets[g+1] - 1 of X and Y.
+struct TileExtra {
   uint8_t *hq;
   float *hs;
   int I;
+  const int32_t *offsets;
+  int G;
 };
 
 // SwiGLU epilogue.  The two waves with the same token slice hold the gate
@@ -57,7 +62,7 @@ struct SwigluOut {
 // give the group amax).
 template <class C>
 __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *xch, uint8_t *scratch, uint16_t *h,
-                                                const SwigluOut &so, int M, int m_wave, int tn, int wave, int wn0,
+                                                const TileExtra &so, int M, int m_wave, int tn, int wave, int wn0,
                                                 int lane) {
   const int lr = lane & 15, g = lane >> 4, slot = wave % C::kWavesPerSlice;
   const bool gate = wn0 == 0;
@@ -135,11 +140,14 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *x
 // and up rows I + 128 tn .. into the second; y is h [M,I].
 // E8: UE8M0 scales (xs, ws are exponent bytes) applied by the MFMA's block
 // scaling, accumulating straight into the accumulators with no VALU work.
-template <int BN, int BM, int WN, int WM, int SB, int CR, bool SWIGLU, bool E8 = false>
+// GROUPED: tiles_m counts token tiles over all groups (an upper bound: the
+// sum of ceil(rows_g / BM) <= ceil(M / BM) + G); a workgroup whose tile lies
+// past the last group's returns at once.
+template <int BN, int BM, int WN, int WM, int SB, int CR, bool SWIGLU, bool E8 = false, bool GROUPED = false>
 __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
     const uint8_t *__restrict__ xq, const std::conditional_t<E8, uint8_t, float> *__restrict__ xs,
-    const uint8_t *__restrict__ wq, const std::conditional_t<E8, uint8_t, float> *__restrict__ ws, int M, int N,
-    int K, uint16_t *__restrict__ y, int tiles_m, int tiles_n, int group_m, SwigluOut so) {
+    const uint8_t *__restrict__ wq_all, const std::conditional_t<E8, uint8_t, float> *__restrict__ ws_all,
+    int M_all, int N, int K, uint16_t *__restrict__ y, int tiles_m, int tiles_n, int group_m, TileExtra so) {
   using C = DenseTile<BN, BM, WN, WM>;
   // One LDS object per stage and panel: copies into one stage and fragment
   // reads of the other are then known not to overlap, so reads never wait for
@@ -157,7 +165,34 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
   tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
-  const int m_base = tm * BM, n_base = tn * BN;
+  // token rows [m_base, M) of this tile and its weight
+  int m_base = tm * BM, M = M_all;
+  const uint8_t *wq = wq_all;
+  const auto *ws = ws_all;
+  if constexpr (GROUPED) {
+    // token tiles are numbered group after group, ceil(rows_g / BM) per group
+    int t = tm, sel = -1, m0 = 0, m1 = 0;
+    // offsets are clamped into [0, M_all] and made nondecreasing, so that any
+    // contents keep every access inside X and Y
+    for (int q = 0; q < so.G; q++) {
+      const int o0 = min(max(so.offsets[q], 0), M_all), o1 = min(max(so.offsets[q + 1], o0), M_all);
+      const int nt = (o1 - o0 + BM - 1) / BM;
+      if (t < nt) {
+        sel = q;
+        m0 = o0 + t * BM;
+        m1 = o1;
+        break;
+      }
+      t -= nt;
+    }
+    sel = __builtin_amdgcn_readfirstlane(sel);
+    if (sel < 0) return;  // past the last group's tiles (uniform: before any barrier)
+    m_base = __builtin_amdgcn_readfirstlane(m0);
+    M = __builtin_amdgcn_readfirstlane(m1);
+    wq = wq_all + (int64_t)sel * N * K;
+    ws = ws_all + (int64_t)sel * (N / kGroup) * (K / kGroup);
+  }
+  const int n_base = tn * BN;
   const int wn0 = (wave / WM) * C::kWaveN, wm0 = (wave % WM) * C::kWaveM;
 
   // Copy slab i of this wave covers panel rows r0 = (i*kWaves + wave)*8 .. +7;
@@ -353,7 +388,7 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
                               int K, uint16_t *y, hipStream_t stream) {
   using C = DenseTile<BN, BM, WN, WM>;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const SwigluOut none{nullptr, nullptr, 0};
+  const TileExtra none{nullptr, nullptr, 0, nullptr, 0};
   if ((K / kGroup) % 4 == 0)
     hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false>), dim3(tiles_m * tiles_n),
                        dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, none);
@@ -415,7 +450,7 @@ hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const ui
   using C = DenseTile<256, 256, 2, 4>;
   const int m = (int)M, k = (int)K;
   const int tiles_m = (m + 255) / 256, tiles_n = (int)(I / 128);
-  const SwigluOut so{hq, hs, (int)I};
+  const TileExtra so{hq, hs, (int)I, nullptr, 0};
   if ((k / kGroup) % 4 == 0)
     hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 4, 4, true>), dim3(tiles_m * tiles_n), dim3(C::kThreads),
                        0, stream, xq, xs, wq, ws, m, (int)(2 * I), k, h, tiles_m, tiles_n, 4, so);
@@ -431,13 +466,29 @@ hipError_t launch_dense_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const u
   const int m = (int)M, n = (int)N, k = (int)K;
   if (m <= 64) return launch_dense_decode(QuantTokensE8{xq, xe, k}, wq, we, m, n, k, y, stream);
   const int tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
-  const SwigluOut none{nullptr, nullptr, 0};
+  const TileExtra none{nullptr, nullptr, 0, nullptr, 0};
   if ((k / kGroup) % 4 == 0)
     hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 4, 4, false, true>), dim3(tiles_m * tiles_n),
                        dim3(C::kThreads), 0, stream, xq, xe, wq, we, m, n, k, y, tiles_m, tiles_n, 4, none);
   else
     hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 1, 4, false, true>), dim3(tiles_m * tiles_n),
                        dim3(C::kThreads), 0, stream, xq, xe, wq, we, m, n, k, y, tiles_m, tiles_n, 4, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                                    const int32_t *offsets, int64_t G, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                                    hipStream_t stream) {
+  using C = DenseTile<256, 256, 2, 4>;
+  const int m = (int)M, n = (int)N, k = (int)K;
+  const int tiles_m = (m + 255) / 256 + (int)G, tiles_n = (n + 255) / 256;
+  const TileExtra ex{nullptr, nullptr, 0, offsets, (int)G};
+  if ((k / kGroup) % 4 == 0)
+    hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 4, 4, false, false, true>), dim3(tiles_m * tiles_n),
+                       dim3(C::kThreads), 0, stream, xq, xs, wq, ws, m, n, k, y, tiles_m, tiles_n, 4, ex);
+  else
+    hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 1, 4, false, false, true>), dim3(tiles_m * tiles_n),
+                       dim3(C::kThreads), 0, stream, xq, xs, wq, ws, m, n, k, y, tiles_m, tiles_n, 4, ex);
   return hipGetLastError();
 }
 

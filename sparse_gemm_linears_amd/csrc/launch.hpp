@@ -22,6 +22,12 @@ hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *
 hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
                               const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
 
+// Grouped (MoE) dense GEMM: expert g multiplies rows offsets[g] .. offsets[g+1]-1
+// (device int32 offsets, nondecreasing, offsets[0] = 0, offsets[G] = M).
+hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                                    const int32_t *offsets, int64_t G, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                                    hipStream_t stream);
+
 // Dense GEMM on a [gate; up] weight (2I rows) with the SwiGLU epilogue:
 // h = bf16(silu(g) * u), plus fp8_quant_act(h) when hq is not NULL.
 hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,

@@ -588,3 +588,30 @@ def test_gemm_ue8m0_is_the_gemm_with_power_of_two_scales():
             blk = sum(decode_exact(int(xq[m, k])) * decode_exact(int(wq[n, k])) for k in range(128 * kb, 128 * kb + 128))
             acc += blk * Fraction(2) ** (int(xe[m, kb]) - 127) * Fraction(2) ** (int(we[0, kb]) - 127)
         assert y[m, n] == float(acc)
+
+
+# ---------------------------------------------------------- grouped GEMM ---
+
+def test_grouped_gemm_oracle_routes_rows_to_their_expert():
+    rng = np.random.default_rng(12)
+    M, K, N, G = 40, 256, 128, 3
+    xq, xs = oracle.quant_act(si.to_bf16_bits(torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))))
+    ws_, wq_ = [], []
+    for g in range(G):
+        q, s = oracle.quant_wblock(si.to_bf16_bits(torch.from_numpy((rng.standard_normal((N, K)) * 0.02 * (g + 1)).astype(np.float32))))
+        wq_.append(q)
+        ws_.append(s)
+    wq, ws = np.stack(wq_), np.stack(ws_)
+    offsets = np.array([0, 17, 17, 40])          # expert 1 gets no tokens
+    y = oracle.grouped_gemm(xq, xs, wq, ws, offsets)
+    assert np.array_equal(y[:17], oracle.gemm(xq[:17], xs[:17], wq[0], ws[0]))
+    assert np.array_equal(y[17:], oracle.gemm(xq[17:], xs[17:], wq[2], ws[2]))
+    # one group covering everything is the plain GEMM
+    assert np.array_equal(oracle.grouped_gemm(xq, xs, wq[1:2], ws[1:2], np.array([0, M])),
+                          oracle.gemm(xq, xs, wq[1], ws[1]))
+    # rows are independent of the order experts are listed in (a swapped lookup fails)
+    perm = oracle.grouped_gemm(xq, xs, wq[::-1].copy(), ws[::-1].copy(), np.array([0, 0, 23, 40]))
+    assert np.array_equal(perm[:23], oracle.gemm(xq[:23], xs[:23], wq[1], ws[1]))
+    assert np.array_equal(perm[23:], oracle.gemm(xq[23:], xs[23:], wq[0], ws[0]))
+    rows = np.array([39, 0, 16, 17])
+    assert np.array_equal(oracle.grouped_gemm(xq, xs, wq, ws, offsets, rows=rows), y[rows])
