@@ -68,6 +68,8 @@ def _load():
             lib.oracle_quant_act.argtypes = [P, I, I, P, P]
             lib.oracle_quant_wblock.argtypes = [P, I, I, P, P]
             lib.oracle_quant_act_ue8m0.argtypes = [P, I, I, P, P]
+            lib.oracle_quant_act_static.argtypes = [P, I, I, ctypes.c_float, P, P]
+            lib.oracle_quant_act_tensor.argtypes = [P, I, I, P, P]
             lib.oracle_quant_wblock_ue8m0.argtypes = [P, I, I, P, P]
             lib.oracle_prune24_mask.argtypes = [P, P, I, I, P]
             lib.oracle_prune24_compress.argtypes = [P, P, I, I, P, P, P]
@@ -76,6 +78,7 @@ def _load():
             lib.oracle_gemm_rows.argtypes = [P, P, P, P, I, I, I, P, I, P]
             lib.oracle_num_threads.restype = ctypes.c_int
             for f in ("oracle_quant_act", "oracle_quant_wblock", "oracle_quant_act_ue8m0",
+                      "oracle_quant_act_static", "oracle_quant_act_tensor",
                       "oracle_quant_wblock_ue8m0", "oracle_prune24_mask",
                       "oracle_prune24_compress", "oracle_decompress24", "oracle_gemm",
                       "oracle_gemm_rows"):
@@ -223,6 +226,30 @@ def gemm(xq, xs, wq, ws, rows: np.ndarray | None = None) -> np.ndarray:
 def sparse24_gemm(xq, xs, vals, meta, ws, rows: np.ndarray | None = None) -> np.ndarray:
     """The GEMM on the decompressed 2:4 weight (pruned places contribute zero)."""
     return gemm(xq, xs, decompress24(vals, meta), ws, rows=rows)
+
+
+def quant_act_static(x_bf16: np.ndarray, s: float):
+    """x [M,K] bf16 bits with one given fp32 scale s -> (codes enc(fp32(x/s)) saturating, s broadcast
+    to [M,K/128])."""
+    _check_bf16(x_bf16, "x")
+    M, K = x_bf16.shape
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    q = np.empty((M, K), np.uint8)
+    sa = np.empty((M, K // GROUP), np.float32)
+    _load().oracle_quant_act_static(_ptr(x), M, K, ctypes.c_float(float(np.float32(s))), _ptr(q), _ptr(sa))
+    return q, sa
+
+
+def quant_act_tensor(x_bf16: np.ndarray):
+    """Per-tensor dynamic scaling: s = fp32(amax over all of x / 448); codes and s broadcast as in
+    ``quant_act_static``."""
+    _check_bf16(x_bf16, "x")
+    M, K = x_bf16.shape
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    q = np.empty((M, K), np.uint8)
+    sa = np.empty((M, K // GROUP), np.float32)
+    _load().oracle_quant_act_tensor(_ptr(x), M, K, _ptr(q), _ptr(sa))
+    return q, sa
 
 
 def quant_act_ue8m0(x_bf16: np.ndarray):

@@ -278,6 +278,36 @@ void oracle_gemm_rows(const uint8_t *xq, const float *xs, const uint8_t *wq, con
 }
 
 /* Threads OpenMP will use for the GEMM (reported with CPU timings). */
+/* ------------------------------------- per-tensor and static act scales -- */
+
+/*
+ * Per-tensor activation scales ("Deployer la parcimonie 2:4 avec FP8 sur
+ * Hopper", pipeline step 3 and "Bonnes pratiques": dynamic per-tensor FP8
+ * scaling) and static scales ("FP8 a granularite fine", section "Chemin rapide
+ * de DeepGEMM": a static activation scheme, the scale fixed beforehand).  Both
+ * quantize every element with one scale s: q = enc(fp32(x / s)), saturating.
+ * The dynamic per-tensor scale is s = fp32(amax / 448) over the whole tensor.
+ * The scale is written to every entry of the [M, K/128] block-scale array, so
+ * that the block-scaled GEMM takes these codes unchanged.
+ */
+void oracle_quant_act_static(const uint16_t *x, int64_t M, int64_t K, float s_in, uint8_t *q, float *s) {
+    int64_t KB = K / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t k = 0; k < K; k++) q[m * K + k] = quantize_one(bf16_to_f32(x[m * K + k]), s_in);
+        for (int64_t kb = 0; kb < KB; kb++) s[m * KB + kb] = s_in;
+    }
+}
+
+void oracle_quant_act_tensor(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < M * K; i++) {
+        float a = fabsf(bf16_to_f32(x[i]));
+        if (a > amax) amax = a;
+    }
+    oracle_quant_act_static(x, M, K, amax / 448.0f, q, s);
+}
+
 /* ------------------------------------------------------ UE8M0 scales ---- */
 
 /*

@@ -615,3 +615,34 @@ def test_grouped_gemm_oracle_routes_rows_to_their_expert():
     assert np.array_equal(perm[23:], oracle.gemm(xq[23:], xs[23:], wq[0], ws[0]))
     rows = np.array([39, 0, 16, 17])
     assert np.array_equal(oracle.grouped_gemm(xq, xs, wq, ws, offsets, rows=rows), y[rows])
+
+
+# ------------------------------------------ per-tensor and static scales ---
+
+def test_quant_act_tensor_and_static_against_exact_arithmetic():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((6, 384)).astype(np.float32)
+    x[2, 5] = 37.0                                              # the tensor's amax
+    xb = si.to_bf16_bits(torch.from_numpy(x))
+    q, s = oracle.quant_act_tensor(xb)
+    vals = si.bf16_bits_to_f32(xb)
+    s_ref, codes = quantize_exact([float(v) for v in vals.ravel()], amax=float(np.abs(vals).max()))
+    assert np.all(s == np.float32(s_ref)) and s.shape == (6, 3)
+    assert np.array_equal(q.ravel(), np.array(codes, np.uint8))
+    # static with that scale gives the same; a smaller static scale saturates the large values
+    qs, ss = oracle.quant_act_static(xb, s_ref)
+    assert np.array_equal(qs, q) and np.all(ss == np.float32(s_ref))
+    q2, _ = oracle.quant_act_static(xb, s_ref / 4)
+    assert q2[2, 5] == 0x7E and np.all(np.abs(q2.astype(np.int16) & 0x7F) <= 0x7E)
+    _, codes2 = quantize_exact([float(v) for v in vals.ravel()], amax=float(np.abs(vals).max()) / 4)
+    assert np.array_equal(q2.ravel(), np.array(codes2, np.uint8))
+
+
+def test_quant_act_tensor_equals_block_scaling_when_every_group_shares_the_amax():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    x[:, ::128] = 9.0                                          # every 1x128 group has amax 9
+    xb = si.to_bf16_bits(torch.from_numpy(x))
+    qt, st = oracle.quant_act_tensor(xb)
+    qb, sb = oracle.quant_act(xb)
+    assert np.array_equal(qt, qb) and np.array_equal(st, sb)
