@@ -83,6 +83,40 @@ fp8l_status fp8_quant_weight_block(const uint16_t *w, int64_t N, int64_t K,
                                    uint8_t *q, float *s, hipStream_t stream);
 
 /*
+ * One scale for the whole tensor, in the block-scale layout: every entry of
+ * the scale array holds the same fp32 s, so fp8_block_gemm and
+ * fp8_sparse24_gemm take these codes and scales unchanged.
+ *
+ * fp8_quant_act_tensor: dynamic per-tensor scaling ("Deployer la parcimonie
+ * 2:4 avec FP8 sur Hopper": pipeline step 3 and "Bonnes pratiques", FP8 with
+ * a scale computed per tensor at run time).  s = fp32(amax / 448), amax the
+ * largest |x| of the whole [M,K] tensor.  Three launches on the stream; s[0]
+ * holds partial maxima between them, so s must not be read before the call's
+ * work on the stream is done.
+ *
+ * fp8_quant_act_static: static activation scaling ("FP8 a granularite fine",
+ * section "Chemin rapide de DeepGEMM": the static activation scheme, a scale
+ * fixed ahead of time).  scale points to one fp32 in device memory (4-byte
+ * aligned, not overlapping q or s), read by the kernel: 0 < *scale < inf is
+ * the caller's contract; values beyond 448 * scale saturate to +-448.
+ *
+ * fp8_quant_weight_tensor: dynamic per-tensor weight scaling (the same
+ * passage of "Deployer la parcimonie 2:4 avec FP8 sur Hopper"), s over all of
+ * W [N,K] written to each of the [N/128,K/128] block scales.
+ *
+ *   x [M,K] bf16 / w [N,K] bf16
+ *   q [M,K] / [N,K] e4m3      q = enc(fp32(x / s)), RNE, saturating at +-448
+ *   s [M,K/128] / [N/128,K/128] fp32, every entry = s; amax == 0 gives s = 0
+ *                             and signed-zero codes
+ */
+fp8l_status fp8_quant_act_tensor(const uint16_t *x, int64_t M, int64_t K,
+                                 uint8_t *q, float *s, hipStream_t stream);
+fp8l_status fp8_quant_act_static(const uint16_t *x, const float *scale, int64_t M, int64_t K,
+                                 uint8_t *q, float *s, hipStream_t stream);
+fp8l_status fp8_quant_weight_tensor(const uint16_t *w, int64_t N, int64_t K,
+                                    uint8_t *q, float *s, hipStream_t stream);
+
+/*
  * 2:4 pruning along K, post-prune block scales and compression ("Deployer la
  * parcimonie 2:4 avec FP8 sur Hopper": pipeline step 2, groups of 4
  * contiguous values along K; step 4, magnitude or activation-aware scores,

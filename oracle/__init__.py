@@ -252,6 +252,17 @@ def quant_act_tensor(x_bf16: np.ndarray):
     return q, sa
 
 
+def quant_weight_tensor(w_bf16: np.ndarray):
+    """Per-tensor dynamic weight scaling: the amax / 448 of all of W [N,K] and the codes of every
+    element with it (the element-wise formula of ``quant_act_tensor`` on the flattened tensor),
+    the scale broadcast to the [N/128,K/128] block-scale layout."""
+    N, K = w_bf16.shape
+    if N % GROUP:
+        raise ValueError("N must be a multiple of 128")
+    q, s = quant_act_tensor(w_bf16)
+    return q, np.full((N // GROUP, K // GROUP), s.flat[0], np.float32)
+
+
 def quant_act_ue8m0(x_bf16: np.ndarray):
     """x [M,K] bf16 bits -> (codes [M,K] uint8, UE8M0 exponents [M,K/128] uint8); scale = 2^(e-127)."""
     _check_bf16(x_bf16, "x")

@@ -29,7 +29,8 @@ FP8L_ERR_LAUNCH = 6
 
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
            "fp8_sparse24_gemm", "fp8_quant_act_ue8m0", "fp8_quant_weight_block_ue8m0", "fp8_block_gemm_ue8m0",
-           "fp8_grouped_gemm", "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear", "fp8lin_status_str")
+           "fp8_grouped_gemm", "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear",
+           "fp8_quant_act_tensor", "fp8_quant_act_static", "fp8_quant_weight_tensor", "fp8lin_status_str")
 MAX_LINEAR_M = 64  # the fused-quantization calls take decode-sized batches
 
 _lock = threading.Lock()
@@ -58,6 +59,9 @@ def load_library():
         sig = {
             "fp8_quant_act": [P, I, I, P, P, P],
             "fp8_quant_weight_block": [P, I, I, P, P, P],
+            "fp8_quant_act_tensor": [P, I, I, P, P, P],
+            "fp8_quant_act_static": [P, P, I, I, P, P, P],
+            "fp8_quant_weight_tensor": [P, I, I, P, P, P],
             "prune24_compress": [P, P, I, I, P, P, P, P],
             "fp8_block_gemm": [P, P, P, P, I, I, I, P, P],
             "fp8_sparse24_gemm": [P, P, P, P, P, I, I, I, P, P],
@@ -130,6 +134,42 @@ def fp8_quant_act(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tenso
     q = _out(q, "q", (M, K), torch.uint8, x)
     s = _out(s, "s", (M, K // GROUP), torch.float32, x)
     _check("fp8_quant_act", load_library().fp8_quant_act(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)))
+    return q, s
+
+
+def fp8_quant_act_tensor(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+    """x [M,K] bf16 -> (q [M,K] codes, s [M,K/128] fp32, every entry the per-tensor amax / 448)."""
+    _want(x, "x", torch.bfloat16)
+    M, K = x.shape
+    q = _out(q, "q", (M, K), torch.uint8, x)
+    s = _out(s, "s", (M, K // GROUP), torch.float32, x)
+    _check("fp8_quant_act_tensor", load_library().fp8_quant_act_tensor(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)))
+    return q, s
+
+
+def fp8_quant_act_static(x: torch.Tensor, scale: torch.Tensor, q: torch.Tensor | None = None,
+                         s: torch.Tensor | None = None):
+    """x [M,K] bf16, scale: one fp32 on the device -> (q [M,K] codes, s [M,K/128] fp32 = scale)."""
+    _want(x, "x", torch.bfloat16)
+    _want(scale, "scale", torch.float32)
+    if scale.numel() != 1 or scale.device != x.device:
+        raise ValueError("scale must be one fp32 value on the device of x")
+    M, K = x.shape
+    q = _out(q, "q", (M, K), torch.uint8, x)
+    s = _out(s, "s", (M, K // GROUP), torch.float32, x)
+    _check("fp8_quant_act_static",
+           load_library().fp8_quant_act_static(_ptr(x), _ptr(scale), M, K, _ptr(q), _ptr(s), _stream(x)))
+    return q, s
+
+
+def fp8_quant_weight_tensor(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+    """w [N,K] bf16 -> (q [N,K] codes, s [N/128,K/128] fp32, every entry the per-tensor amax / 448)."""
+    _want(w, "w", torch.bfloat16)
+    N, K = w.shape
+    q = _out(q, "q", (N, K), torch.uint8, w)
+    s = _out(s, "s", (N // GROUP, K // GROUP), torch.float32, w)
+    _check("fp8_quant_weight_tensor",
+           load_library().fp8_quant_weight_tensor(_ptr(w), N, K, _ptr(q), _ptr(s), _stream(w)))
     return q, s
 
 

@@ -94,6 +94,44 @@ fp8l_status fp8_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, f
   return launched(fp8lin::launch_quant_act(x, M, K, q, s, stream));
 }
 
+fp8l_status fp8_quant_act_tensor(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s,
+                                 hipStream_t stream) {
+  if (bad_mk(M, K)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!x || !q || !s) return FP8L_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{x, M * K * 2}};
+  const Range outs[] = {{q, M * K}, {s, M * (K / 128) * 4}};
+  if (any_alias(outs, 2, ins, 1)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_quant_tensor(x, M * K, q, s, M * (K / 128), stream));
+}
+
+fp8l_status fp8_quant_act_static(const uint16_t *x, const float *scale, int64_t M, int64_t K, uint8_t *q, float *s,
+                                 hipStream_t stream) {
+  if (bad_mk(M, K)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!x || !scale || !q || !s) return FP8L_ERR_NULL;
+  if (!aligned16(x) || ((uintptr_t)scale & 3u) || !aligned16(q) || !aligned16(s)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{x, M * K * 2}, {scale, 4}};
+  const Range outs[] = {{q, M * K}, {s, M * (K / 128) * 4}};
+  if (any_alias(outs, 2, ins, 2)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_quant_static(x, scale, M * K, q, s, M * (K / 128), stream));
+}
+
+fp8l_status fp8_quant_weight_tensor(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
+                                    hipStream_t stream) {
+  if (bad_nk(N, K)) return FP8L_ERR_SHAPE;
+  if (!w || !q || !s) return FP8L_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{w, N * K * 2}};
+  const Range outs[] = {{q, N * K}, {s, (N / 128) * (K / 128) * 4}};
+  if (any_alias(outs, 2, ins, 1)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_quant_tensor(w, N * K, q, s, (N / 128) * (K / 128), stream));
+}
+
 fp8l_status fp8_quant_weight_block(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
                                    hipStream_t stream) {
   if (bad_nk(N, K)) return FP8L_ERR_SHAPE;

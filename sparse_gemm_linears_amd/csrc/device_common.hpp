@@ -97,22 +97,11 @@ __device__ __forceinline__ uint32_t quantize4_pow2(const float (&x)[4], float in
 // |bf16| as an integer: ordering of non-NaN magnitudes is the integer ordering.
 __device__ __forceinline__ uint32_t bf16_abs_bits(uint32_t b16) { return b16 & 0x7FFFu; }
 
-// One 1x128 activation group held by 16 consecutive lanes, 8 bf16 values
-// (16 bytes) per lane: returns this lane's 8 codes and the group scale.  The
-// group amax is an integer max over |bf16| bit patterns, shuffled across the
-// 16 lanes (all 16 must be active); s = amax / 448 as an IEEE division; codes
-// by the fast quotient with the exact-division fallback.
-__device__ __forceinline__ uint2 quantize_group16(const uint4 &raw, float &s_out) {
+// Codes of the 8 bf16 values packed in raw with one scale sc: the fast path,
+// and the exact divisions when some value needs them or sc is out of the fast
+// range.
+__device__ __forceinline__ uint2 quantize8_scaled(const uint4 &raw, float sc) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t amax_bits = 0;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    amax_bits = max(amax_bits, bf16_abs_bits(w[i] & 0xFFFFu));
-    amax_bits = max(amax_bits, bf16_abs_bits(w[i] >> 16));
-  }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 16));
-  const float sc = bf16_to_f32(amax_bits) / 448.0f;
   const float rs = __builtin_amdgcn_rcpf(sc);
   float v[2][4];
 #pragma unroll
@@ -130,8 +119,30 @@ __device__ __forceinline__ uint2 quantize_group16(const uint4 &raw, float &s_out
 #pragma unroll
     for (int i = 0; i < 2; i++) packed[i] = quantize4_exact(v[i], sc);
   }
-  s_out = sc;
   return make_uint2(packed[0], packed[1]);
+}
+
+// Largest |x| of the 8 bf16 values packed in raw, as bf16 magnitude bits.
+__device__ __forceinline__ uint32_t amax8_bits(const uint4 &raw) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t a = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) a = max(a, max(bf16_abs_bits(w[i] & 0xFFFFu), bf16_abs_bits(w[i] >> 16)));
+  return a;
+}
+
+// One 1x128 activation group held by 16 consecutive lanes, 8 bf16 values
+// (16 bytes) per lane: returns this lane's 8 codes and the group scale.  The
+// group amax is an integer max over |bf16| bit patterns, shuffled across the
+// 16 lanes (all 16 must be active); s = amax / 448 as an IEEE division; codes
+// by the fast quotient with the exact-division fallback.
+__device__ __forceinline__ uint2 quantize_group16(const uint4 &raw, float &s_out) {
+  uint32_t amax_bits = amax8_bits(raw);
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 16));
+  const float sc = bf16_to_f32(amax_bits) / 448.0f;
+  s_out = sc;
+  return quantize8_scaled(raw, sc);
 }
 
 // v_mfma_f32_16x16x128_f8f6f4 with both operands e4m3 and no block scale.

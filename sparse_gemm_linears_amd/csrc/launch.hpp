@@ -9,6 +9,13 @@ namespace fp8lin {
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, hipStream_t stream);
 hipError_t launch_quant_wblock(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, hipStream_t stream);
+// One scale for a whole tensor of n bf16 values (n a multiple of 8), written
+// to all n_s entries of s (n_s >= 1): the dynamic per-tensor amax / 448, or a
+// static scale read from device memory.
+constexpr int64_t kTensorAmaxParts = 1024;
+hipError_t launch_quant_tensor(const uint16_t *x, int64_t n, uint8_t *q, float *s, int64_t n_s, hipStream_t stream);
+hipError_t launch_quant_static(const uint16_t *x, const float *scale, int64_t n, uint8_t *q, float *s, int64_t n_s,
+                               hipStream_t stream);
 // UE8M0 (power-of-two) scale variants: one exponent byte per group / block.
 hipError_t launch_quant_act_ue8m0(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, uint8_t *e, hipStream_t stream);
 hipError_t launch_quant_wblock_ue8m0(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, uint8_t *e,

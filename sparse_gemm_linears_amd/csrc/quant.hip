@@ -159,6 +159,87 @@ __global__ __launch_bounds__(256) void quant_wblock_ue8m0_kernel(const uint16_t*
   }
 }
 
+// ---------------------------------------------------------------------------
+// One scale for a whole tensor (dynamic per-tensor, or static): codes of the
+// flattened tensor in 8-element chunks (16 bytes of bf16 per thread), and the
+// scale written to every entry of the block-scale array, so the block-scaled
+// GEMM takes the result unchanged.  The dynamic scale needs the amax of the
+// whole tensor before any code: partial maxima per block are parked in the
+// scale array itself (as bf16 magnitude bits), one block folds them into
+// s[0] = amax / 448, and the quantizer reads its scale from s[0] and fills the
+// rest of the array.  Three ordered launches on the stream; no atomics, no
+// buffer beyond the outputs, and the result does not depend on the grid.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void amax_partial_kernel(const uint16_t* __restrict__ x, int64_t n_chunks,
+                                                           uint32_t* __restrict__ part) {
+  __shared__ uint32_t wave_max[4];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t a = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n_chunks; i += 4 * stride) {
+    uint4 r[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) r[u] = *reinterpret_cast<const uint4*>(x + (i + u * stride) * 8);
+#pragma unroll
+    for (int u = 0; u < 4; u++) a = max(a, amax8_bits(r[u]));
+  }
+  for (; i < n_chunks; i += stride) a = max(a, amax8_bits(*reinterpret_cast<const uint4*>(x + i * 8)));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off, 64));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+}
+
+// One block: s[0] <- fp32(amax / 448) from the n_part partial maxima held as
+// bits in s[0 .. n_part).  Every read is done before the barrier, the single
+// write after it.
+__global__ __launch_bounds__(256) void amax_finish_kernel(float* s, int n_part) {
+  __shared__ uint32_t wave_max[4];
+  const uint32_t* part = reinterpret_cast<const uint32_t*>(s);
+  uint32_t a = 0;
+  for (int i = threadIdx.x; i < n_part; i += 256) a = max(a, part[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off, 64));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s[0] = bf16_to_f32(max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]))) / 448.0f;
+}
+
+// Codes of chunk i with the scale *scale; thread i also writes s[i] for
+// s_from <= i < n_s (the grid has at least n_s threads).  scale may point
+// into s when s_from excludes that entry.
+__global__ __launch_bounds__(256) void quant_scaled_kernel(const uint16_t* __restrict__ x, const float* scale,
+                                                           int64_t n_chunks, uint8_t* __restrict__ q, float* s,
+                                                           int64_t n_s, int64_t s_from) {
+  const float sc = *scale;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n_chunks)
+    *reinterpret_cast<uint2*>(q + i * 8) = quantize8_scaled(*reinterpret_cast<const uint4*>(x + i * 8), sc);
+  if (i >= s_from && i < n_s) s[i] = sc;
+}
+
+hipError_t launch_quant_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s, int64_t n_s,
+                               hipStream_t stream) {
+  const int64_t n_chunks = n / 8;
+  const int n_part = (int)(n_s < kTensorAmaxParts ? n_s : kTensorAmaxParts);
+  hipLaunchKernelGGL(amax_partial_kernel, dim3((unsigned)n_part), dim3(256), 0, stream, x, n_chunks,
+                     reinterpret_cast<uint32_t*>(s));
+  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(256), 0, stream, s, n_part);
+  hipLaunchKernelGGL(quant_scaled_kernel, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, stream, x,
+                     (const float*)s, n_chunks, q, s, n_s, (int64_t)1);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_static(const uint16_t* x, const float* scale, int64_t n, uint8_t* q, float* s, int64_t n_s,
+                               hipStream_t stream) {
+  const int64_t n_chunks = n / 8;
+  hipLaunchKernelGGL(quant_scaled_kernel, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, stream, x, scale,
+                     n_chunks, q, s, n_s, (int64_t)0);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act_ue8m0(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* e,
                                   hipStream_t stream) {
   const int64_t n_groups = M * (K / kGroup);

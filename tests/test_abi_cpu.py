@@ -84,6 +84,27 @@ def test_weight_quant_validation(lib):
     assert lib.fp8_quant_weight_block(P(A), 128, 128, P(A), P(C), None) == sgl.FP8L_ERR_ALIAS
 
 
+def test_tensor_scale_quant_validation(lib):
+    t = lib.fp8_quant_act_tensor
+    assert t(P(A), 4, 100, P(B), P(C), None) == sgl.FP8L_ERR_SHAPE
+    assert t(P(A), 4, 128, None, P(C), None) == sgl.FP8L_ERR_NULL
+    assert t(P(A), 4, 128, P(B), P(C + 8), None) == sgl.FP8L_ERR_ALIGN
+    assert t(P(A), 4, 128, P(B), P(A + 16), None) == sgl.FP8L_ERR_ALIAS
+    assert t(None, 0, 128, None, None, None) == sgl.FP8L_OK
+    st = lib.fp8_quant_act_static
+    assert st(P(A), P(D), 4, 100, P(B), P(C), None) == sgl.FP8L_ERR_SHAPE
+    assert st(P(A), None, 4, 128, P(B), P(C), None) == sgl.FP8L_ERR_NULL
+    assert st(P(A), P(D + 2), 4, 128, P(B), P(C), None) == sgl.FP8L_ERR_ALIGN
+    assert st(P(A), P(C + 4), 4, 128, P(B), P(C), None) == sgl.FP8L_ERR_ALIAS     # scale inside s
+    assert st(P(A), P(B + 12), 4, 128, P(B), P(C), None) == sgl.FP8L_ERR_ALIAS    # scale inside q
+    assert st(None, None, 0, 128, None, None, None) == sgl.FP8L_OK
+    w = lib.fp8_quant_weight_tensor
+    assert w(P(A), 100, 128, P(B), P(C), None) == sgl.FP8L_ERR_SHAPE
+    assert w(P(A), 128, 128, P(B), None, None) == sgl.FP8L_ERR_NULL
+    assert w(P(A), 128, 128, P(B + 4), P(C), None) == sgl.FP8L_ERR_ALIGN
+    assert w(P(A), 128, 128, P(B), P(B + 64), None) == sgl.FP8L_ERR_ALIAS
+
+
 def test_prune_validation(lib):
     f = lib.prune24_compress
     assert f(P(A), None, 128, 130, P(B), P(C), P(D), None) == sgl.FP8L_ERR_SHAPE

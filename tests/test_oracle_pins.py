@@ -646,3 +646,16 @@ def test_quant_act_tensor_equals_block_scaling_when_every_group_shares_the_amax(
     qt, st = oracle.quant_act_tensor(xb)
     qb, sb = oracle.quant_act(xb)
     assert np.array_equal(qt, qb) and np.array_equal(st, sb)
+
+
+def test_quant_weight_tensor_equals_block_scaling_when_every_block_shares_the_amax():
+    rng = np.random.default_rng(16)
+    w = (0.02 * rng.standard_normal((256, 384))).astype(np.float32)
+    w[::128, ::128] = -0.75                                    # every 128x128 block has amax 0.75
+    wb = si.to_bf16_bits(torch.from_numpy(w))
+    qt, st = oracle.quant_weight_tensor(wb)
+    qb, sb = oracle.quant_wblock(wb)
+    assert st.shape == (2, 3) and np.array_equal(qt, qb) and np.array_equal(st, sb)
+    w[7, 300] = 3.0                                            # one block now holds the tensor amax
+    qt2, st2 = oracle.quant_weight_tensor(si.to_bf16_bits(torch.from_numpy(w)))
+    assert np.all(st2 == np.float32(3.0) / np.float32(448.0)) and qt2[7, 300] == 0x7E
