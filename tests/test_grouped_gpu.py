@@ -62,3 +62,19 @@ def test_grouped_gemm_single_group_and_empty(gpu_lib):
     off = np.array([0, 0, M], np.int32)        # all tokens to expert 1
     y = gpu_lib.fp8_grouped_gemm(dev(xq), dev(xs), dev(wq), dev(ws), dev(off))
     assert_gemm_close(y, oracle.gemm(xq, xs, wq[1], ws[1]), "one non-empty group")
+
+
+def test_grouped_gemm_few_tokens_and_empty_batch(gpu_lib):
+    """Decode-sized routing (a handful of tokens over several experts, some empty)
+    and an empty batch."""
+    K, N = 1024, 512
+    wq, ws = expert_weights(4, N, K, seed=11)
+    M = 5
+    xq, xs = oracle.quant_act(si.activations(M, K))
+    off = np.array([0, 2, 2, 5, 5], np.int32)
+    y = gpu_lib.fp8_grouped_gemm(dev(xq), dev(xs), dev(wq), dev(ws), dev(off))
+    assert_gemm_close(y, oracle.grouped_gemm(xq, xs, wq, ws, off), "five tokens over four experts")
+    xq0 = np.zeros((0, K), np.uint8)
+    xs0 = np.zeros((0, K // 128), np.float32)
+    y0 = gpu_lib.fp8_grouped_gemm(dev(xq0), dev(xs0), dev(wq), dev(ws), dev(np.zeros(5, np.int32)))
+    assert tuple(y0.shape) == (0, N)
