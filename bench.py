@@ -264,21 +264,30 @@ def time_calls(torch, f, reps):
 
 def bench_ue8m0(sgl, si, torch, np, dev, bf16, steps):
     """UE8M0 (power-of-two) scales on the four Llama-3-8B shapes at M=4096: the two
-    quantizers and the GEMM whose scales the MFMA applies."""
+    quantizers, and the GEMM whose scales the MFMA applies timed in alternating
+    batches with the fp32-scale GEMM of the same shape (clock drift between
+    separate runs is larger than the difference between the two)."""
     M = si.PREFILL_M
     res = {}
     for name, K, N in si.LLAMA3_8B:
         x, w = bf16(si.activations(M, K)), bf16(si.weights(N, K))
         xq, xe = sgl.fp8_quant_act_ue8m0(x)
         wq, we = sgl.fp8_quant_weight_block_ue8m0(w)
+        xq4, xs4 = sgl.fp8_quant_act(x)
+        wq4, ws4 = sgl.fp8_quant_weight_block(w)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         t_qa = time_calls(torch, lambda: sgl.fp8_quant_act_ue8m0(x, xq, xe), steps)
         t_qw = time_calls(torch, lambda: sgl.fp8_quant_weight_block_ue8m0(w, wq, we), steps)
-        t_g = time_calls(torch, lambda: sgl.fp8_block_gemm_ue8m0(xq, xe, wq, we, y), steps)
+        t_e8, t_f32 = [], []
+        for _ in range(3):
+            t_f32.append(time_calls(torch, lambda: sgl.fp8_block_gemm(xq4, xs4, wq4, ws4, y), steps))
+            t_e8.append(time_calls(torch, lambda: sgl.fp8_block_gemm_ue8m0(xq, xe, wq, we, y), steps))
+        t_g, t_f = sorted(t_e8)[1], sorted(t_f32)[1]
         tf = 2 * M * N * K / t_g / 1e6
         res[name] = {"quant_act_us": round(t_qa, 2), "quant_wblock_us": round(t_qw, 2), "gemm_us": round(t_g, 2),
-                     "gemm_tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
-        del x, w, xq, xe, wq, we, y
+                     "gemm_tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "fp32_scale_gemm_us": round(t_f, 2)}
+        del x, w, xq, xe, wq, we, xq4, xs4, wq4, ws4, y
     torch.cuda.empty_cache()
     return res
 

@@ -7,11 +7,15 @@
  * no infinities, 0x7F/0xFF = NaN, largest finite 448), view-compatible with
  * torch.float8_e4m3fn.  Scales are fp32.  G = 128 is the group / block edge.
  *
- * Ownership: the caller allocates every input and output; the library never
- * allocates, frees or keeps a pointer after a call returns, keeps no state
- * between calls besides a per-device architecture check, and needs no
- * workspace.  Calls may be made from several host threads on different
- * streams.
+ * Ownership: the caller allocates every input and output; the library keeps
+ * no pointer after a call returns and no state between calls besides
+ * per-device architecture and compute-unit counts.  One call allocates:
+ * fp8_block_gemm with M > 64 and too few 256-wide output tiles to cover half
+ * of the compute units splits K, and takes an fp32 workspace of at most 256
+ * tiles' worth (S * M * N * 4 bytes, S <= 16) from the device's stream-ordered
+ * memory pool (hipMallocAsync on `stream`), releasing it on the same stream
+ * (hipFreeAsync) after the kernels that use it.  Calls may be made from
+ * several host threads on different streams.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (NULL = the default stream) and returns without
@@ -27,7 +31,9 @@
  *   FP8L_ERR_ALIGN   a pointer is not 16-byte aligned;
  *   FP8L_ERR_ALIAS   an output overlaps an input or another output;
  *   FP8L_ERR_DEVICE  the current HIP device is missing or is not gfx950;
- *   FP8L_ERR_LAUNCH  the kernel launch was rejected by the runtime.
+ *   FP8L_ERR_LAUNCH  the kernel launch was rejected by the runtime;
+ *   FP8L_ERR_MEMORY  the split-K workspace could not be allocated (no kernel
+ *                    runs).
  * M == 0 (an empty batch) returns FP8L_OK without launching and without
  * looking at the M-sized buffers.  There is no fallback path: an unsupported
  * case is an error, never a silently slower kernel.
@@ -50,7 +56,8 @@ enum {
     FP8L_ERR_ALIGN = 3,
     FP8L_ERR_ALIAS = 4,
     FP8L_ERR_DEVICE = 5,
-    FP8L_ERR_LAUNCH = 6
+    FP8L_ERR_LAUNCH = 6,
+    FP8L_ERR_MEMORY = 7
 };
 
 /*
@@ -150,7 +157,10 @@ fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N
  *   wq [N,K] e4m3, ws [N/128,K/128] fp32   from fp8_quant_weight_block
  *   y [M,N] bf16   y[m,n] = bf16_rne( sum_kb xs[m,kb] * ws[n/128,kb] *
  *                                     sum_{k in kb} dec(xq[m,k]) * dec(wq[n,k]) )
- * The inner block sums are exact FP8 products accumulated in fp32.
+ * The inner block sums are exact FP8 products accumulated in fp32.  With
+ * M > 64 and few output tiles the K blocks are summed in up to 16 fp32
+ * partials (each in K order) that are then added in a fixed order, which
+ * changes only the fp32 rounding order; results are deterministic either way.
  */
 fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
                            int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);

@@ -5,7 +5,7 @@ Python face of the C-ABI library ``libfp8lin.so`` (declared in
 names.  torch supplies device memory and the stream; the arithmetic runs in
 the library's HIP kernels.
 """
-from ._binding import (EXPORTS, FP8L_ERR_ALIAS, FP8L_ERR_ALIGN, FP8L_ERR_DEVICE, FP8L_ERR_LAUNCH,
+from ._binding import (EXPORTS, FP8L_ERR_ALIAS, FP8L_ERR_ALIGN, FP8L_ERR_DEVICE, FP8L_ERR_LAUNCH, FP8L_ERR_MEMORY,
                        FP8L_ERR_NULL, FP8L_ERR_SHAPE, FP8L_OK, GROUP, LIB_PATH, MAX_LINEAR_M, Fp8LinError,
                        fp8_block_gemm, fp8_block_gemm_swiglu, fp8_block_gemm_ue8m0, fp8_block_linear,
                        fp8_grouped_gemm,
@@ -20,5 +20,5 @@ __all__ = [
     "fp8_quant_act_static", "fp8_quant_weight_tensor", "MAX_LINEAR_M", "load_library", "status_str", "Fp8LinError",
     "EXPORTS", "GROUP", "LIB_PATH",
     "FP8L_OK", "FP8L_ERR_NULL", "FP8L_ERR_SHAPE", "FP8L_ERR_ALIGN", "FP8L_ERR_ALIAS", "FP8L_ERR_DEVICE",
-    "FP8L_ERR_LAUNCH",
+    "FP8L_ERR_LAUNCH", "FP8L_ERR_MEMORY",
 ]

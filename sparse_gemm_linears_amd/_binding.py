@@ -26,6 +26,7 @@ FP8L_ERR_ALIGN = 3
 FP8L_ERR_ALIAS = 4
 FP8L_ERR_DEVICE = 5
 FP8L_ERR_LAUNCH = 6
+FP8L_ERR_MEMORY = 7
 
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
            "fp8_sparse24_gemm", "fp8_quant_act_ue8m0", "fp8_quant_weight_block_ue8m0", "fp8_block_gemm_ue8m0",

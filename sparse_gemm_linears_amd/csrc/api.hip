@@ -73,7 +73,7 @@ constexpr int64_t kMaxGroups = 4096;   // experts of one grouped GEMM
 fp8l_status launched(hipError_t e) {
   if (e != hipSuccess) {
     (void)hipGetLastError();
-    return FP8L_ERR_LAUNCH;
+    return e == hipErrorOutOfMemory ? FP8L_ERR_MEMORY : FP8L_ERR_LAUNCH;
   }
   return FP8L_OK;
 }
@@ -297,6 +297,7 @@ const char *fp8lin_status_str(fp8l_status status) {
     case FP8L_ERR_ALIAS: return "an output overlaps an input or another output";
     case FP8L_ERR_DEVICE: return "no gfx950 (MI355X) device is current";
     case FP8L_ERR_LAUNCH: return "kernel launch failed";
+    case FP8L_ERR_MEMORY: return "the split-K workspace could not be allocated";
     default: return "unknown status";
   }
 }

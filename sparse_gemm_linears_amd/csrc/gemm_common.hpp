@@ -227,6 +227,22 @@ __device__ __forceinline__ void store_token_tile(uint8_t *scratch, const v4f (&a
   }
 }
 
+// fp32 partial tile of token tile c straight from registers: lane (token
+// l%16, rows 4*(l/16) + 16*r .. +3) stores 16 contiguous bytes per row tile,
+// four lanes making 64 contiguous bytes of a token's row.  The partials are
+// read back by the split-K reduction, so they go through the caches normally.
+template <int RT>
+__device__ __forceinline__ void store_token_tile_f32(const v4f (&acc_c)[RT], float *out, int M, int N, int m0, int n0,
+                                                     int lane) {
+  const int m = m0 + (lane & 15), g = lane >> 4;
+  if (m >= M) return;
+#pragma unroll
+  for (int r = 0; r < RT; r++) {
+    const int n = n0 + 16 * r + 4 * g;
+    if (n < N) *reinterpret_cast<v4f *>(out + (int64_t)m * N + n) = acc_c[r];
+  }
+}
+
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin (block b runs on
 // XCD b % 8), each XCD with its own L2.  The remap gives every XCD one
 // contiguous range of logical tile ids; the logical order then walks groups of

@@ -13,6 +13,8 @@
 //    coalesced bf16 stores through LDS at the end;
 //  * decode kernel (M <= 64): the weight streams from HBM straight into MFMA
 //    registers, the waves of a workgroup split K and meet in LDS at the end.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -31,7 +33,7 @@ struct DenseTile {
   static constexpr int kACopies = BN / 8 / kWaves, kBCopies = BM / 8 / kWaves;  // 1 KB = 8 rows per copy
   static constexpr int kATile = BN * 128, kBTile = BM * 128;
   static constexpr int kWavesPerSlice = WM;  // waves sharing a weight slice (one per token slice)
-  static_assert(BN == 256 && BM == 256, "panels are addressed as two 128-row halves");
+  static_assert(BN == 256 && (BM == 256 || BM == 128), "panels are addressed as 128-row halves");
   static_assert(128 % (8 * kWaves) == 0, "copy slabs tile the 128-row halves");
   static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
   static_assert(kWaveN == 128, "a wave covers one 128-row weight scale block (and 256-byte epilogue rows)");
@@ -44,12 +46,16 @@ struct DenseTile {
 //  per-token 1x128 e4m3 codes hq [M,I] and scales hs [M,I/128] as well.
 //  Grouped GEMM: G expert weights [G][N][K] (scales [G][N/128][K/128]); the
 //  tokens of expert g are rows offsets[g] .. offsets[g+1] - 1 of X and Y.
+//  Split K: workgroup (tile, s) covers K blocks [s * kb_split, +kb_split) and
+//  writes its fp32 partial tile to part + s * M * N ([M][N]).
 struct TileExtra {
   uint8_t *hq;
   float *hs;
   int I;
   const int32_t *offsets;
   int G;
+  float *part;
+  int kb_split;
 };
 
 // SwiGLU epilogue.  The two waves with the same token slice hold the gate
@@ -143,7 +149,10 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *x
 // GROUPED: tiles_m counts token tiles over all groups (an upper bound: the
 // sum of ceil(rows_g / BM) <= ceil(M / BM) + G); a workgroup whose tile lies
 // past the last group's returns at once.
-template <int BN, int BM, int WN, int WM, int SB, int CR, bool SWIGLU, bool E8 = false, bool GROUPED = false>
+// PARTIAL: split K over blockIdx.y (so.kb_split K blocks each, a multiple of
+// SB) and store unrounded fp32 partial tiles instead of y.
+template <int BN, int BM, int WN, int WM, int SB, int CR, bool SWIGLU, bool E8 = false, bool GROUPED = false,
+          bool PARTIAL = false>
 __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
     const uint8_t *__restrict__ xq, const std::conditional_t<E8, uint8_t, float> *__restrict__ xs,
     const uint8_t *__restrict__ wq_all, const std::conditional_t<E8, uint8_t, float> *__restrict__ ws_all,
@@ -159,7 +168,14 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
   const int cj = lane >> 3, cp = lane & 7;  // copy lane -> (row in an 8-row slab, chunk position)
-  const int KB = K / kGroup, NB = N / kGroup;
+  // KBs: K blocks per row (the stride of the scale rows); KB: K blocks this
+  // workgroup accumulates, starting at block kb0
+  const int KBs = K / kGroup, NB = N / kGroup;
+  int kb0 = 0, KB = KBs;
+  if constexpr (PARTIAL) {
+    kb0 = blockIdx.y * so.kb_split;
+    KB = min(so.kb_split, KBs - kb0);
+  }
 
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -204,12 +220,14 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
   // first weight row of each 128-row panel half
   const int w_half0 = SWIGLU ? 128 * tn : n_base;
   const int w_half1 = SWIGLU ? so.I + 128 * tn : n_base + 128;
-  const uint8_t *xpanel = xq + (int64_t)m_base * K;
-  const rsrc_t rw0 = panel_rows128(wq + (int64_t)w_half0 * K, N - w_half0, 0, K);
-  const rsrc_t rw1 = panel_rows128(wq + (int64_t)w_half1 * K, N - w_half1, 0, K);
+  // (a K range starting at block kb0 shifts every panel row by kb0 * 128
+  // bytes; reads stay below row offset (kb0 + KB) * 128 <= K)
+  const uint8_t *xpanel = xq + (int64_t)m_base * K + kb0 * kGroup;
+  const rsrc_t rw0 = panel_rows128(wq + (int64_t)w_half0 * K + kb0 * kGroup, N - w_half0, 0, K);
+  const rsrc_t rw1 = panel_rows128(wq + (int64_t)w_half1 * K + kb0 * kGroup, N - w_half1, 0, K);
   const rsrc_t rx0 = panel_rows128(xpanel, M - m_base, 0, K), rx1 = panel_rows128(xpanel, M - m_base, 128, K);
   std::conditional_t<E8, TokenExps<BM, SB>, TokenScales<BM, SB>> scales;
-  scales.init(lds_s, xs, M, KB, m_base, tid);
+  scales.init(lds_s, xs + kb0, M, KBs, m_base, tid);
 
   // One 128-wide K block of the weight and token panels into LDS stage `st`.
   auto issue_copy = [&](int kb, int st, int j) {
@@ -240,7 +258,7 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
     for (int c = 0; c < C::CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int nb_wave = min((wn0 == 0 ? w_half0 : w_half1) / kGroup, NB - 1);
-  const auto *ws_row = ws + (int64_t)nb_wave * KB;
+  const auto *ws_row = ws + (int64_t)nb_wave * KBs + kb0;
 
   // Token fragments live in registers one K step ahead: bx[ST] holds this
   // step's, and the next step's are read from LDS during row tiles
@@ -348,7 +366,16 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
 
   // epilogue through a wave-private 4 KB slice of the (now idle) weight stage 0
   uint8_t *scratch = lds_a0 + wave * 4096;
-  if constexpr (!SWIGLU) {
+  if constexpr (PARTIAL) {
+    float *part = so.part + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) {
+      v4f col[C::RT];
+#pragma unroll
+      for (int r = 0; r < C::RT; r++) col[r] = acc[r][c];
+      store_token_tile_f32<C::RT>(col, part, M, N, m_base + wm0 + 16 * c, n_base + wn0, lane);
+    }
+  } else if constexpr (!SWIGLU) {
 #pragma unroll
     for (int c = 0; c < C::CT; c++) {
       v4f col[C::RT];
@@ -381,20 +408,89 @@ struct DenseWeight {
   }
 };
 
+// ===================================================== split-K reduction ==
+
+// y = bf16(sum over s of part[s]), the S partials [S][M*N] added in order s =
+// 0, 1, .. (deterministic); four elements per thread, grid-stride.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int S, int64_t mn,
+                                                            uint16_t *__restrict__ y) {
+  const int64_t n4 = mn / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    v4f acc = *reinterpret_cast<const v4f *>(part + 4 * i);
+    for (int s = 1; s < S; s++) acc += *reinterpret_cast<const v4f *>(part + (int64_t)s * mn + 4 * i);
+    *reinterpret_cast<uint2 *>(y + 4 * i) = pack_bf16x4(acc);
+  }
+}
+
 // ================================================================ dispatch ==
+
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Tile shape and K split of a tile-kernel GEMM.  A 256 x 128 tile costs
+// about 0.62 of a 256 x 256 one (measured on the Llama-3-8B shapes), so it
+// wins where the 256 x 256 grid leaves much of its last wave of workgroups
+// (one per CU) idle.  When even that grid covers at most half of the CUs, K
+// is split over up to 16 workgroups per tile, each with at least four K
+// blocks (a multiple of four when the scales go four at a time); the fp32
+// partials are summed in a second kernel.
+struct TilePlan {
+  int bm, splits, kb_split;
+};
+
+static TilePlan plan_tiles(int M, int N, int K, int cus) {
+  const int tn = (N + 255) / 256;
+  const int t256 = ((M + 255) / 256) * tn, t128 = ((M + 127) / 128) * tn;
+  const double cost256 = (double)((t256 + cus - 1) / cus), cost128 = 0.62 * (double)((t128 + cus - 1) / cus);
+  TilePlan p{cost128 < 0.97 * cost256 ? 128 : 256, 1, K / kGroup};
+  const int tiles = p.bm == 128 ? t128 : t256, kb = K / kGroup;
+  if (2 * tiles <= cus && kb >= 8) {
+    const int step = kb % 4 == 0 ? 4 : 1;
+    int s = std::min(std::min(cus / tiles, kb / 4), 16);
+    if (s > 1) {
+      int per = (kb + s - 1) / s;
+      per = (per + step - 1) / step * step;
+      p.splits = (kb + per - 1) / per;
+      p.kb_split = per;
+    }
+  }
+  return p;
+}
 
 template <int BN, int BM, int WN, int WM>
 static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int M, int N,
-                              int K, uint16_t *y, hipStream_t stream) {
+                              int K, uint16_t *y, int splits, int kb_split, float *part, hipStream_t stream) {
   using C = DenseTile<BN, BM, WN, WM>;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const TileExtra none{nullptr, nullptr, 0, nullptr, 0};
-  if ((K / kGroup) % 4 == 0)
-    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false>), dim3(tiles_m * tiles_n),
-                       dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, none);
-  else
-    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4, false>), dim3(tiles_m * tiles_n),
-                       dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, none);
+  const TileExtra ex{nullptr, nullptr, 0, nullptr, 0, part, kb_split};
+  const dim3 grid(tiles_m * tiles_n, splits);
+  if (splits > 1) {
+    if ((K / kGroup) % 4 == 0)
+      hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false, false, false, true>), grid,
+                         dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
+    else
+      hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4, false, false, false, true>), grid,
+                         dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
+  } else if ((K / kGroup) % 4 == 0) {
+    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false>), grid, dim3(C::kThreads), 0, stream, xq, xs,
+                       wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
+  } else {
+    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4, false>), grid, dim3(C::kThreads), 0, stream, xq, xs,
+                       wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
+  }
   return hipGetLastError();
 }
 
@@ -441,7 +537,27 @@ hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *
                              int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
   if (m <= 64) return launch_dense_decode(QuantTokens{xq, xs, k}, wq, ws, m, n, k, y, stream);
-  return launch_tile<256, 256, 2, 4>(xq, xs, wq, ws, m, n, k, y, stream);
+  const TilePlan p = plan_tiles(m, n, k, device_cu_count());
+  float *part = nullptr;
+  if (p.splits > 1) {
+    const hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&part),
+                                        (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = p.bm == 128
+                     ? launch_tile<256, 128, 2, 4>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
+                     : launch_tile<256, 256, 2, 4>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
+  if (p.splits > 1) {
+    if (e == hipSuccess) {
+      const int64_t mn = (int64_t)m * n;
+      const int64_t blocks = std::min<int64_t>((mn / 4 + 255) / 256, 4096);
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, p.splits, mn, y);
+      e = hipGetLastError();
+    }
+    const hipError_t f = hipFreeAsync(part, stream);
+    if (e == hipSuccess) e = f;
+  }
+  return e;
 }
 
 hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,

@@ -47,12 +47,13 @@ def test_grouped_gemm(gpu_lib, M, G, N, K):
                                      si.sample_rows(M, 16, seed=13)]))
     assert_gemm_close(y[torch.from_numpy(rows).to("cuda")], oracle.grouped_gemm(xq, xs, wq, ws, offsets, rows=rows),
                       f"grouped M={M} G={G}")
-    # groups with more than 64 rows run the same tile kernel as fp8_block_gemm: identical bits
+    # every row of every group against fp8_block_gemm of that group alone (the two
+    # may add the fp32 K-block sums in different orders: compared to the tolerance)
     for g in range(G):
         o0, o1 = int(offsets[g]), int(offsets[g + 1])
-        if o1 - o0 > 64:
+        if o1 > o0:
             yg = gpu_lib.fp8_block_gemm(dev(xq[o0:o1]), dev(xs[o0:o1]), dev(wq[g]), dev(ws[g]))
-            assert torch.equal(y[o0:o1].view(torch.int16), yg.view(torch.int16)), f"group {g}"
+            assert_gemm_close(y[o0:o1], yg.float().cpu().numpy().astype(np.float64), f"group {g}")
 
 
 def test_grouped_gemm_single_group_and_empty(gpu_lib):
