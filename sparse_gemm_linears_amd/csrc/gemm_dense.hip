@@ -422,10 +422,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   }
 }
 
+hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream) {
+  const int64_t blocks = std::min<int64_t>((mn / 4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, mn, y);
+  return hipGetLastError();
+}
+
 // ================================================================ dispatch ==
 
 // Compute units of the current device (cached per device).
-static int device_cu_count() {
+int device_cu_count() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
@@ -447,11 +453,7 @@ static int device_cu_count() {
 // is split over up to 16 workgroups per tile, each with at least four K
 // blocks (a multiple of four when the scales go four at a time); the fp32
 // partials are summed in a second kernel.
-struct TilePlan {
-  int bm, splits, kb_split;
-};
-
-static TilePlan plan_tiles(int M, int N, int K, int cus) {
+TilePlan plan_tiles(int M, int N, int K, int cus) {
   const int tn = (N + 255) / 256;
   const int t256 = ((M + 255) / 256) * tn, t128 = ((M + 127) / 128) * tn;
   const double cost256 = (double)((t256 + cus - 1) / cus), cost128 = 0.62 * (double)((t128 + cus - 1) / cus);
@@ -548,12 +550,7 @@ hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *
                      ? launch_tile<256, 128, 2, 4>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
                      : launch_tile<256, 256, 2, 4>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
   if (p.splits > 1) {
-    if (e == hipSuccess) {
-      const int64_t mn = (int64_t)m * n;
-      const int64_t blocks = std::min<int64_t>((mn / 4 + 255) / 256, 4096);
-      hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, p.splits, mn, y);
-      e = hipGetLastError();
-    }
+    if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
     const hipError_t f = hipFreeAsync(part, stream);
     if (e == hipSuccess) e = f;
   }

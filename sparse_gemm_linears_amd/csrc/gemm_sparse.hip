@@ -46,19 +46,23 @@ struct SparseTile {
   static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
   static_assert(kWaveN == 128, "a wave covers one 128-row weight scale block (and 256-byte epilogue rows)");
   static_assert(BM <= kThreads, "one thread per token scale");
-  static_assert(kWaves * 4096 <= kBTile, "epilogue scratch fits in one token stage");
+  static_assert(kWaves * 4096 <= 2 * kBTile && kBTile % 4096 == 0, "epilogue scratch fits in the token stages");
+  static constexpr int kScratchWavesPerStage = kBTile / 4096;
 };
 
 // SB: K blocks per token-scale load (4 when K/128 is a multiple of 4, else 1).
 // CR: the next K block's copies are issued across the first CR row tiles.
-template <int BN, int BM, int WN, int WM, int SB, int CR>
+// PARTIAL: split K over blockIdx.y (kb_split K blocks each, a multiple of
+// SB) and store unrounded fp32 partial tiles to part + blockIdx.y * M * N.
+template <int BN, int BM, int WN, int WM, int SB, int CR, bool PARTIAL = false>
 __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t *__restrict__ xq,
                                                                  const float *__restrict__ xs,
                                                                  const uint8_t *__restrict__ wv,
                                                                  const uint8_t *__restrict__ wm,
                                                                  const float *__restrict__ ws, int M, int N, int K,
                                                                  uint16_t *__restrict__ y, int tiles_m,
-                                                                 int tiles_n, int group_m) {
+                                                                 int tiles_n, int group_m, float *part,
+                                                                 int kb_split) {
   using C = SparseTile<BN, BM, WN, WM>;
   // one LDS object per stage and panel (see the dense tile kernel)
   __shared__ __align__(16) uint8_t lds_v0[C::kVTile], lds_v1[C::kVTile];
@@ -69,8 +73,20 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
   const int cj = lane >> 3, cp = lane & 7;
-  const int KB = K / kGroup, NB = N / kGroup;
+  // KBs: K blocks per row (the stride of the scale rows); KB: K blocks this
+  // workgroup accumulates, starting at block kb0 (every operand pointer below
+  // is shifted to it; row strides are unchanged)
+  const int KBs = K / kGroup, NB = N / kGroup;
+  int kb0 = 0, KB = KBs;
+  if constexpr (PARTIAL) {
+    kb0 = blockIdx.y * kb_split;
+    KB = min(kb_split, KBs - kb0);
+  }
   const int64_t vrow_bytes = K / 2, mrow_bytes = K / 8;
+  xq += kb0 * kGroup;
+  xs += kb0;
+  wv += kb0 * 64;
+  wm += kb0 * 16;
 
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -94,7 +110,7 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
     b_lane[i] = (uint32_t)((min(r0 + cj, M - 1) - min(r0, M - 1)) * K + copy_chunk);
   }
   TokenScales<BM, SB> scales;
-  scales.init(lds_s, xs, M, KB, m_base, tid);
+  scales.init(lds_s, xs, M, KBs, m_base, tid);
 
   // copy j of a K block: 0 .. kVCopies-1 values, kVCopies the index words
   // (waves below kMCopyWaves), then the token panel
@@ -137,7 +153,7 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
     for (int c = 0; c < C::CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int nb_wave = min((n_base + wn0) / kGroup, NB - 1);
-  const float *ws_row = ws + (int64_t)nb_wave * KB;
+  const float *ws_row = ws + (int64_t)nb_wave * KBs + kb0;
 
   auto step = [&](int kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
@@ -203,14 +219,19 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
     if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{});
   }
 
-  // epilogue through a wave-private 4 KB slice of the (now idle) token stage 0
-  uint8_t *scratch = lds_b0 + wave * 4096;
+  // epilogue through a wave-private 4 KB slice of the (now idle) token stages
+  constexpr int kPer = C::kScratchWavesPerStage;
+  uint8_t *scratch = (wave < kPer ? lds_b0 : lds_b1) + (wave % kPer) * 4096;
 #pragma unroll
   for (int c = 0; c < C::CT; c++) {
     v4f col[C::RT];
 #pragma unroll
     for (int r = 0; r < C::RT; r++) col[r] = acc[r][c];
-    store_token_tile<C::RT>(scratch, col, y, M, N, m_base + wm0 + 16 * c, n_base + wn0, lane);
+    if constexpr (PARTIAL)
+      store_token_tile_f32<C::RT>(col, part + (int64_t)blockIdx.y * M * N, M, N, m_base + wm0 + 16 * c,
+                                  n_base + wn0, lane);
+    else
+      store_token_tile<C::RT>(scratch, col, y, M, N, m_base + wm0 + 16 * c, n_base + wn0, lane);
   }
 }
 
@@ -239,15 +260,25 @@ struct SparseWeight {
 
 template <int BN, int BM, int WN, int WM>
 static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
-                              const float *ws, int M, int N, int K, uint16_t *y, hipStream_t stream) {
+                              const float *ws, int M, int N, int K, uint16_t *y, int splits, int kb_split,
+                              float *part, hipStream_t stream) {
   using C = SparseTile<BN, BM, WN, WM>;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  if ((K / kGroup) % 4 == 0)
-    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 4, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
-                       stream, xq, xs, wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4);
-  else
-    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 1, 4>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
-                       stream, xq, xs, wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4);
+  const dim3 grid(tiles_m * tiles_n, splits);
+  if (splits > 1) {
+    if ((K / kGroup) % 4 == 0)
+      hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 4, 4, true>), grid, dim3(C::kThreads), 0, stream, xq, xs,
+                         wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4, part, kb_split);
+    else
+      hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 1, 4, true>), grid, dim3(C::kThreads), 0, stream, xq, xs,
+                         wv, wm, ws, M, N, K, y, tiles_m, tiles_n, 4, part, kb_split);
+  } else if ((K / kGroup) % 4 == 0) {
+    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 4, 4>), grid, dim3(C::kThreads), 0, stream, xq, xs, wv, wm,
+                       ws, M, N, K, y, tiles_m, tiles_n, 4, part, kb_split);
+  } else {
+    hipLaunchKernelGGL((sparse_tile_kernel<BN, BM, WN, WM, 1, 4>), grid, dim3(C::kThreads), 0, stream, xq, xs, wv, wm,
+                       ws, M, N, K, y, tiles_m, tiles_n, 4, part, kb_split);
+  }
   return hipGetLastError();
 }
 
@@ -294,7 +325,22 @@ hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t 
                               const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
   if (m <= 64) return launch_sparse_decode(QuantTokens{xq, xs, k}, wv, wm, ws, m, n, k, y, stream);
-  return launch_tile<256, 256, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, stream);
+  const TilePlan p = plan_tiles(m, n, k, device_cu_count());
+  float *part = nullptr;
+  if (p.splits > 1) {
+    const hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&part),
+                                        (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = p.bm == 128
+                     ? launch_tile<256, 128, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
+                     : launch_tile<256, 256, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
+  if (p.splits > 1) {
+    if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
+    const hipError_t f = hipFreeAsync(part, stream);
+    if (e == hipSuccess) e = f;
+  }
+  return e;
 }
 
 hipError_t launch_sparse_linear(const uint16_t *x, const uint8_t *wv, const uint8_t *wm, const float *ws, int64_t M,

@@ -9,6 +9,17 @@ namespace fp8lin {
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, hipStream_t stream);
 hipError_t launch_quant_wblock(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, hipStream_t stream);
+// Tile-kernel plan shared by the dense and 2:4 GEMMs: tile height (256 or 128
+// tokens) and K split (splits workgroups per tile, kb_split K blocks each).
+// Split GEMMs store fp32 partials [splits][M][N] that launch_splitk_reduce
+// adds in order into y.
+struct TilePlan {
+  int bm, splits, kb_split;
+};
+int device_cu_count();
+TilePlan plan_tiles(int M, int N, int K, int cus);
+hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
+
 // One scale for a whole tensor of n bf16 values (n a multiple of 8), written
 // to all n_s entries of s (n_s >= 1): the dynamic per-tensor amax / 448, or a
 // static scale read from device memory.

@@ -1,4 +1,4 @@
-"""Block-scaled GEMM at mid-size M (65 .. ~1000 tokens), where the tile kernel
+"""Block-scaled dense and 2:4 GEMMs at mid-size M (65 .. ~1000 tokens), where the tile kernel
 runs with 256 x 128 tiles and, when the tiles cover at most half of the
 compute units, splits K over several workgroups whose fp32 partials are summed
 in a second kernel.  Parity with the oracle within the GEMM tolerance, on the
@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import synth_inputs as si
-from test_parity_gpu import DEV, assert_gemm_close, llama_acts, llama_weight, run_dense, sample_tile_rows
+from test_parity_gpu import (DEV, assert_gemm_close, llama_acts, llama_sparse_weight, llama_weight, run_dense,
+                             run_sparse, sample_tile_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,4 +53,32 @@ def test_dense_gemm_mid_m_deterministic(gpu_lib):
     _, (wq, ws) = llama_weight(14336, 4096)
     a = run_dense(gpu_lib, xq, xs, wq, ws)
     b = run_dense(gpu_lib, xq, xs, wq, ws)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [65, 256, 1000])
+@pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
+def test_sparse_gemm_mid_m(gpu_lib, name, K, N, M):
+    _, (xq, xs) = llama_acts(M, K)
+    _, (vals, meta, ws) = llama_sparse_weight(K, N, True)
+    y = run_sparse(gpu_lib, xq, xs, vals, meta, ws)
+    rows = sample_tile_rows(M, 8)
+    assert_gemm_close(y[torch.from_numpy(rows).to(DEV)], oracle.sparse24_gemm(xq, xs, vals, meta, ws, rows=rows),
+                      f"2:4 {name} M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 384, 2048), (97, 256, 1152), (700, 640, 4096)])
+def test_sparse_gemm_mid_m_ragged(gpu_lib, M, N, K):
+    x = si.activations(M, K, outliers=False)
+    vals, meta, ws = oracle.prune24_compress(si.weights(N, K))
+    xq, xs = oracle.quant_act(x)
+    assert_gemm_close(run_sparse(gpu_lib, xq, xs, vals, meta, ws), oracle.sparse24_gemm(xq, xs, vals, meta, ws),
+                      f"2:4 {M}x{N}x{K}")
+
+
+def test_sparse_gemm_mid_m_deterministic(gpu_lib):
+    _, (xq, xs) = llama_acts(128, 14336)
+    _, (vals, meta, ws) = llama_sparse_weight(14336, 4096, True)
+    a = run_sparse(gpu_lib, xq, xs, vals, meta, ws)
+    b = run_sparse(gpu_lib, xq, xs, vals, meta, ws)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
