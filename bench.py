@@ -66,7 +66,7 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--no-decode", action="store_true", help="skip the decode-M GEMM measurements")
+    p.add_argument("--no-decode", action="store_true", help="skip the decode-M and mid-M GEMM measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=1024, help="token rows in the CPU oracle sample")
     return p.parse_args()
@@ -228,6 +228,7 @@ def main():
     swiglu = bench_swiglu(sgl, si, torch, np, dev, bf16, args.steps)
     ue8m0 = bench_ue8m0(sgl, si, torch, np, dev, bf16, args.steps)
     decode = None if args.no_decode else bench_decode(sgl, si, torch, np, dev, bf16)
+    mid_m = None if args.no_decode else bench_mid_m(sgl, si, torch, np, dev, bf16, args.steps)
     cpu = None if args.no_cpu else cpu_baseline(si, np, args.cpu_rows)
 
     out = {
@@ -244,6 +245,7 @@ def main():
         "swiglu": swiglu,
         "ue8m0": ue8m0,
         "decode": decode,
+        "mid_m": mid_m,
     }
     print(json.dumps(out))
 
@@ -375,6 +377,29 @@ def bench_decode(sgl, si, torch, np, dev, bf16):
                     res[f"{name}.M16.dense"]["us"] / res[f"{name}.M16.sparse"]["us"], 3)
         del dense_w, sparse_w
         torch.cuda.empty_cache()
+    return res
+
+
+def bench_mid_m(sgl, si, torch, np, dev, bf16, steps):
+    """Mid-size batches (M in {128, 512}) on the four Llama-3-8B shapes, dense and
+    2:4: the tile kernels with the tile height and K split chosen for the
+    shape (back-to-back calls; the weight of one shape fits the MALL, so these
+    are the compute-side times)."""
+    res = {}
+    for name, K, N in si.LLAMA3_8B:
+        w = bf16(si.weights(N, K))
+        wq, ws = sgl.fp8_quant_weight_block(w)
+        wv, wm, ws2 = sgl.prune24_compress(w)
+        for M in (128, 512):
+            xq, xs = sgl.fp8_quant_act(bf16(si.activations(M, K)))
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for kind, f in (("dense", lambda: sgl.fp8_block_gemm(xq, xs, wq, ws, y)),
+                            ("sparse", lambda: sgl.fp8_sparse24_gemm(xq, xs, wv, wm, ws2, y))):
+                us = time_calls(torch, f, steps)
+                flops = 2 * M * N * K * (1 if kind == "dense" else 0.5)
+                res[f"{name}.M{M}.{kind}"] = {"us": round(us, 2), "tflops": round(flops / us / 1e6, 1)}
+        del w, wq, ws, wv, wm, ws2
+    torch.cuda.empty_cache()
     return res
 
 

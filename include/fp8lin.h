@@ -9,12 +9,14 @@
  *
  * Ownership: the caller allocates every input and output; the library keeps
  * no pointer after a call returns and no state between calls besides
- * per-device architecture and compute-unit counts.  One call allocates:
+ * per-device architecture and compute-unit counts.  Two calls allocate:
  * fp8_block_gemm with M > 64 and too few 256-wide output tiles to cover half
  * of the compute units splits K, and takes an fp32 workspace of at most 256
- * tiles' worth (S * M * N * 4 bytes, S <= 16) from the device's stream-ordered
- * memory pool (hipMallocAsync on `stream`), releasing it on the same stream
- * (hipFreeAsync) after the kernels that use it.  Calls may be made from
+ * tiles' worth (S * M * N * 4 bytes, S <= 16) from a stream-ordered memory
+ * pool the library creates once per device (hipMallocFromPoolAsync on
+ * `stream`), releasing it on the same stream (hipFreeAsync) after the kernels
+ * that use it; the pool keeps up to 256 MB cached until the process ends.
+ * fp8_sparse24_gemm does the same.  Calls may be made from
  * several host threads on different streams.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its

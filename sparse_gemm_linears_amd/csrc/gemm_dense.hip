@@ -15,6 +15,8 @@
 //    registers, the waves of a workgroup split K and meet in LDS at the end.
 #include <algorithm>
 #include <atomic>
+#include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -430,6 +432,46 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint1
 
 // ================================================================ dispatch ==
 
+// Split-K workspace: one library-owned stream-ordered memory pool per device,
+// keeping up to 256 MB cached between calls (the default pool hands memory
+// back to the driver at every synchronisation, so each step of an inference
+// loop would pay a fresh allocation).
+static hipError_t workspace_pool(hipMemPool_t *out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static hipMemPool_t pools[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!pools[dev]) {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if ((e = hipMemPoolCreate(&pool, &props)) != hipSuccess) return e;
+    uint64_t keep = uint64_t(256) << 20;
+    if ((e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return e;
+    }
+    pools[dev] = pool;
+  }
+  *out = pools[dev];
+  return hipSuccess;
+}
+
+hipError_t workspace_alloc(float **p, size_t bytes, hipStream_t stream) {
+  hipMemPool_t pool;
+  const hipError_t e = workspace_pool(&pool);
+  if (e != hipSuccess) return e;
+  return hipMallocFromPoolAsync(reinterpret_cast<void **>(p), bytes, pool, stream);
+}
+
 // Compute units of the current device (cached per device).
 int device_cu_count() {
   constexpr int kMaxDevices = 64;
@@ -542,8 +584,7 @@ hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *
   const TilePlan p = plan_tiles(m, n, k, device_cu_count());
   float *part = nullptr;
   if (p.splits > 1) {
-    const hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&part),
-                                        (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
+    const hipError_t e = workspace_alloc(&part, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
     if (e != hipSuccess) return e;
   }
   hipError_t e = p.bm == 128

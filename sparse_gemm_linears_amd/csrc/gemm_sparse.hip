@@ -328,8 +328,7 @@ hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   const TilePlan p = plan_tiles(m, n, k, device_cu_count());
   float *part = nullptr;
   if (p.splits > 1) {
-    const hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&part),
-                                        (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
+    const hipError_t e = workspace_alloc(&part, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
     if (e != hipSuccess) return e;
   }
   hipError_t e = p.bm == 128

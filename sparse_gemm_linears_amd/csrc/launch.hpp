@@ -19,6 +19,9 @@ struct TilePlan {
 int device_cu_count();
 TilePlan plan_tiles(int M, int N, int K, int cus);
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
+// Stream-ordered workspace from the library's per-device pool; released with
+// hipFreeAsync on the same stream.
+hipError_t workspace_alloc(float **p, size_t bytes, hipStream_t stream);
 
 // One scale for a whole tensor of n bf16 values (n a multiple of 8), written
 // to all n_s entries of s (n_s >= 1): the dynamic per-tensor amax / 448, or a
