@@ -65,12 +65,18 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
     c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
   }
 
+  // all eight row loads in flight before any arithmetic (interleaved with the
+  // scoring, the compiler waits for each load before issuing the next)
+  const uint16_t* wp = w + row0 * K + kcol;
+  uint4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) raw[i] = *reinterpret_cast<const uint4*>(wp + (int64_t)i * 16 * K);
+
   Kept2 kept[8][2];
   uint32_t amax_bits = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(w + (row0 + 16 * i) * K + kcol);
-    const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint32_t r[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       const uint32_t lo = r[2 * h], hi = r[2 * h + 1];
