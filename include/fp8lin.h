@@ -9,14 +9,18 @@
  *
  * Ownership: the caller allocates every input and output; the library keeps
  * no pointer after a call returns and no state between calls besides
- * per-device architecture and compute-unit counts.  Two calls allocate:
- * fp8_block_gemm with M > 64 and too few 256-wide output tiles to cover half
- * of the compute units splits K, and takes an fp32 workspace of at most 256
- * tiles' worth (S * M * N * 4 bytes, S <= 16) from a stream-ordered memory
- * pool the library creates once per device (hipMallocFromPoolAsync on
- * `stream`), releasing it on the same stream (hipFreeAsync) after the kernels
- * that use it; the pool keeps up to 256 MB cached until the process ends.
- * fp8_sparse24_gemm does the same.  Calls may be made from
+ * per-device architecture and compute-unit counts.  Four calls may allocate,
+ * from a stream-ordered memory pool the library creates once per device
+ * (hipMallocFromPoolAsync on `stream`, released with hipFreeAsync on the same
+ * stream after the kernels that use it; the pool keeps up to 256 MB cached
+ * until the process ends):
+ *   fp8_block_gemm and fp8_sparse24_gemm on the tile kernel (M > 64, or
+ *   M > 32 with N * K >= 2^25) with too few output tiles to cover half of the
+ *   compute units split K, with an fp32 workspace of at most 256 tiles' worth
+ *   (S * M * N * 4 bytes, S <= 16);
+ *   fp8_block_linear and fp8_sparse24_linear with M > 32 and N * K >= 2^25
+ *   quantize the tokens into a workspace (M * K + 4 * M * K / 128 bytes) and
+ *   run the tile GEMM on them.  Calls may be made from
  * several host threads on different streams.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
@@ -159,9 +163,10 @@ fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N
  *   wq [N,K] e4m3, ws [N/128,K/128] fp32   from fp8_quant_weight_block
  *   y [M,N] bf16   y[m,n] = bf16_rne( sum_kb xs[m,kb] * ws[n/128,kb] *
  *                                     sum_{k in kb} dec(xq[m,k]) * dec(wq[n,k]) )
- * The inner block sums are exact FP8 products accumulated in fp32.  With
- * M > 64 and few output tiles the K blocks are summed in up to 16 fp32
- * partials (each in K order) that are then added in a fixed order, which
+ * The inner block sums are exact FP8 products accumulated in fp32.  Small
+ * batches (M <= 32, or M <= 64 when N * K < 2^25) run a weight-streaming
+ * kernel; the rest run the tile kernel.  With few output tiles the K blocks
+ * are summed in up to 16 fp32 partials (each in K order) that are then added in a fixed order, which
  * changes only the fp32 rounding order; results are deterministic either way.
  */
 fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
@@ -261,8 +266,11 @@ fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint
  *   wq [N,K] e4m3, ws [N/128,K/128] fp32   from fp8_quant_weight_block
  *   y [M,N] bf16
  * y is bit-identical to fp8_quant_act(x) followed by fp8_block_gemm on the
- * resulting codes and scales: each workgroup quantizes the activations it
- * reads with the same arithmetic, and the codes are never written out.
+ * resulting codes and scales.  Where fp8_block_gemm runs its weight-streaming
+ * kernel, each workgroup quantizes the activations it reads with the same
+ * arithmetic and the codes are never written out; where it runs the tile
+ * kernel (M > 32 with N * K >= 2^25) this call is those two calls, with the
+ * codes in a pool workspace.
  * M > 64 is FP8L_ERR_SHAPE: for a larger batch, quantize it once with
  * fp8_quant_act and call fp8_block_gemm.
  * Performance: every workgroup quantizes the activations it needs, so the

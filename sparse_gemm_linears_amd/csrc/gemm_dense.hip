@@ -514,28 +514,52 @@ TilePlan plan_tiles(int M, int N, int K, int cus) {
   return p;
 }
 
-template <int BN, int BM, int WN, int WM>
-static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int M, int N,
-                              int K, uint16_t *y, int splits, int kb_split, float *part, hipStream_t stream) {
+// S: float (fp32 scales) or uint8_t (UE8M0 exponents, E8 = true).
+template <int BN, int BM, int WN, int WM, bool E8, class S>
+static hipError_t launch_tile(const uint8_t *xq, const S *xs, const uint8_t *wq, const S *ws, int M, int N, int K,
+                              uint16_t *y, int splits, int kb_split, float *part, hipStream_t stream) {
   using C = DenseTile<BN, BM, WN, WM>;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const TileExtra ex{nullptr, nullptr, 0, nullptr, 0, part, kb_split};
   const dim3 grid(tiles_m * tiles_n, splits);
   if (splits > 1) {
     if ((K / kGroup) % 4 == 0)
-      hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false, false, false, true>), grid,
+      hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false, E8, false, true>), grid,
                          dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
     else
-      hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4, false, false, false, true>), grid,
+      hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4, false, E8, false, true>), grid,
                          dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
   } else if ((K / kGroup) % 4 == 0) {
-    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false>), grid, dim3(C::kThreads), 0, stream, xq, xs,
-                       wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
+    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false, E8>), grid, dim3(C::kThreads), 0, stream, xq,
+                       xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
   } else {
-    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4, false>), grid, dim3(C::kThreads), 0, stream, xq, xs,
-                       wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
+    hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 1, 4, false, E8>), grid, dim3(C::kThreads), 0, stream, xq,
+                       xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
   }
   return hipGetLastError();
+}
+
+// Tile-kernel GEMM with the planned tile height and K split (workspace and
+// reduction included).
+template <bool E8, class S>
+static hipError_t tile_gemm(const uint8_t *xq, const S *xs, const uint8_t *wq, const S *ws, int m, int n, int k,
+                            uint16_t *y, hipStream_t stream) {
+  const TilePlan p = plan_tiles(m, n, k, device_cu_count());
+  float *part = nullptr;
+  if (p.splits > 1) {
+    const hipError_t e = workspace_alloc(&part, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e =
+      p.bm == 128
+          ? launch_tile<256, 128, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
+          : launch_tile<256, 256, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
+  if (p.splits > 1) {
+    if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
+    const hipError_t f = hipFreeAsync(part, stream);
+    if (e == hipSuccess) e = f;
+  }
+  return e;
 }
 
 template <class X, int RT, int CT, int NW, int D>
@@ -580,22 +604,8 @@ static hipError_t launch_dense_decode(X xop, const uint8_t *wq, const typename X
 hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
                              int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (m <= 64) return launch_dense_decode(QuantTokens{xq, xs, k}, wq, ws, m, n, k, y, stream);
-  const TilePlan p = plan_tiles(m, n, k, device_cu_count());
-  float *part = nullptr;
-  if (p.splits > 1) {
-    const hipError_t e = workspace_alloc(&part, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = p.bm == 128
-                     ? launch_tile<256, 128, 2, 4>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
-                     : launch_tile<256, 256, 2, 4>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
-  if (p.splits > 1) {
-    if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
-    const hipError_t f = hipFreeAsync(part, stream);
-    if (e == hipSuccess) e = f;
-  }
-  return e;
+  if (!use_tile_kernel(m, n, k)) return launch_dense_decode(QuantTokens{xq, xs, k}, wq, ws, m, n, k, y, stream);
+  return tile_gemm<false>(xq, xs, wq, ws, m, n, k, y, stream);
 }
 
 hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
@@ -616,18 +626,9 @@ hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const ui
 
 hipError_t launch_dense_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uint8_t *wq, const uint8_t *we,
                                    int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
-  using C = DenseTile<256, 256, 2, 4>;
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (m <= 64) return launch_dense_decode(QuantTokensE8{xq, xe, k}, wq, we, m, n, k, y, stream);
-  const int tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
-  const TileExtra none{nullptr, nullptr, 0, nullptr, 0};
-  if ((k / kGroup) % 4 == 0)
-    hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 4, 4, false, true>), dim3(tiles_m * tiles_n),
-                       dim3(C::kThreads), 0, stream, xq, xe, wq, we, m, n, k, y, tiles_m, tiles_n, 4, none);
-  else
-    hipLaunchKernelGGL((dense_tile_kernel<256, 256, 2, 4, 1, 4, false, true>), dim3(tiles_m * tiles_n),
-                       dim3(C::kThreads), 0, stream, xq, xe, wq, we, m, n, k, y, tiles_m, tiles_n, 4, none);
-  return hipGetLastError();
+  if (!use_tile_kernel(m, n, k)) return launch_dense_decode(QuantTokensE8{xq, xe, k}, wq, we, m, n, k, y, stream);
+  return tile_gemm<true>(xq, xe, wq, we, m, n, k, y, stream);
 }
 
 hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
@@ -648,6 +649,10 @@ hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const u
 
 hipError_t launch_dense_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
                                int64_t K, uint16_t *y, hipStream_t stream) {
+  if (use_tile_kernel(M, N, K))
+    return quantize_then(x, M, K, stream, [&](const uint8_t *xq, const float *xs) {
+      return launch_dense_gemm(xq, xs, wq, ws, M, N, K, y, stream);
+    });
   if (staged_tokens_fit(M, K))
     return launch_dense_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wq, ws, (int)M, (int)N, (int)K, y, stream);
   return launch_dense_decode(Bf16Tokens{x, (int)K}, wq, ws, (int)M, (int)N, (int)K, y, stream);

@@ -324,7 +324,7 @@ static hipError_t launch_sparse_decode(X xop, const uint8_t *wv, const uint8_t *
 hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
                               const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (m <= 64) return launch_sparse_decode(QuantTokens{xq, xs, k}, wv, wm, ws, m, n, k, y, stream);
+  if (!use_tile_kernel(m, n, k)) return launch_sparse_decode(QuantTokens{xq, xs, k}, wv, wm, ws, m, n, k, y, stream);
   const TilePlan p = plan_tiles(m, n, k, device_cu_count());
   float *part = nullptr;
   if (p.splits > 1) {
@@ -344,6 +344,10 @@ hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t 
 
 hipError_t launch_sparse_linear(const uint16_t *x, const uint8_t *wv, const uint8_t *wm, const float *ws, int64_t M,
                                 int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  if (use_tile_kernel(M, N, K))
+    return quantize_then(x, M, K, stream, [&](const uint8_t *xq, const float *xs) {
+      return launch_sparse_gemm(xq, xs, wv, wm, ws, M, N, K, y, stream);
+    });
   if (staged_tokens_fit(M, K))
     return launch_sparse_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wv, wm, ws, (int)M, (int)N, (int)K, y,
                                 stream);

@@ -18,10 +18,35 @@ struct TilePlan {
 };
 int device_cu_count();
 TilePlan plan_tiles(int M, int N, int K, int cus);
+// Decode kernel or tile kernel: the decode kernel streams the weight once but
+// re-reads the tokens per workgroup, so past 32 tokens the tile kernel (split
+// K) is faster on large weights (measured on MI355X: from M = 48 on the
+// 28672x4096 and 4096x14336 Llama-3-8B weights, dense and 2:4, while the
+// 6144x4096 and 4096x4096 ones stay faster in the decode kernel up to 64).
+inline bool use_tile_kernel(int64_t M, int64_t N, int64_t K) {
+  return M > 64 || (M > 32 && N * K >= (int64_t(1) << 25));
+}
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
 // Stream-ordered workspace from the library's per-device pool; released with
 // hipFreeAsync on the same stream.
 hipError_t workspace_alloc(float **p, size_t bytes, hipStream_t stream);
+
+// Tokens quantized into a workspace from the library pool, then the GEMM on
+// them: exactly fp8_quant_act followed by gemm(xq, xs).
+template <class Gemm>
+inline hipError_t quantize_then(const uint16_t *x, int64_t M, int64_t K, hipStream_t stream, Gemm gemm) {
+  const size_t q_bytes = ((size_t)M * (size_t)K + 255) / 256 * 256;
+  const size_t s_bytes = (size_t)M * (size_t)(K / 128) * sizeof(float);
+  float *ws_mem = nullptr;
+  hipError_t e = workspace_alloc(&ws_mem, q_bytes + s_bytes, stream);
+  if (e != hipSuccess) return e;
+  uint8_t *xq = reinterpret_cast<uint8_t *>(ws_mem);
+  float *xs = reinterpret_cast<float *>(xq + q_bytes);
+  e = launch_quant_act(x, M, K, xq, xs, stream);
+  if (e == hipSuccess) e = gemm(xq, xs);
+  const hipError_t f = hipFreeAsync(ws_mem, stream);
+  return e == hipSuccess ? f : e;
+}
 
 // One scale for a whole tensor of n bf16 values (n a multiple of 8), written
 // to all n_s entries of s (n_s >= 1): the dynamic per-tensor amax / 448, or a

@@ -1,4 +1,5 @@
-"""Block-scaled dense and 2:4 GEMMs at mid-size M (65 .. ~1000 tokens), where the tile kernel
+"""Block-scaled dense, 2:4 and UE8M0 GEMMs at mid-size M (33 .. ~1000 tokens:
+past 32 tokens on the large weights, past 64 on all), where the tile kernel
 runs with 256 x 128 tiles and, when the tiles cover at most half of the
 compute units, splits K over several workgroups whose fp32 partials are summed
 in a second kernel.  Parity with the oracle within the GEMM tolerance, on the
@@ -11,13 +12,13 @@ import torch
 
 import oracle
 import synth_inputs as si
-from test_parity_gpu import (DEV, assert_gemm_close, llama_acts, llama_sparse_weight, llama_weight, run_dense,
+from test_parity_gpu import (DEV, assert_gemm_close, dev, llama_acts, llama_sparse_weight, llama_weight, run_dense,
                              run_sparse, sample_tile_rows)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M", [65, 128, 256, 512, 1000])
+@pytest.mark.parametrize("M", [33, 48, 65, 128, 256, 512, 1000])
 @pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
 def test_dense_gemm_mid_m(gpu_lib, name, K, N, M):
     _, (xq, xs) = llama_acts(M, K)
@@ -56,7 +57,7 @@ def test_dense_gemm_mid_m_deterministic(gpu_lib):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [65, 256, 1000])
+@pytest.mark.parametrize("M", [48, 65, 256, 1000])
 @pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
 def test_sparse_gemm_mid_m(gpu_lib, name, K, N, M):
     _, (xq, xs) = llama_acts(M, K)
@@ -82,3 +83,14 @@ def test_sparse_gemm_mid_m_deterministic(gpu_lib):
     a = run_sparse(gpu_lib, xq, xs, vals, meta, ws)
     b = run_sparse(gpu_lib, xq, xs, vals, meta, ws)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [48, 128, 512])
+@pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
+def test_ue8m0_gemm_mid_m(gpu_lib, name, K, N, M):
+    xq, xe = oracle.quant_act_ue8m0(llama_acts(M, K)[0])
+    wq, we = oracle.quant_wblock_ue8m0(llama_weight(K, N)[0])
+    y = gpu_lib.fp8_block_gemm_ue8m0(dev(xq), dev(xe), dev(wq), dev(we))
+    rows = sample_tile_rows(M, 8)
+    assert_gemm_close(y[torch.from_numpy(rows).to(DEV)], oracle.gemm_ue8m0(xq, xe, wq, we, rows=rows),
+                      f"ue8m0 {name} M={M}")
