@@ -311,18 +311,15 @@ def bench_swiglu(sgl, si, torch, np, dev, bf16, steps):
         "gemm_only": lambda: sgl.fp8_block_gemm(xq, xs, wq, ws, y),
         "quant_act_of_h": lambda: sgl.fp8_quant_act(h, hq, hs),
     }
+    # three alternating rounds, medians: the order of separate runs shifts the
+    # clock by more than the differences measured here
+    times = {name: [] for name in runs}
+    for _ in range(3):
+        for name, f in runs.items():
+            times[name].append(time_calls(torch, f, steps))
     res = {}
-    for name, f in runs.items():
-        for _ in range(3):
-            f()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            f()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+    for name in runs:
+        us = sorted(times[name])[1]
         entry = {"us": round(us, 2)}
         if name != "quant_act_of_h":
             entry["tflops"] = round(2 * M * 2 * I * K / us / 1e6, 1)
