@@ -9,7 +9,7 @@
  *
  * Ownership: the caller allocates every input and output; the library keeps
  * no pointer after a call returns and no state between calls besides
- * per-device architecture and compute-unit counts.  Four calls may allocate,
+ * per-device architecture and compute-unit counts.  Five calls may allocate,
  * from a stream-ordered memory pool the library creates once per device
  * (hipMallocFromPoolAsync on `stream`, released with hipFreeAsync on the same
  * stream after the kernels that use it; the pool keeps up to 256 MB cached
@@ -20,7 +20,9 @@
  *   (S * M * N * 4 bytes, S <= 16);
  *   fp8_block_linear and fp8_sparse24_linear with M > 32 and N * K >= 2^25
  *   quantize the tokens into a workspace (M * K + 4 * M * K / 128 bytes) and
- *   run the tile GEMM on them.  Calls may be made from
+ *   run the tile GEMM on them;
+ *   fp8_block_gemm_swiglu with few tokens keeps the fp32 partials of the
+ *   stacked GEMM in a workspace.  Calls may be made from
  * several host threads on different streams.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
@@ -247,8 +249,12 @@ fp8l_status fp8_block_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uin
  *                                   g, u the fp32 block-scaled sums of fp8_block_gemm
  *   hq [M,I] e4m3, hs [M,I/128]     fp8_quant_act(h), the next layer's input
  *                                   (both NULL: not produced)
- * I must be a positive multiple of 128.  Meant for prefill-sized M: every
- * call runs 256-token tiles.
+ * I must be a positive multiple of 128.  Prefill-sized M runs the fused
+ * kernel (256-token tiles, SwiGLU and the quantization in the epilogue).
+ * Where that grid would leave compute units idle (few tokens), the stacked
+ * GEMM runs on smaller tiles and/or split K into fp32 partials held in a pool
+ * workspace (S * M * 2I * 4 bytes), and one more kernel sums them and applies
+ * SwiGLU and the quantization with the same arithmetic.
  */
 fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
                                   int64_t M, int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs,

@@ -412,6 +412,53 @@ struct DenseWeight {
 
 // ===================================================== split-K reduction ==
 
+// SwiGLU of summed partials, and optionally the group quantization of h:
+// part [S][M][2I] fp32, gate sums in columns [0, I), up sums in [I, 2I).  16
+// lanes own one 1x128 group of h (8 values each); h = bf16(silu(g) * u) as in
+// the tile kernel's SwiGLU epilogue, codes and scale from quantize_group16 on
+// the stored bf16 values (the arithmetic of fp8_quant_act).
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float *__restrict__ part, int S, int M, int I,
+                                                            uint16_t *__restrict__ h, uint8_t *__restrict__ hq,
+                                                            float *__restrict__ hs) {
+  const int lane16 = threadIdx.x & 15, gpr = I / kGroup;
+  const int64_t grp = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = grp < (int64_t)M * gpr;  // uniform over the 16 lanes of a group
+  const int64_t m = live ? grp / gpr : 0, col = (live ? grp % gpr : 0) * kGroup + lane16 * 8;
+  const int64_t mn2 = (int64_t)M * 2 * I;
+  v4f g[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}}, u[2] = {g[0], g[0]};
+  if (live) {
+    const float *pg = part + m * 2 * I + col, *pu = pg + I;
+    for (int s = 0; s < S; s++) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        g[i] += *reinterpret_cast<const v4f *>(pg + (int64_t)s * mn2 + 4 * i);
+        u[i] += *reinterpret_cast<const v4f *>(pu + (int64_t)s * mn2 + 4 * i);
+      }
+    }
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    uint32_t b2[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const float gv = g[i / 2][2 * (i % 2) + j], uv = u[i / 2][2 * (i % 2) + j];
+      b2[j] = f32_to_bf16_rne(gv * uv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)));
+    }
+    w[i] = b2[0] | (b2[1] << 16);
+  }
+  const uint4 raw = make_uint4(w[0], w[1], w[2], w[3]);
+  if (live) *reinterpret_cast<uint4 *>(h + m * I + col) = raw;
+  if (hq) {
+    float sc;
+    const uint2 codes = quantize_group16(raw, sc);
+    if (live) {
+      *reinterpret_cast<uint2 *>(hq + m * I + col) = codes;
+      if (lane16 == 0) hs[m * gpr + col / kGroup] = sc;
+    }
+  }
+}
+
 // y = bf16(sum over s of part[s]), the S partials [S][M*N] added in order s =
 // 0, 1, .. (deterministic); four elements per thread, grid-stride.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int S, int64_t mn,
@@ -515,6 +562,7 @@ TilePlan plan_tiles(int M, int N, int K, int cus) {
 }
 
 // S: float (fp32 scales) or uint8_t (UE8M0 exponents, E8 = true).
+// part != nullptr: fp32 partials (splits of kb_split K blocks) instead of y.
 template <int BN, int BM, int WN, int WM, bool E8, class S>
 static hipError_t launch_tile(const uint8_t *xq, const S *xs, const uint8_t *wq, const S *ws, int M, int N, int K,
                               uint16_t *y, int splits, int kb_split, float *part, hipStream_t stream) {
@@ -522,7 +570,7 @@ static hipError_t launch_tile(const uint8_t *xq, const S *xs, const uint8_t *wq,
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const TileExtra ex{nullptr, nullptr, 0, nullptr, 0, part, kb_split};
   const dim3 grid(tiles_m * tiles_n, splits);
-  if (splits > 1) {
+  if (part) {
     if ((K / kGroup) % 4 == 0)
       hipLaunchKernelGGL((dense_tile_kernel<BN, BM, WN, WM, 4, 4, false, E8, false, true>), grid,
                          dim3(C::kThreads), 0, stream, xq, xs, wq, ws, M, N, K, y, tiles_m, tiles_n, 4, ex);
@@ -554,6 +602,7 @@ static hipError_t tile_gemm(const uint8_t *xq, const S *xs, const uint8_t *wq, c
       p.bm == 128
           ? launch_tile<256, 128, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
           : launch_tile<256, 256, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
+  // (part is NULL when splits == 1: launch_tile then writes y)
   if (p.splits > 1) {
     if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
     const hipError_t f = hipFreeAsync(part, stream);
@@ -612,7 +661,26 @@ hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const ui
                                    int64_t M, int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs,
                                    hipStream_t stream) {
   using C = DenseTile<256, 256, 2, 4>;
-  const int m = (int)M, k = (int)K;
+  const int m = (int)M, k = (int)K, n2 = (int)(2 * I);
+  const TilePlan p = plan_tiles(m, n2, k, device_cu_count());
+  if (p.bm != 256 || p.splits > 1) {
+    // few output tiles: the tile GEMM of the stacked weight into fp32 partials
+    // (K split as planned), then SwiGLU and the quantization in one pass
+    float *part = nullptr;
+    hipError_t e = workspace_alloc(&part, (size_t)p.splits * (size_t)m * (size_t)n2 * sizeof(float), stream);
+    if (e != hipSuccess) return e;
+    e = p.bm == 128
+            ? launch_tile<256, 128, 2, 4, false>(xq, xs, wq, ws, m, n2, k, nullptr, p.splits, p.kb_split, part, stream)
+            : launch_tile<256, 256, 2, 4, false>(xq, xs, wq, ws, m, n2, k, nullptr, p.splits, p.kb_split, part, stream);
+    if (e == hipSuccess) {
+      const int64_t groups = (int64_t)m * (I / kGroup);
+      hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)((groups + 15) / 16)), dim3(256), 0, stream, part,
+                         p.splits, m, (int)I, h, hq, hs);
+      e = hipGetLastError();
+    }
+    const hipError_t f = hipFreeAsync(part, stream);
+    return e == hipSuccess ? f : e;
+  }
   const int tiles_m = (m + 255) / 256, tiles_n = (int)(I / 128);
   const TileExtra so{hq, hs, (int)I, nullptr, 0};
   if ((k / kGroup) % 4 == 0)

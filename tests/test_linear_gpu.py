@@ -132,7 +132,8 @@ def gate_up_weight(K: int, I: int):
     return oracle.quant_wblock(si.weights(2 * I, K))
 
 
-@pytest.mark.parametrize("M,I,K", [(4096, 14336, 4096), (300, 256, 640), (16, 128, 128), (513, 384, 1152)])
+@pytest.mark.parametrize("M,I,K", [(4096, 14336, 4096), (300, 256, 640), (16, 128, 128), (513, 384, 1152),
+                                   (1, 14336, 4096), (64, 14336, 4096), (200, 14336, 4096), (97, 384, 1152)])
 def test_gemm_swiglu(gpu_lib, M, I, K):
     x = si.activations(M, K, outliers=(K == 4096))
     xq, xs = oracle.quant_act(x)
