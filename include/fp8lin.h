@@ -272,17 +272,15 @@ fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint
  *   wq [N,K] e4m3, ws [N/128,K/128] fp32   from fp8_quant_weight_block
  *   y [M,N] bf16
  * y is bit-identical to fp8_quant_act(x) followed by fp8_block_gemm on the
- * resulting codes and scales.  Where fp8_block_gemm runs its weight-streaming
- * kernel, each workgroup quantizes the activations it reads with the same
- * arithmetic and the codes are never written out; where it runs the tile
- * kernel (M > 32 with N * K >= 2^25) this call is those two calls, with the
- * codes in a pool workspace.
+ * resulting codes and scales.  One or two tokens (with the M x K codes fitting
+ * in 36 KB of LDS) are quantized inside the weight-streaming kernel: every
+ * workgroup quantizes the tokens into LDS and the codes are never written out.
+ * Otherwise, where re-quantizing in every workgroup would cost more than it
+ * saves, the call is those two calls, with the codes in a pool workspace.
  * M > 64 is FP8L_ERR_SHAPE: for a larger batch, quantize it once with
  * fp8_quant_act and call fp8_block_gemm.
- * Performance: every workgroup quantizes the activations it needs, so the
- * fused call is faster than the two calls only while that work is small.
  * Measured on MI355X (Llama-3-8B shapes, HIP graphs), one or two tokens save
- * 0.2-2.5 us per call; from three tokens on the two-call path is faster.
+ * 0.2-2.5 us per call against the two calls.
  */
 fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
                              int64_t K, uint16_t *y, hipStream_t stream);

@@ -33,7 +33,6 @@ struct QuantTokens {
   const float *xs;
   int K;
   static constexpr bool kStaged = false, kE8 = false;
-  static constexpr int kRawRegs = 9;  // VGPRs per loaded K block
   typedef float Scale;
   struct Raw {
     v8i q;
@@ -59,7 +58,6 @@ struct QuantTokensE8 {
   const uint8_t *xe;
   int K;
   static constexpr bool kStaged = false, kE8 = true;
-  static constexpr int kRawRegs = 9;
   typedef uint8_t Scale;
   struct Raw {
     v8i q;
@@ -78,71 +76,6 @@ struct QuantTokensE8 {
   }
 };
 
-// bf16 tokens quantized on the fly, with the arithmetic of fp8_quant_act (so
-// the codes and scales are the same bits): group amax of |x| over the 128
-// channels of the K block (the four lane groups of a token hold 32 channels
-// each: two xor-shuffles), s = amax / 448 as an IEEE division, codes from
-// x * rcp(s) with the exact-division fallback near rounding midpoints.  Lane
-// group g holds channels [16g, 16g+16) and [64+16g, 64+16g+16), the fragment
-// layout of the MFMA operand.
-struct Bf16Tokens {
-  const uint16_t *x;
-  int K;
-  static constexpr bool kStaged = false, kE8 = false;
-  static constexpr int kRawRegs = 16;  // VGPRs per loaded K block
-  typedef float Scale;
-  struct Raw {
-    uint4 v[4];
-  };
-  __device__ __forceinline__ void stage(uint8_t *, int, int, int) {}
-  __device__ __forceinline__ Raw load(int m, int kb, int g) const {
-    const uint16_t *row = x + (int64_t)m * K + (int64_t)kb * kGroup;
-    Raw r;
-    r.v[0] = *reinterpret_cast<const uint4 *>(row + 16 * g);
-    r.v[1] = *reinterpret_cast<const uint4 *>(row + 16 * g + 8);
-    r.v[2] = *reinterpret_cast<const uint4 *>(row + 64 + 16 * g);
-    r.v[3] = *reinterpret_cast<const uint4 *>(row + 64 + 16 * g + 8);
-    return r;
-  }
-  __device__ __forceinline__ void make(const Raw &r, v8i &frag, float &s_out) const {
-    uint32_t w[16];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      w[4 * i] = r.v[i].x;
-      w[4 * i + 1] = r.v[i].y;
-      w[4 * i + 2] = r.v[i].z;
-      w[4 * i + 3] = r.v[i].w;
-    }
-    uint32_t amax_bits = 0;
-#pragma unroll
-    for (int i = 0; i < 16; i++)
-      amax_bits = max(amax_bits, max(bf16_abs_bits(w[i] & 0xFFFFu), bf16_abs_bits(w[i] >> 16)));
-    amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 16, 64));
-    amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 32, 64));
-    const float s = bf16_to_f32(amax_bits) / 448.0f;
-    const float rs = __builtin_amdgcn_rcpf(s);
-    uint32_t need = scale_fast_ok(s) ? 0u : 1u;
-    uint32_t packed[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const float v[4] = {bf16_to_f32(w[2 * i] & 0xFFFFu), __uint_as_float(w[2 * i] & 0xFFFF0000u),
-                          bf16_to_f32(w[2 * i + 1] & 0xFFFFu), __uint_as_float(w[2 * i + 1] & 0xFFFF0000u)};
-      packed[i] = quantize4_fast(v, rs, need);
-    }
-    if (__builtin_expect(need != 0u, 0)) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const float v[4] = {bf16_to_f32(w[2 * i] & 0xFFFFu), __uint_as_float(w[2 * i] & 0xFFFF0000u),
-                            bf16_to_f32(w[2 * i + 1] & 0xFFFFu), __uint_as_float(w[2 * i + 1] & 0xFFFF0000u)};
-        packed[i] = quantize4_exact(v, s);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; i++) frag[i] = (int)packed[i];
-    s_out = s;
-  }
-};
-
 // bf16 tokens quantized once per workgroup into LDS before the GEMM loop (for
 // small M, where M x K codes fit in LDS): 16 lanes per 1x128 group, the
 // arithmetic of fp8_quant_act (quantize_group16), codes [M][K] and scales
@@ -153,7 +86,6 @@ struct StagedTokens {
   uint8_t *codes;
   float *scales;
   static constexpr bool kStaged = true, kE8 = false;
-  static constexpr int kRawRegs = 9;
   typedef float Scale;
   struct Raw {
     v8i q;

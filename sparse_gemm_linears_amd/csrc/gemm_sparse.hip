@@ -302,10 +302,7 @@ static hipError_t launch_decode_for(X xop, const uint8_t *wv, const uint8_t *wm,
     if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wv, wm, ws, M, N, K, y, stream);
   if constexpr (CT <= 2)
     if (N >= 16384) return launch_decode<X, 4, CT, 8, 2>(xop, wv, wm, ws, M, N, K, y, stream);
-  // bf16 tokens take 16 registers per K block and token tile: one block in
-  // flight for the widest tile
-  constexpr int D2 = (CT == 4 && X::kRawRegs > 9) ? 1 : 2;
-  if (N >= 6144) return launch_decode<X, 2, CT, 8, D2>(xop, wv, wm, ws, M, N, K, y, stream);
+  if (N >= 6144) return launch_decode<X, 2, CT, 8, 2>(xop, wv, wm, ws, M, N, K, y, stream);
   return launch_decode<X, 1, CT, 8, 1>(xop, wv, wm, ws, M, N, K, y, stream);
 }
 
@@ -342,16 +339,16 @@ hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   return e;
 }
 
+// As the dense linear: in-kernel quantization for one or two tokens, else
+// fp8_quant_act into a pool workspace and fp8_sparse24_gemm.
 hipError_t launch_sparse_linear(const uint16_t *x, const uint8_t *wv, const uint8_t *wm, const float *ws, int64_t M,
                                 int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
-  if (use_tile_kernel(M, N, K))
-    return quantize_then(x, M, K, stream, [&](const uint8_t *xq, const float *xs) {
-      return launch_sparse_gemm(xq, xs, wv, wm, ws, M, N, K, y, stream);
-    });
-  if (staged_tokens_fit(M, K))
+  if (!use_tile_kernel(M, N, K) && staged_tokens_fit(M, K))
     return launch_sparse_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wv, wm, ws, (int)M, (int)N, (int)K, y,
                                 stream);
-  return launch_sparse_decode(Bf16Tokens{x, (int)K}, wv, wm, ws, (int)M, (int)N, (int)K, y, stream);
+  return quantize_then(x, M, K, stream, [&](const uint8_t *xq, const float *xs) {
+    return launch_sparse_gemm(xq, xs, wv, wm, ws, M, N, K, y, stream);
+  });
 }
 
 }  // namespace fp8lin
