@@ -8,22 +8,30 @@
  * torch.float8_e4m3fn.  Scales are fp32.  G = 128 is the group / block edge.
  *
  * Ownership: the caller allocates every input and output; the library keeps
- * no pointer after a call returns and no state between calls besides
- * per-device architecture and compute-unit counts.  Five calls may allocate,
- * from a stream-ordered memory pool the library creates once per device
- * (hipMallocFromPoolAsync on `stream`, released with hipFreeAsync on the same
- * stream after the kernels that use it; the pool keeps up to 256 MB cached
- * until the process ends):
+ * no pointer to them after a call returns.  Besides per-device architecture
+ * and compute-unit counts, it keeps scratch memory of its own for the calls
+ * that need one, until the process ends:
  *   fp8_block_gemm and fp8_sparse24_gemm on the tile kernel (M > 64, or
  *   M > 32 with N * K >= 2^25) with too few output tiles to cover half of the
- *   compute units split K, with an fp32 workspace of at most 256 tiles' worth
- *   (S * M * N * 4 bytes, S <= 16);
- *   fp8_block_linear and fp8_sparse24_linear with M > 32 and N * K >= 2^25
- *   quantize the tokens into a workspace (M * K + 4 * M * K / 128 bytes) and
- *   run the tile GEMM on them;
+ *   compute units split K, with S * M * N * 4 bytes of fp32 partials
+ *   (S <= 16, at most 256 tiles' worth);
+ *   fp8_block_linear and fp8_sparse24_linear from three tokens on quantize
+ *   the tokens into M * K + 4 * M * K / 128 bytes (and may split K as above);
  *   fp8_block_gemm_swiglu with few tokens keeps the fp32 partials of the
- *   stacked GEMM in a workspace.  Calls may be made from
- * several host threads on different streams.
+ *   stacked GEMM (S * M * 2I * 4 bytes).
+ * The scratch memory is held per device, stream and capture:
+ *   - outside stream capture, one buffer per stream, from a stream-ordered
+ *     pool the library creates once per device (hipMallocFromPoolAsync on
+ *     `stream`; a larger need frees the old buffer with hipFreeAsync on the
+ *     same stream first).  Calls on one stream share it, so calls on one
+ *     stream must be issued in order from one host thread at a time; calls
+ *     on different streams, from any threads, do not interact;
+ *   - under stream capture, buffers of the capture's own (hipMalloc, made
+ *     with the thread's capture mode relaxed for that call), kept until the
+ *     process ends because the graph holds their address: a replay shares
+ *     no scratch memory with eager calls or with other graphs, and may run on
+ *     any stream.  Past 1 GiB kept for captures, a capture allocates in the
+ *     graph instead (stream-ordered pool allocation and free nodes).
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (NULL = the default stream) and returns without
@@ -40,8 +48,8 @@
  *   FP8L_ERR_ALIAS   an output overlaps an input or another output;
  *   FP8L_ERR_DEVICE  the current HIP device is missing or is not gfx950;
  *   FP8L_ERR_LAUNCH  the kernel launch was rejected by the runtime;
- *   FP8L_ERR_MEMORY  the split-K workspace could not be allocated (no kernel
- *                    runs).
+ *   FP8L_ERR_MEMORY  scratch memory for the call could not be allocated (no
+ *                    kernel runs).
  * M == 0 (an empty batch) returns FP8L_OK without launching and without
  * looking at the M-sized buffers.  There is no fallback path: an unsupported
  * case is an error, never a silently slower kernel.
@@ -252,8 +260,8 @@ fp8l_status fp8_block_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uin
  * I must be a positive multiple of 128.  Prefill-sized M runs the fused
  * kernel (256-token tiles, SwiGLU and the quantization in the epilogue).
  * Where that grid would leave compute units idle (few tokens), the stacked
- * GEMM runs on smaller tiles and/or split K into fp32 partials held in a pool
- * workspace (S * M * 2I * 4 bytes), and one more kernel sums them and applies
+ * GEMM runs on smaller tiles and/or split K into fp32 partials held in library
+ * scratch memory (S * M * 2I * 4 bytes), and one more kernel sums them and applies
  * SwiGLU and the quantization with the same arithmetic.
  */
 fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
@@ -276,7 +284,7 @@ fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint
  * in 36 KB of LDS) are quantized inside the weight-streaming kernel: every
  * workgroup quantizes the tokens into LDS and the codes are never written out.
  * Otherwise, where re-quantizing in every workgroup would cost more than it
- * saves, the call is those two calls, with the codes in a pool workspace.
+ * saves, the call is those two calls, with the codes in library scratch memory.
  * M > 64 is FP8L_ERR_SHAPE: for a larger batch, quantize it once with
  * fp8_quant_act and call fp8_block_gemm.
  * Measured on MI355X (Llama-3-8B shapes, HIP graphs), one or two tokens save

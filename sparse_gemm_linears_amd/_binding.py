@@ -232,8 +232,8 @@ def fp8_sparse24_gemm(xq, xs, wvals, wmeta, ws, y: torch.Tensor | None = None):
 
 
 def fp8_block_linear(x, wq, ws, y: torch.Tensor | None = None):
-    """(x [M,K] bf16 with M <= 64, wq [N,K], ws [N/128,K/128]) -> y [M,N] bf16; the activations are
-    quantized inside the kernel (bit-identical to fp8_quant_act followed by fp8_block_gemm)."""
+    """(x [M,K] bf16 with M <= 64, wq [N,K], ws [N/128,K/128]) -> y [M,N] bf16, bit-identical to fp8_quant_act
+    followed by fp8_block_gemm (one or two tokens are quantized inside the GEMM kernel)."""
     wq = _codes(wq)
     _want(x, "x", torch.bfloat16)
     _want(wq, "wq", torch.uint8)

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libfp8lin.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "quant.hip", "prune24.hip", "gemm_dense.hip", "gemm_sparse.hip"]
+SOURCES = ["api.hip", "quant.hip", "prune24.hip", "gemm_dense.hip", "gemm_sparse.hip", "workspace.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -297,7 +297,7 @@ const char *fp8lin_status_str(fp8l_status status) {
     case FP8L_ERR_ALIAS: return "an output overlaps an input or another output";
     case FP8L_ERR_DEVICE: return "no gfx950 (MI355X) device is current";
     case FP8L_ERR_LAUNCH: return "kernel launch failed";
-    case FP8L_ERR_MEMORY: return "the split-K workspace could not be allocated";
+    case FP8L_ERR_MEMORY: return "scratch memory for the call could not be allocated";
     default: return "unknown status";
   }
 }

@@ -15,8 +15,6 @@
 //    registers, the waves of a workgroup split K and meet in LDS at the end.
 #include <algorithm>
 #include <atomic>
-#include <cstring>
-#include <mutex>
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -479,46 +477,6 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint1
 
 // ================================================================ dispatch ==
 
-// Split-K workspace: one library-owned stream-ordered memory pool per device,
-// keeping up to 256 MB cached between calls (the default pool hands memory
-// back to the driver at every synchronisation, so each step of an inference
-// loop would pay a fresh allocation).
-static hipError_t workspace_pool(hipMemPool_t *out) {
-  constexpr int kMaxDevices = 64;
-  static std::mutex mu;
-  static hipMemPool_t pools[kMaxDevices] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!pools[dev]) {
-    hipMemPoolProps props;
-    std::memset(&props, 0, sizeof(props));
-    props.allocType = hipMemAllocationTypePinned;
-    props.handleTypes = hipMemHandleTypeNone;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = dev;
-    hipMemPool_t pool = nullptr;
-    if ((e = hipMemPoolCreate(&pool, &props)) != hipSuccess) return e;
-    uint64_t keep = uint64_t(256) << 20;
-    if ((e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
-      (void)hipMemPoolDestroy(pool);
-      return e;
-    }
-    pools[dev] = pool;
-  }
-  *out = pools[dev];
-  return hipSuccess;
-}
-
-hipError_t workspace_alloc(float **p, size_t bytes, hipStream_t stream) {
-  hipMemPool_t pool;
-  const hipError_t e = workspace_pool(&pool);
-  if (e != hipSuccess) return e;
-  return hipMallocFromPoolAsync(reinterpret_cast<void **>(p), bytes, pool, stream);
-}
-
 // Compute units of the current device (cached per device).
 int device_cu_count() {
   constexpr int kMaxDevices = 64;
@@ -593,11 +551,13 @@ template <bool E8, class S>
 static hipError_t tile_gemm(const uint8_t *xq, const S *xs, const uint8_t *wq, const S *ws, int m, int n, int k,
                             uint16_t *y, hipStream_t stream) {
   const TilePlan p = plan_tiles(m, n, k, device_cu_count());
-  float *part = nullptr;
+  Workspace scratch;
   if (p.splits > 1) {
-    const hipError_t e = workspace_alloc(&part, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
+    const hipError_t e =
+        workspace_acquire(&scratch, kSlotPartials, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
     if (e != hipSuccess) return e;
   }
+  float *part = static_cast<float *>(scratch.p);
   hipError_t e =
       p.bm == 128
           ? launch_tile<256, 128, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
@@ -605,7 +565,7 @@ static hipError_t tile_gemm(const uint8_t *xq, const S *xs, const uint8_t *wq, c
   // (part is NULL when splits == 1: launch_tile then writes y)
   if (p.splits > 1) {
     if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
-    const hipError_t f = hipFreeAsync(part, stream);
+    const hipError_t f = workspace_release(&scratch);
     if (e == hipSuccess) e = f;
   }
   return e;
@@ -663,9 +623,11 @@ hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const ui
   if (p.bm != 256 || p.splits > 1) {
     // few output tiles: the tile GEMM of the stacked weight into fp32 partials
     // (K split as planned), then SwiGLU and the quantization in one pass
-    float *part = nullptr;
-    hipError_t e = workspace_alloc(&part, (size_t)p.splits * (size_t)m * (size_t)n2 * sizeof(float), stream);
+    Workspace scratch;
+    hipError_t e =
+        workspace_acquire(&scratch, kSlotPartials, (size_t)p.splits * (size_t)m * (size_t)n2 * sizeof(float), stream);
     if (e != hipSuccess) return e;
+    float *part = static_cast<float *>(scratch.p);
     e = p.bm == 128
             ? launch_tile<256, 128, 2, 4, false>(xq, xs, wq, ws, m, n2, k, nullptr, p.splits, p.kb_split, part, stream)
             : launch_tile<256, 256, 2, 4, false>(xq, xs, wq, ws, m, n2, k, nullptr, p.splits, p.kb_split, part, stream);
@@ -675,7 +637,7 @@ hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const ui
                          p.splits, m, (int)I, h, hq, hs);
       e = hipGetLastError();
     }
-    const hipError_t f = hipFreeAsync(part, stream);
+    const hipError_t f = workspace_release(&scratch);
     return e == hipSuccess ? f : e;
   }
   const int tiles_m = (m + 255) / 256, tiles_n = (int)(I / 128);
@@ -713,7 +675,7 @@ hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const u
 }
 
 // One or two tokens: quantized inside the decode kernel (StagedTokens).  More:
-// fp8_quant_act into a pool workspace, then fp8_block_gemm (measured faster
+// fp8_quant_act into library scratch memory, then fp8_block_gemm (measured faster
 // from three tokens on: every decode workgroup would re-quantize all M x K).
 hipError_t launch_dense_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
                                int64_t K, uint16_t *y, hipStream_t stream) {

@@ -323,24 +323,26 @@ hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   const int m = (int)M, n = (int)N, k = (int)K;
   if (!use_tile_kernel(m, n, k)) return launch_sparse_decode(QuantTokens{xq, xs, k}, wv, wm, ws, m, n, k, y, stream);
   const TilePlan p = plan_tiles(m, n, k, device_cu_count());
-  float *part = nullptr;
+  Workspace scratch;
   if (p.splits > 1) {
-    const hipError_t e = workspace_alloc(&part, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
+    const hipError_t e =
+        workspace_acquire(&scratch, kSlotPartials, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
     if (e != hipSuccess) return e;
   }
+  float *part = static_cast<float *>(scratch.p);
   hipError_t e = p.bm == 128
                      ? launch_tile<256, 128, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
                      : launch_tile<256, 256, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
   if (p.splits > 1) {
     if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
-    const hipError_t f = hipFreeAsync(part, stream);
+    const hipError_t f = workspace_release(&scratch);
     if (e == hipSuccess) e = f;
   }
   return e;
 }
 
 // As the dense linear: in-kernel quantization for one or two tokens, else
-// fp8_quant_act into a pool workspace and fp8_sparse24_gemm.
+// fp8_quant_act into library scratch memory and fp8_sparse24_gemm.
 hipError_t launch_sparse_linear(const uint16_t *x, const uint8_t *wv, const uint8_t *wm, const float *ws, int64_t M,
                                 int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   if (!use_tile_kernel(M, N, K) && staged_tokens_fit(M, K))

@@ -27,24 +27,35 @@ inline bool use_tile_kernel(int64_t M, int64_t N, int64_t K) {
   return M > 64 || (M > 32 && N * K >= (int64_t(1) << 25));
 }
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
-// Stream-ordered workspace from the library's per-device pool; released with
-// hipFreeAsync on the same stream.
-hipError_t workspace_alloc(float **p, size_t bytes, hipStream_t stream);
+// Library-owned scratch memory for the work a call puts on `stream`: kept
+// between calls per (device, stream, slot), and per capture for calls under
+// stream capture (a captured graph keeps its own).  Calls on one stream share
+// it, so they must be issued in stream order (not from several host threads
+// at once on one stream).  workspace_release returns it (a no-op unless the
+// memory was a one-off allocation).
+enum WorkspaceSlot { kSlotPartials = 0, kSlotTokens = 1 };
+struct Workspace {
+  void *p = nullptr;
+  hipStream_t stream = nullptr;
+  bool transient = false;
+};
+hipError_t workspace_acquire(Workspace *w, WorkspaceSlot slot, size_t bytes, hipStream_t stream);
+hipError_t workspace_release(Workspace *w);
 
-// Tokens quantized into a workspace from the library pool, then the GEMM on
-// them: exactly fp8_quant_act followed by gemm(xq, xs).
+// Tokens quantized into library scratch memory, then the GEMM on them: exactly
+// fp8_quant_act followed by gemm(xq, xs).
 template <class Gemm>
 inline hipError_t quantize_then(const uint16_t *x, int64_t M, int64_t K, hipStream_t stream, Gemm gemm) {
   const size_t q_bytes = ((size_t)M * (size_t)K + 255) / 256 * 256;
   const size_t s_bytes = (size_t)M * (size_t)(K / 128) * sizeof(float);
-  float *ws_mem = nullptr;
-  hipError_t e = workspace_alloc(&ws_mem, q_bytes + s_bytes, stream);
+  Workspace ws;
+  hipError_t e = workspace_acquire(&ws, kSlotTokens, q_bytes + s_bytes, stream);
   if (e != hipSuccess) return e;
-  uint8_t *xq = reinterpret_cast<uint8_t *>(ws_mem);
+  uint8_t *xq = static_cast<uint8_t *>(ws.p);
   float *xs = reinterpret_cast<float *>(xq + q_bytes);
   e = launch_quant_act(x, M, K, xq, xs, stream);
   if (e == hipSuccess) e = gemm(xq, xs);
-  const hipError_t f = hipFreeAsync(ws_mem, stream);
+  const hipError_t f = workspace_release(&ws);
   return e == hipSuccess ? f : e;
 }
 
