@@ -131,18 +131,76 @@ __device__ __forceinline__ uint32_t amax8_bits(const uint4 &raw) {
   return a;
 }
 
-// One 1x128 activation group held by 16 consecutive lanes, 8 bf16 values
-// (16 bytes) per lane: returns this lane's 8 codes and the group scale.  The
-// group amax is an integer max over |bf16| bit patterns, shuffled across the
-// 16 lanes (all 16 must be active); s = amax / 448 as an IEEE division; codes
-// by the fast quotient with the exact-division fallback.
-__device__ __forceinline__ uint2 quantize_group16(const uint4 &raw, float &s_out) {
-  uint32_t amax_bits = amax8_bits(raw);
+// Scale of a group whose largest magnitude amax is a bf16 value (given as
+// fp32 bits): s = amax / 448 and rs = 1 / s, both IEEE divisions.  For
+// 2^-90 <= amax < inf the e4m3 code of fl(x / s), for every bf16 x with
+// |x| <= amax, equals the code of the quotient corrected once by FMA,
+//   q0 = fl(x rs),  q = fl(q0 - fl(q0 s - x) rs)
+// (fused operations; an exhaustive check over every such pair of bf16 amax
+// and x, both signs; q itself can be one ulp off fl(x / s), but never next
+// to an e4m3 rounding midpoint).  The remainder is taken as q0 s - x, not
+// x - q0 s, so that x = -0 gives -0 (the other form gives +0 - 0 = +0).
+// Below 2^-90 the remainder can underflow and the codes differ in a few
+// cases, so zero, tiny and non-finite amax take the IEEE divisions.
+struct GroupScale {
+  float s, rs;
+  bool fast;
+};
+
+__device__ __forceinline__ GroupScale group_scale(uint32_t amax_f32_bits) {
+  GroupScale g;
+  g.s = __uint_as_float(amax_f32_bits) / 448.0f;
+  g.rs = 1.0f / g.s;
+  g.fast = amax_f32_bits >= 0x12800000u && amax_f32_bits < 0x7F800000u;
+  return g;
+}
+
+// Codes of four values of a group with g.fast set (see group_scale).
+__device__ __forceinline__ uint32_t quantize4_corrected(const float (&x)[4], const GroupScale &g) {
+  float q[4];
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 16));
-  const float sc = bf16_to_f32(amax_bits) / 448.0f;
-  s_out = sc;
-  return quantize8_scaled(raw, sc);
+  for (int j = 0; j < 4; j++) {
+    const float q0 = x[j] * g.rs;
+    const float r = __builtin_fmaf(q0, g.s, -x[j]);  // rounded, then negated as an operand
+    q[j] = __builtin_fmaf(-r, g.rs, q0);
+  }
+  return e4m3_pack4(q[0], q[1], q[2], q[3]);
+}
+
+// Codes of four values of a group: corrected quotients, or the IEEE
+// divisions when the scale is outside the checked range.
+__device__ __forceinline__ uint32_t quantize4_group(const float (&x)[4], const GroupScale &g) {
+  return g.fast ? quantize4_corrected(x, g) : quantize4_exact(x, g.s);
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in every lane
+// of the row: two quad permutations, then rotations of the row by 4 and 8.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
+  return v;
+}
+
+// One 1x128 activation group held by 16 consecutive lanes (one DPP row; all
+// 16 active), 8 bf16 values (16 bytes) per lane: returns this lane's 8 codes
+// and the group scale.  The group amax is an integer max over |bf16| bit
+// patterns; s = amax / 448 as an IEEE division; codes as in group_scale.
+__device__ __forceinline__ uint2 quantize_group16(const uint4 &raw, float &s_out) {
+  const GroupScale g = group_scale(row16_max(amax8_bits(raw)) << 16);
+  s_out = g.s;
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    v[i][0] = bf16_to_f32(w[2 * i] & 0xFFFFu);
+    v[i][1] = __uint_as_float(w[2 * i] & 0xFFFF0000u);
+    v[i][2] = bf16_to_f32(w[2 * i + 1] & 0xFFFFu);
+    v[i][3] = __uint_as_float(w[2 * i + 1] & 0xFFFF0000u);
+  }
+  if (__builtin_expect(g.fast, 1)) return make_uint2(quantize4_corrected(v[0], g), quantize4_corrected(v[1], g));
+  return make_uint2(quantize4_exact(v[0], g.s), quantize4_exact(v[1], g.s));
 }
 
 // v_mfma_f32_16x16x128_f8f6f4 with both operands e4m3 and no block scale.

@@ -103,21 +103,13 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *x
           for (int e = 0; e < 4; e++) amax_bits = max(amax_bits, __float_as_uint(hv[r][e]) & 0x7FFFFFFFu);
         amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 16, 64));
         amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 32, 64));
-        const float sc = __uint_as_float(amax_bits) / 448.0f;
-        const float rs = __builtin_amdgcn_rcpf(sc);
-        uint32_t need = scale_fast_ok(sc) ? 0u : 1u;
+        const GroupScale gs = group_scale(amax_bits);
+        const float sc = gs.s;
         uint32_t words[C::RT];
 #pragma unroll
         for (int r = 0; r < C::RT; r++) {
           const float v[4] = {hv[r][0], hv[r][1], hv[r][2], hv[r][3]};
-          words[r] = quantize4_fast(v, rs, need);
-        }
-        if (__builtin_expect(need != 0u, 0)) {
-#pragma unroll
-          for (int r = 0; r < C::RT; r++) {
-            const float v[4] = {hv[r][0], hv[r][1], hv[r][2], hv[r][3]};
-            words[r] = quantize4_exact(v, sc);
-          }
+          words[r] = quantize4_group(v, gs);
         }
         // codes through the wave's LDS scratch (16 rows x 128 bytes, 16-byte
         // chunks XOR-swizzled by row) so that each row goes out as 128

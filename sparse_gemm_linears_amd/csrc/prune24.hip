@@ -98,18 +98,14 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
   if ((t & 63) == 0) wave_max[t >> 6] = amax_bits;
   __syncthreads();
   amax_bits = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
-  const float sc = __uint_as_float(amax_bits) / 448.0f;
-  const float rs = __builtin_amdgcn_rcpf(sc);
-  const bool ok = scale_fast_ok(sc);
-  if (t == 0) s[(int64_t)nb * KB + kb] = sc;
+  const GroupScale g = group_scale(amax_bits);
+  if (t == 0) s[(int64_t)nb * KB + kb] = g.s;
 
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const int64_t n = row0 + 16 * i;
     const float kv[4] = {kept[i][0].first, kept[i][0].second, kept[i][1].first, kept[i][1].second};
-    uint32_t need = ok ? 0u : 1u;
-    uint32_t word = quantize4_fast(kv, rs, need);
-    if (__builtin_expect(need != 0u, 0)) word = quantize4_exact(kv, sc);
+    const uint32_t word = quantize4_group(kv, g);
     *reinterpret_cast<uint32_t*>(vals + n * (K / 2) + kcol / 2) = word;
     // the 16 lanes of a row segment hold its 16 consecutive meta bytes: every
     // fourth lane gathers four of them for one 4-byte store

@@ -1,8 +1,9 @@
 // Activation (per-token 1x128) and weight (128x128 block) e4m3 quantizers.
 //
 // Both are HBM-bound streaming kernels: 16-byte loads of bf16, the group /
-// block maximum of |x| by cross-lane and LDS reductions, one IEEE fp32
-// division per element, integer RNE encoding, packed stores.
+// block maximum of |x| by cross-lane and LDS reductions, the quotient x / s
+// by a multiply and two FMAs (group_scale), hardware RNE encoding, packed
+// stores.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -59,10 +60,8 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(const uint16_t* __res
   if ((t & 63) == 0) wave_max[t >> 6] = amax_bits;
   __syncthreads();
   amax_bits = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
-  const float sc = bf16_to_f32(amax_bits) / 448.0f;
-  const float rs = __builtin_amdgcn_rcpf(sc);
-  const bool ok = scale_fast_ok(sc);
-  if (t == 0) s[(int64_t)nb * KB + kb] = sc;
+  const GroupScale g = group_scale(amax_bits << 16);
+  if (t == 0) s[(int64_t)nb * KB + kb] = g.s;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     float v[2][4];
@@ -74,15 +73,8 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(const uint16_t* __res
       v[h][2] = bf16_to_f32(hi & 0xFFFFu);
       v[h][3] = __uint_as_float(hi & 0xFFFF0000u);
     }
-    uint32_t need = ok ? 0u : 1u;
-    uint32_t packed[2];
-#pragma unroll
-    for (int h = 0; h < 2; h++) packed[h] = quantize4_fast(v[h], rs, need);
-    if (__builtin_expect(need != 0u, 0)) {
-#pragma unroll
-      for (int h = 0; h < 2; h++) packed[h] = quantize4_exact(v[h], sc);
-    }
-    *reinterpret_cast<uint2 *>(q + base + (int64_t)i * 16 * K) = make_uint2(packed[0], packed[1]);
+    *reinterpret_cast<uint2 *>(q + base + (int64_t)i * 16 * K) =
+        make_uint2(quantize4_group(v[0], g), quantize4_group(v[1], g));
   }
 }
 
