@@ -44,6 +44,7 @@ struct SparseTile {
   static constexpr int kVTile = BN * 64, kMTile = BN * 16, kBTile = BM * 128;
   static_assert(BN % (16 * kWaves) == 0 && BM % (8 * kWaves) == 0 && kMCopyWaves <= kWaves, "tile mismatch");
   static_assert(kWaves % 2 == 0, "copy slabs alternate 16-row parity per wave");
+  static_assert(kWaves * 16 == 128 && BN == 256, "one value slab of every wave is one 128-row panel half");
   static_assert(kWaveN == 128, "a wave covers one 128-row weight scale block (and 256-byte epilogue rows)");
   static_assert(BM <= kThreads, "one thread per token scale");
   static_assert(kWaves * 4096 <= 2 * kBTile && kBTile % 4096 == 0, "epilogue scratch fits in the token stages");
@@ -95,20 +96,26 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
   const int m_base = tm * BM, n_base = tn * BN;
   const int wn0 = (wave / WM) * C::kWaveN, wm0 = (wave % WM) * C::kWaveM;
 
-  // value copies: slab i covers rows r0 = (i*kWaves + wave)*16 .. +15, lane l
-  // writes chunk position l%4 of row r0 + l/4 (logical chunk (l%4) ^ vswz(row))
+  // Copies through buffer resources over 128-row panel halves (rows past the
+  // matrix edge read as zeros; their outputs are never stored), with one
+  // per-lane offset per panel and the K block and half-panel row in the
+  // scalar offset, so walking K costs no VALU.
+  //  values: slab i covers rows r0 = (i*kWaves + wave)*16 .. +15 (half i*16*kWaves/128);
+  //    lane l writes chunk position l%4 of row r0 + l/4 (logical chunk (l%4) ^ vswz(row));
+  //  index words: one 64-row slab per wave for waves < kMCopyWaves;
+  //  tokens: slab i covers rows (i*kWaves + wave)*8 .. +7, as in the dense kernel.
   const int vrow_in_slab = lane >> 2, vpos = lane & 3;
-  const uint32_t v_lane = (uint32_t)(vrow_in_slab * vrow_bytes + 16 * (vpos ^ vswz(vrow_in_slab)));
-  // index-word copies: one 64-row slab per wave for waves < kMCopyWaves
-  const uint32_t m_lane = (uint32_t)(lane * mrow_bytes);
-  // token copies as in the dense kernel
-  const int copy_chunk = 16 * (cp ^ swz(cj + 8 * (wave & 1)));
-  uint32_t b_lane[C::kBCopies];
-#pragma unroll
-  for (int i = 0; i < C::kBCopies; i++) {
-    const int r0 = m_base + (i * C::kWaves + wave) * 8;
-    b_lane[i] = (uint32_t)((min(r0 + cj, M - 1) - min(r0, M - 1)) * K + copy_chunk);
-  }
+  const uint32_t v_voff =
+      (uint32_t)((wave * 16 + vrow_in_slab) * vrow_bytes + 16 * (vpos ^ vswz(vrow_in_slab)));
+  const uint32_t m_voff = (uint32_t)(((wave % 2) * 64 + lane) * mrow_bytes);
+  const uint32_t b_voff = (uint32_t)((wave * 8 + cj) * K + 16 * (cp ^ swz(cj + 8 * (wave & 1))));
+  const uint8_t *vpanel = wv + (int64_t)n_base * vrow_bytes, *mpanel = wm + (int64_t)n_base * mrow_bytes;
+  const uint8_t *xpanel = xq + (int64_t)m_base * K;
+  const rsrc_t rv0 = panel_rows128(vpanel, N - n_base, 0, (int)vrow_bytes);
+  const rsrc_t rv1 = panel_rows128(vpanel, N - n_base, 128, (int)vrow_bytes);
+  const rsrc_t rm0 = panel_rows128(mpanel, N - n_base, 0, (int)mrow_bytes);
+  const rsrc_t rm1 = panel_rows128(mpanel, N - n_base, 128, (int)mrow_bytes);
+  const rsrc_t rx0 = panel_rows128(xpanel, M - m_base, 0, K), rx1 = panel_rows128(xpanel, M - m_base, 128, K);
   TokenScales<BM, SB> scales;
   scales.init(lds_s, xs, M, KBs, m_base, tid);
 
@@ -116,20 +123,17 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
   // (waves below kMCopyWaves), then the token panel
   auto issue_copy = [&](int kb, int st, int j) {
     if (j < C::kVCopies) {
-      const int r0 = (j * C::kWaves + wave) * 16;
-      const uint8_t *base = wv + (int64_t)min(n_base + r0, N - 16) * vrow_bytes + (int64_t)kb * 64;
-      copy16_global_to_lds(base + v_lane, (st ? lds_v1 : lds_v0) + r0 * 64);
+      const int r0 = (j * C::kWaves + wave) * 16;  // rows j*128 + 16*wave .. +15: half j of the panel
+      const uint32_t soff = (uint32_t)kb * 64u + (uint32_t)((j * C::kWaves * 16) % 128) * (uint32_t)vrow_bytes;
+      buffer_copy16_to_lds((j * C::kWaves * 16) < 128 ? rv0 : rv1, v_voff, soff, (st ? lds_v1 : lds_v0) + r0 * 64);
     } else if (j == C::kVCopies) {
-      if (wave < C::kMCopyWaves) {
-        const int r0 = wave * 64;
-        const uint8_t *base = wm + (int64_t)min(n_base + r0, N - 64) * mrow_bytes + (int64_t)kb * 16;
-        copy16_global_to_lds(base + m_lane, (st ? lds_m1 : lds_m0) + r0 * 16);
-      }
+      if (wave < C::kMCopyWaves)
+        buffer_copy16_to_lds(wave < 2 ? rm0 : rm1, m_voff, (uint32_t)kb * 16u, (st ? lds_m1 : lds_m0) + wave * 64 * 16);
     } else {
       const int i = j - C::kVCopies - 1;
-      const int r0 = (i * C::kWaves + wave) * 8;
-      const uint8_t *base = xq + (int64_t)min(m_base + r0, M - 1) * K + (int64_t)kb * kGroup;
-      copy16_global_to_lds(base + b_lane[i], (st ? lds_b1 : lds_b0) + r0 * 128);
+      const int first = i * C::kWaves * 8;  // panel row of wave 0's slab
+      const uint32_t soff = (uint32_t)kb * 128u + (uint32_t)(first % 128) * (uint32_t)K;
+      buffer_copy16_to_lds(first < 128 ? rx0 : rx1, b_voff, soff, (st ? lds_b1 : lds_b0) + (first + wave * 8) * 128);
     }
   };
   constexpr int kCopies = C::kVCopies + 1 + C::kBCopies;
@@ -154,13 +158,28 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
 
   const int nb_wave = min((n_base + wn0) / kGroup, NB - 1);
   const float *ws_row = ws + (int64_t)nb_wave * KBs + kb0;
+  // the weight scale of the next step is loaded during this one, as a vector
+  // (buffer) load counted with the copies: a scalar load can return out of
+  // order, and while one is pending every LDS wait would have to drain all
+  // LDS reads in flight
+  const rsrc_t rws = make_rsrc(ws_row, (uint32_t)KB * 4u);
+  float sw_cur = ws_row[0];
 
   auto step = [&](int kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     const bool more = kb + 1 < KB;
     const bool scale_load = (kb % SB == 0) && (kb + SB < KB);
     if (scale_load) scales.load(kb / SB + 1);
-    const float sw = ws_row[kb];
+    const float sw = sw_cur;
+    const float sw_next = more ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                     rws, 0, (uint32_t)(kb + 1) * 4u, 0))
+                               : 0.f;
+    // the first row's weight fragment first: the first MFMAs wait only for it
+    // and the token fragments they use
+    const uint8_t *Vt = ST ? lds_v1 : lds_v0;
+    const uint8_t *Mt = ST ? lds_m1 : lds_m0;
+    v4i af_next = make_v4i(*reinterpret_cast<const uint4 *>(Vt + v_off));
+    int ix_next = *reinterpret_cast<const int *>(Mt + m_off);
     v8i bf[C::CT];
     float scl[C::CT];
 #pragma unroll
@@ -168,10 +187,6 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
       bf[c] = load_frag_at(ST ? lds_b1 : lds_b0, b_lo, b_hi, c * 2048);
       scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
     }
-    const uint8_t *Vt = ST ? lds_v1 : lds_v0;
-    const uint8_t *Mt = ST ? lds_m1 : lds_m0;
-    v4i af_next = make_v4i(*reinterpret_cast<const uint4 *>(Vt + v_off));
-    int ix_next = *reinterpret_cast<const int *>(Mt + m_off);
     v4f p_prev[C::CT];
 #pragma unroll
     for (int r = 0; r < C::RT; r++) {
@@ -204,8 +219,11 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
       acc[C::RT - 1][c] += scl[c] * p_prev[c];
       pin(acc[C::RT - 1][c]);
     }
-    if (more || scale_load) wait_global_loads();
+    // copies, token scales and the next weight scale have landed (vmcnt and
+    // lgkmcnt drained: the LDS reads of this step are all consumed by now)
+    if (more || scale_load) __builtin_amdgcn_s_waitcnt(0x0070);
     if (scale_load) scales.store(kb / SB + 1);
+    sw_cur = sw_next;
     __syncthreads();
   };
 
