@@ -248,6 +248,14 @@ __device__ __forceinline__ void store_token_tile_f32(const v4f (&acc_c)[RT], flo
 // contiguous range of logical tile ids; the logical order then walks groups of
 // `group_m` token tiles column by column, so an XCD's concurrent tiles share
 // weight and activation panels in its L2.
+// Whether workgroup b has a logical tile when only `total` tiles exist (a grid
+// of at least `total` workgroups; the rest return): XCD x takes the first
+// total / 8 (+1 for x < total % 8) of its workgroups b = x, x + 8, ...
+__device__ __forceinline__ bool tile_slot_used(int b, int total) {
+  const int q = total / 8, r = total % 8;
+  return b / 8 < q + (b % 8 < r ? 1 : 0);
+}
+
 __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
   const int total = tiles_m * tiles_n;
   const int q = total / 8, r = total % 8;

@@ -138,9 +138,10 @@ __device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *x
 // and up rows I + 128 tn .. into the second; y is h [M,I].
 // E8: UE8M0 scales (xs, ws are exponent bytes) applied by the MFMA's block
 // scaling, accumulating straight into the accumulators with no VALU work.
-// GROUPED: tiles_m counts token tiles over all groups (an upper bound: the
-// sum of ceil(rows_g / BM) <= ceil(M / BM) + G); a workgroup whose tile lies
-// past the last group's returns at once.
+// GROUPED: tiles_m bounds the token tiles over all groups (the sum of
+// ceil(rows_g / BM) <= ceil(M / BM) + G); the tiles that exist are counted
+// from the offsets and ordered as in the plain kernel, and the workgroups
+// beyond them return at once.
 // PARTIAL: split K over blockIdx.y (so.kb_split K blocks each, a multiple of
 // SB) and store unrounded fp32 partial tiles instead of y.
 template <int BN, int BM, int WN, int WM, int SB, int CR, bool SWIGLU, bool E8 = false, bool GROUPED = false,
@@ -169,8 +170,21 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
     KB = min(so.kb_split, KBs - kb0);
   }
 
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+  int tm, tn, tiles_m_used = tiles_m;
+  if constexpr (GROUPED) {
+    // the launch covers the worst case; the tile order (and its split over the
+    // XCDs) covers only the token tiles that exist, so that the surplus
+    // workgroups, which return at once, are spread over every XCD instead of
+    // taking whole XCDs at the end of the order
+    int real = 0;
+    for (int q = 0; q < so.G; q++) {
+      const int o0 = min(max(so.offsets[q], 0), M_all), o1 = min(max(so.offsets[q + 1], o0), M_all);
+      real += (o1 - o0 + BM - 1) / BM;
+    }
+    tiles_m_used = __builtin_amdgcn_readfirstlane(min(real, tiles_m));
+    if (!tile_slot_used(blockIdx.x, tiles_m_used * tiles_n)) return;  // uniform: before any barrier
+  }
+  tile_coords(blockIdx.x, tiles_m_used, tiles_n, group_m, tm, tn);
   tm = __builtin_amdgcn_readfirstlane(tm);
   tn = __builtin_amdgcn_readfirstlane(tn);
   // token rows [m_base, M) of this tile and its weight
