@@ -40,8 +40,8 @@ CALIB_BYTES = 256 << 20    # size of the traffic-calibration copy
 # fp8_block_gemm_gate_up_m4096_traffic.md has the commands and the readings),
 # each scaled by the same counter's reading for the calibration copy.  It is
 # reported only while the kernel's sources hash to the value it was taken on.
-TRAFFIC = {"bytes_per_launch": 941574572,
-           "sources_sha256": "fe60c20e9180df3fbbcbef634fb3fed161bf4a637d0cd0531926c5cbf8ff0948"}
+TRAFFIC = {"bytes_per_launch": 941600436,
+           "sources_sha256": "6089d2b658435f125617568368c76e8f5ce8e9c52f255c89a554f6206e5781ac"}
 TRAFFIC_SOURCES = ("sparse_gemm_linears_amd/csrc/gemm_dense.hip", "sparse_gemm_linears_amd/csrc/gemm_common.hpp",
                    "sparse_gemm_linears_amd/csrc/device_common.hpp")
 
@@ -164,12 +164,17 @@ def main():
     dom_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in dom_ev]))
 
     # ----------------------------------- per-kernel times (HIP events) ------
+    # Steps back to back with one synchronisation at the end, so that the GPU
+    # is always behind the host and an event pair brackets only its kernel;
+    # the first step (which starts on an idle stream, with the host's launch
+    # latency inside its first pair) is dropped.
     durations = {(li, ki): [] for li in range(len(layers)) for ki in range(len(kernels))}
-    for _ in range(args.steps):
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in kernels] for _ in layers]
+    evs = [[[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in kernels] for _ in layers] for _ in range(args.steps + 1)]
+    for ev in evs:
         step(ev)
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    for ev in evs[1:]:
         for li in range(len(layers)):
             for ki in range(len(kernels)):
                 durations[(li, ki)].append(ev[li][ki][0].elapsed_time(ev[li][ki][1]) * 1e3)  # us
