@@ -127,11 +127,13 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
     const float kv[4] = {kept[i][0].first, kept[i][0].second, kept[i][1].first, kept[i][1].second};
     const uint32_t word = quantize4_group(kv, g);
     *reinterpret_cast<uint32_t*>(vals + n * (K / 2) + kcol / 2) = word;
-    // the 16 lanes of a row segment hold its 16 consecutive meta bytes: every
-    // fourth lane gathers four of them for one 4-byte store
+    // the 16 lanes of a row segment hold its 16 consecutive meta bytes: the
+    // first lane of each quad gathers the bytes of lanes 1, 2, 3 of its quad
+    // (DPP quad broadcasts) for one 4-byte store
     const uint32_t mb = kept[i][0].nib | (kept[i][1].nib << 4);
-    const uint32_t m4 = mb | ((uint32_t)__shfl_down((int)mb, 1, 16) << 8) |
-                        ((uint32_t)__shfl_down((int)mb, 2, 16) << 16) | ((uint32_t)__shfl_down((int)mb, 3, 16) << 24);
+    const uint32_t m4 = mb | ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x55, 0xF, 0xF, false) << 8) |
+                        ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xAA, 0xF, 0xF, false) << 16) |
+                        ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xFF, 0xF, 0xF, false) << 24);
     if ((t & 3) == 0) *reinterpret_cast<uint32_t*>(meta + n * (K / 8) + kcol / 8) = m4;
   }
 }
