@@ -2,9 +2,10 @@
 linear calls, SwiGLU partials), kept between calls per stream and per capture.
 Calls whose needs grow on a fresh stream with no synchronisation between them,
 calls on two streams at once, a graph replayed on one stream while the same
-calls run eagerly on another, and two graphs captured on one stream replayed
-on two streams at once: every output equals that of the call run alone, bit
-for bit (the calls themselves are checked against the oracle elsewhere)."""
+calls run eagerly on another, two graphs captured on one stream replayed on
+two streams at once, and captures past the memory kept for captures: every
+output equals that of the call run alone, bit for bit (the calls themselves
+are checked against the oracle elsewhere)."""
 from __future__ import annotations
 
 import pytest
@@ -167,3 +168,33 @@ def test_two_graphs_from_one_stream_replayed_at_once(gpu_lib, setup):
         torch.cuda.synchronize()
         check(a, refs, f"graph a, replay {i}")
         check(b, refs, f"graph b, replay {i}")
+
+
+def test_captures_past_the_kept_limit(gpu_lib, setup):
+    """Captures keep their scratch memory (up to 1 GiB in all); past that a
+    capture allocates inside its graph instead.  Forty captures of a split-K
+    GEMM needing 33.5 or 67 MB each (down projection, 256 tokens: 8 or 16
+    splits of 256 x 4096 fp32, by the tile height chosen) cross the limit;
+    every graph, replayed afterwards, gives the eager result."""
+    _, K, N = shape("down")
+    _, (xq, xs) = llama_acts(256, K)
+    _, (wq, ws) = llama_weight(K, N)
+    a, b, c, d = dev(xq), dev(xs), dev(wq), dev(ws)
+    ref = gpu_lib.fp8_block_gemm(a, b, c, d)
+    torch.cuda.synchronize()
+    ys, graphs = [], []
+    for _ in range(40):
+        y = torch.zeros_like(ref)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gpu_lib.fp8_block_gemm(a, b, c, d, y)
+        ys.append(y)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for y, g in zip(ys, graphs):
+            y.zero_()
+            g.replay()
+        torch.cuda.synchronize()
+        for j, y in enumerate(ys):
+            assert torch.equal(bits(y), bits(ref)), f"pass {i}, graph {j}"
