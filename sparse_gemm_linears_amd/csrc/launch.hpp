@@ -19,12 +19,14 @@ struct TilePlan {
 int device_cu_count();
 TilePlan plan_tiles(int M, int N, int K, int cus);
 // Decode kernel or tile kernel: the decode kernel streams the weight once but
-// re-reads the tokens per workgroup, so past 32 tokens the tile kernel (split
-// K) is faster on large weights (measured on MI355X: from M = 48 on the
-// 28672x4096 and 4096x14336 Llama-3-8B weights, dense and 2:4, while the
-// 6144x4096 and 4096x4096 ones stay faster in the decode kernel up to 64).
+// re-reads the tokens per workgroup, so past about 20 tokens the tile kernel
+// (split K) is faster on large weights (measured on MI355X, HIP-graph replay
+// from HBM, on the 28672x4096 and 4096x14336 Llama-3-8B weights: at 16 tokens
+// the decode kernel is faster, at 21 the two tie or the tile kernel leads by
+// up to 11 %, at 32 the tile kernel leads by 6-21 %, dense and 2:4), while the
+// 6144x4096 and 4096x4096 weights stay faster in the decode kernel up to 64.
 inline bool use_tile_kernel(int64_t M, int64_t N, int64_t K) {
-  return M > 64 || (M > 32 && N * K >= (int64_t(1) << 25));
+  return M > 64 || (M > 20 && N * K >= (int64_t(1) << 25));
 }
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
 // Library-owned scratch memory for the work a call puts on `stream`: kept

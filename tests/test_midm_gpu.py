@@ -1,5 +1,5 @@
-"""Block-scaled dense, 2:4 and UE8M0 GEMMs at mid-size M (33 .. ~1000 tokens:
-past 32 tokens on the large weights, past 64 on all), where the tile kernel
+"""Block-scaled dense, 2:4 and UE8M0 GEMMs at mid-size M (21 .. ~1000 tokens:
+past 20 tokens on the large weights, past 64 on all), where the tile kernel
 runs with 256 x 128 tiles and, when the tiles cover at most half of the
 compute units, splits K over several workgroups whose fp32 partials are summed
 in a second kernel.  Parity with the oracle within the GEMM tolerance, on the
@@ -18,7 +18,7 @@ from test_parity_gpu import (DEV, assert_gemm_close, dev, llama_acts, llama_spar
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M", [33, 48, 65, 128, 256, 512, 1000])
+@pytest.mark.parametrize("M", [20, 21, 24, 33, 48, 65, 128, 256, 512, 1000])
 @pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
 def test_dense_gemm_mid_m(gpu_lib, name, K, N, M):
     _, (xq, xs) = llama_acts(M, K)
@@ -57,7 +57,7 @@ def test_dense_gemm_mid_m_deterministic(gpu_lib):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [48, 65, 256, 1000])
+@pytest.mark.parametrize("M", [20, 21, 48, 65, 256, 1000])
 @pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
 def test_sparse_gemm_mid_m(gpu_lib, name, K, N, M):
     _, (xq, xs) = llama_acts(M, K)
@@ -85,7 +85,7 @@ def test_sparse_gemm_mid_m_deterministic(gpu_lib):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [48, 128, 512])
+@pytest.mark.parametrize("M", [21, 48, 128, 512])
 @pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
 def test_ue8m0_gemm_mid_m(gpu_lib, name, K, N, M):
     xq, xe = oracle.quant_act_ue8m0(llama_acts(M, K)[0])
