@@ -189,6 +189,14 @@ fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq
  * The pruned positions contribute zero.
  *
  *   wvals [N,K/2] e4m3, wmeta [N,K/8], ws [N/128,K/128] fp32
+ *
+ * On the tile kernel, a workgroup that accumulates at least 32 K blocks may
+ * keep its running sums in units of the current K block's scale (rescaled by
+ * the ratio of consecutive scales, the last scale applied at the end) when
+ * every scale product it uses is a normal fp32 number in [2^-100, 2^100], all
+ * within 2^60 of each other, and no scale is zero; otherwise it adds scaled
+ * partials.  The two differ only in fp32 rounding (about one ulp per K block
+ * for the rescaling); results are deterministic either way.
  */
 fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t *wvals,
                               const uint8_t *wmeta, const float *ws, int64_t M, int64_t N,

@@ -55,8 +55,14 @@ struct SparseTile {
 // CR: the next K block's copies are issued across the first CR row tiles.
 // PARTIAL: split K over blockIdx.y (kb_split K blocks each, a multiple of
 // SB) and store unrounded fp32 partial tiles to part + blockIdx.y * M * N.
+// Unsplit 256x128 tiles are held to 128 registers (four waves per SIMD), so
+// that two workgroups share a CU: the ratio form fits in that budget (the
+// plain form spills a few registers there; it runs only for ill-conditioned
+// scales).  Measured on QKV at M = 4096: 121 -> 99 us.  Split-K launches
+// (mid-size M) have at most one workgroup per CU and keep the plain form.
 template <int BN, int BM, int WN, int WM, int SB, int CR, bool PARTIAL = false>
-__global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t *__restrict__ xq,
+__global__ __launch_bounds__(WN *WM * 64) __attribute__((amdgpu_waves_per_eu((BM == 128 && !PARTIAL) ? 4 : 1)))
+void sparse_tile_kernel(const uint8_t *__restrict__ xq,
                                                                  const float *__restrict__ xs,
                                                                  const uint8_t *__restrict__ wv,
                                                                  const uint8_t *__restrict__ wm,
@@ -70,6 +76,7 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
   __shared__ __align__(16) uint8_t lds_m0[C::kMTile], lds_m1[C::kMTile];
   __shared__ __align__(16) uint8_t lds_b0[C::kBTile], lds_b1[C::kBTile];
   __shared__ __align__(16) float lds_s[2 * SB * BM];
+  __shared__ uint32_t xs_range[BM];  // per token: exponent range of its scales (see below)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
@@ -164,9 +171,21 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
   // LDS reads in flight
   const rsrc_t rws = make_rsrc(ws_row, (uint32_t)KB * 4u);
   float sw_cur = ws_row[0];
+  // Ratio form of the scale accumulation (when every scale this wave uses is
+  // well conditioned, see below): acc holds the running sum in units of the
+  // current K block's scale, so each sparse MFMA accumulates straight into it
+  // after one multiply by the ratio of the previous scale to the current one,
+  // and the last scale is applied once at the end.  The plain form needs a
+  // cleared partial per MFMA (the sparse MFMA accumulates into its
+  // destination, so two register moves) and an FMA per output.
+  bool ratio_form = false;
+  float unit[C::CT];
+#pragma unroll
+  for (int c = 0; c < C::CT; c++) unit[c] = 1.f;
 
-  auto step = [&](int kb, auto st_tag) {
+  auto step = [&](int kb, auto st_tag, auto form_tag) {
     constexpr int ST = decltype(st_tag)::value;
+    constexpr bool kRatio = decltype(form_tag)::value;
     const bool more = kb + 1 < KB;
     const bool scale_load = (kb % SB == 0) && (kb + SB < KB);
     if (scale_load) scales.load(kb / SB + 1);
@@ -187,37 +206,67 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
       bf[c] = load_frag_at(ST ? lds_b1 : lds_b0, b_lo, b_hi, c * 2048);
       scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
     }
-    v4f p_prev[C::CT];
+    if constexpr (kRatio) {
+      float ratio[C::CT];
 #pragma unroll
-    for (int r = 0; r < C::RT; r++) {
-      if (more && r < kCopyRows) {
-#pragma unroll
-        for (int j = r * kCopiesPerRow; j < (r + 1) * kCopiesPerRow && j < kCopies; j++) issue_copy(kb + 1, ST ^ 1, j);
+      for (int c = 0; c < C::CT; c++) {
+        ratio[c] = unit[c] * __builtin_amdgcn_rcpf(scl[c]);
+        unit[c] = scl[c];
       }
-      const v4i af = af_next;
-      const int ix = ix_next;
-      if (r + 1 < C::RT) {
-        af_next = make_v4i(*reinterpret_cast<const uint4 *>(Vt + v_off + (r + 1) * 1024));
-        ix_next = *reinterpret_cast<const int *>(Mt + m_off + (r + 1) * 256);
-      }
-      v4f p_cur[C::CT];
 #pragma unroll
-      for (int c = 0; c < C::CT; c++) p_cur[c] = smfmac_16x16x128_fp8(af, bf[c], ix);
-      if (r > 0) {
+      for (int r = 0; r < C::RT; r++) {
+        if (more && r < kCopyRows) {
+#pragma unroll
+          for (int j = r * kCopiesPerRow; j < (r + 1) * kCopiesPerRow && j < kCopies; j++)
+            issue_copy(kb + 1, ST ^ 1, j);
+        }
+        const v4i af = af_next;
+        const int ix = ix_next;
+        if (r + 1 < C::RT) {
+          af_next = make_v4i(*reinterpret_cast<const uint4 *>(Vt + v_off + (r + 1) * 1024));
+          ix_next = *reinterpret_cast<const int *>(Mt + m_off + (r + 1) * 256);
+        }
 #pragma unroll
         for (int c = 0; c < C::CT; c++) {
-          acc[r - 1][c] += scl[c] * p_prev[c];
-          pin(acc[r - 1][c]);
+          acc[r][c] = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(af, bf[c], acc[r][c] * ratio[c], ix, 0, 0);
+          pin(acc[r][c]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      v4f p_prev[C::CT];
+#pragma unroll
+      for (int r = 0; r < C::RT; r++) {
+        if (more && r < kCopyRows) {
+#pragma unroll
+          for (int j = r * kCopiesPerRow; j < (r + 1) * kCopiesPerRow && j < kCopies; j++)
+            issue_copy(kb + 1, ST ^ 1, j);
+        }
+        const v4i af = af_next;
+        const int ix = ix_next;
+        if (r + 1 < C::RT) {
+          af_next = make_v4i(*reinterpret_cast<const uint4 *>(Vt + v_off + (r + 1) * 1024));
+          ix_next = *reinterpret_cast<const int *>(Mt + m_off + (r + 1) * 256);
+        }
+        v4f p_cur[C::CT];
+#pragma unroll
+        for (int c = 0; c < C::CT; c++) p_cur[c] = smfmac_16x16x128_fp8(af, bf[c], ix);
+        if (r > 0) {
+#pragma unroll
+          for (int c = 0; c < C::CT; c++) {
+            acc[r - 1][c] += scl[c] * p_prev[c];
+            pin(acc[r - 1][c]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < C::CT; c++) p_prev[c] = p_cur[c];
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int c = 0; c < C::CT; c++) p_prev[c] = p_cur[c];
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int c = 0; c < C::CT; c++) {
-      acc[C::RT - 1][c] += scl[c] * p_prev[c];
-      pin(acc[C::RT - 1][c]);
+      for (int c = 0; c < C::CT; c++) {
+        acc[C::RT - 1][c] += scl[c] * p_prev[c];
+        pin(acc[C::RT - 1][c]);
+      }
     }
     // copies, token scales and the next weight scale have landed (vmcnt and
     // lgkmcnt drained: the LDS reads of this step are all consumed by now)
@@ -227,14 +276,92 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
     __syncthreads();
   };
 
+  // The ratio form pays for its scan of the scales over long K ranges only
+  // (short split-K ranges keep the plain form).
+  constexpr int kRatioMinKB = 32;
+  const bool try_ratio = KB >= kRatioMinKB;
   issue_copies(0, 0);
   scales.load(0);
+  // While the first copies are in flight: the exponent range of every token
+  // scale of the tile over this K range, per token (kTpt threads per token,
+  // combined in consecutive lanes), into xs_range as (min << 8) | max of the
+  // biased exponents, or ~0 when a scale is zero, subnormal or not finite.
+  {
+    constexpr int kTpt = C::kThreads / BM;
+    static_assert(kTpt == 2 || kTpt == 4, "threads per token in the scale scan");
+    const int tt = tid / kTpt, part = tid % kTpt;
+    uint32_t lo = 255u, hi = 0u, odd = 0u;
+    if (try_ratio && m_base + tt < M) {
+      const float *row = xs + (int64_t)(m_base + tt) * KBs;
+      const int chunk = (KB + kTpt - 1) / kTpt, k0 = part * chunk, k1 = min(KB, k0 + chunk);
+#pragma unroll 8
+      for (int kb = k0; kb < k1; kb++) {
+        const uint32_t e = (__float_as_uint(row[kb]) & 0x7FFFFFFFu) >> 23;
+        odd |= (uint32_t)(e == 0u || e == 255u);
+        lo = min(lo, e);
+        hi = max(hi, e);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < kTpt; off <<= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+      odd |= (uint32_t)__shfl_xor((int)odd, off, 64);
+    }
+    if (part == 0) xs_range[tt] = odd ? ~0u : (lo << 8) | hi;
+  }
+  // the same for this wave's weight scale row (every lane of the wave)
+  uint32_t wlo = 255u, whi = 0u, wodd = 0u;
+  for (int kb = try_ratio ? lane : KB; kb < KB; kb += 64) {
+    const uint32_t e = (__float_as_uint(ws_row[kb]) & 0x7FFFFFFFu) >> 23;
+    wodd |= (uint32_t)(e == 0u || e == 255u);
+    wlo = min(wlo, e);
+    whi = max(whi, e);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    wlo = min(wlo, (uint32_t)__shfl_xor((int)wlo, off, 64));
+    whi = max(whi, (uint32_t)__shfl_xor((int)whi, off, 64));
+    wodd |= (uint32_t)__shfl_xor((int)wodd, off, 64);
+  }
   wait_global_loads();
   scales.store(0);
   __syncthreads();
-  for (int kb = 0; kb < KB; kb += 2) {
-    step(kb, std::integral_constant<int, 0>{});
-    if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{});
+  {
+    // The ratio form is exact algebra; in fp32 it needs every scale product
+    // xs * ws this wave uses to be a normal number in [2^-100, 2^100] and all
+    // of them within 2^60 of each other: then no ratio, no rescaled sum (at
+    // most K/128 * 2^25 * 2^60) and no rescaled partial (at least 2^-18 *
+    // 2^-60) leaves the normal range, and the rescalings add a relative error
+    // of about one ulp per K block.  A zero scale is excluded as well: the
+    // form cannot skip a K block whose scale is zero while its codes are not.
+    // Tokens past M are ignored (their outputs are never stored).  Each wave
+    // decides for itself; otherwise it runs the plain form.
+    bool ok = try_ratio && wodd == 0u;
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) {
+      const int tok = wm0 + 16 * c + lr;
+      if (m_base + tok < M) {
+        const uint32_t r = xs_range[tok];
+        const int xlo = (int)(r >> 8), xhi = (int)(r & 0xFFu);
+        ok = ok && r != ~0u && (xhi - xlo) + (int)(whi - wlo) + 2 <= 60 && xlo + (int)wlo >= 154 &&
+             xhi + (int)whi <= 352;
+      }
+    }
+    ratio_form = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64(!ok) == 0)) != 0;
+  }
+  // two separate loops, one per form, so that each is register-allocated on
+  // its own; every wave passes the same barriers in either
+  if (ratio_form) {
+    for (int kb = 0; kb < KB; kb += 2) {
+      step(kb, std::integral_constant<int, 0>{}, std::true_type{});
+      if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    }
+  } else {
+    for (int kb = 0; kb < KB; kb += 2) {
+      step(kb, std::integral_constant<int, 0>{}, std::false_type{});
+      if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    }
   }
 
   // epilogue through a wave-private 4 KB slice of the (now idle) token stages
@@ -243,8 +370,9 @@ __global__ __launch_bounds__(WN *WM * 64) void sparse_tile_kernel(const uint8_t 
 #pragma unroll
   for (int c = 0; c < C::CT; c++) {
     v4f col[C::RT];
+    const float u = ratio_form ? unit[c] : 1.f;
 #pragma unroll
-    for (int r = 0; r < C::RT; r++) col[r] = acc[r][c];
+    for (int r = 0; r < C::RT; r++) col[r] = acc[r][c] * u;
     if constexpr (PARTIAL)
       store_token_tile_f32<C::RT>(col, part + (int64_t)blockIdx.y * M * N, M, N, m_base + wm0 + 16 * c,
                                   n_base + wn0, lane);
