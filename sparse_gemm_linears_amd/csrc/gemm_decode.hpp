@@ -165,11 +165,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
   typename W::Frag a[D][RT];
   typename X::Raw b[D][CT];
   typename X::Scale sw[D];
+  // The weight scale comes through a vector load like the other operands:
+  // vector loads complete in order, so a wait can leave younger slots in
+  // flight (scalar loads complete out of order and would need a full wait).
+  const rsrc_t rws = make_rsrc(ws_row, (uint32_t)(KB * sizeof(typename X::Scale)));
   auto load_w = [&](int slot, int i) {
     const int kb = wave + i * NW;
 #pragma unroll
     for (int r = 0; r < RT; r++) a[slot][r] = wop.load(n0 + 16 * r + lr, kb, g);
-    sw[slot] = ws_row[kb];
+    if constexpr (X::kE8)
+      sw[slot] = __builtin_amdgcn_raw_buffer_load_b8(rws, 0, kb, 0);
+    else
+      sw[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws, 0, kb * 4, 0));
   };
   auto load_x = [&](int slot, int i) {
     const int kb = wave + i * NW;
@@ -183,47 +190,75 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 #pragma unroll
     for (int c = 0; c < CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // the first weight loads go out before the tokens are staged, so their HBM
-  // latency overlaps the staging
-#pragma unroll
-  for (int d = 0; d < D; d++)
-    if (d < n_w) load_w(d, d);
   if constexpr (X::kStaged) {
+    // the first weight loads go out before the tokens are staged, so their
+    // HBM latency overlaps the staging
+    if (n_w > 0)
+#pragma unroll
+      for (int d = 0; d < D; d++) load_w(d, d);
     extern __shared__ __align__(16) uint8_t staged_lds[];
     xop.stage(staged_lds, M, threadIdx.x, NW * 64);
     __syncthreads();
-  }
+    if (n_w > 0)
 #pragma unroll
-  for (int d = 0; d < D; d++)
-    if (d < n_w) load_x(d, d);
-  for (int i0 = 0; i0 < n_w; i0 += D) {
+      for (int d = 0; d < D; d++) load_x(d, d);
+  } else if (n_w > 0) {
+    // slot by slot, in the loop's order (the waits count loads by age)
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      const int i = i0 + d;
-      if (i < n_w) {
-#pragma unroll
-        for (int c = 0; c < CT; c++) {
-          v8i bf;
-          if constexpr (X::kE8) {
-            uint32_t ex;
-            xop.make(b[d][c], bf, ex);
-#pragma unroll
-            for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(a[d][r], bf, acc[r][c], sw[d], ex);
-          } else {
-            float sx;
-            xop.make(b[d][c], bf, sx);
-            const float scl = sx * sw[d];
-#pragma unroll
-            for (int r = 0; r < RT; r++) acc[r][c] += scl * wop.mma(a[d][r], bf);
-          }
-        }
-        if (i + D < n_w) {
-          load_w(d, i + D);
-          load_x(d, i + D);
-        }
-      }
+      load_w(d, d);
+      load_x(d, d);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  auto consume = [&](int d) {
+#pragma unroll
+    for (int c = 0; c < CT; c++) {
+      v8i bf;
+      if constexpr (X::kE8) {
+        uint32_t ex;
+        xop.make(b[d][c], bf, ex);
+#pragma unroll
+        for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(a[d][r], bf, acc[r][c], sw[d], ex);
+      } else {
+        float sx;
+        xop.make(b[d][c], bf, sx);
+        const float scl = sx * sw[d];
+#pragma unroll
+        for (int r = 0; r < RT; r++) acc[r][c] += scl * wop.mma(a[d][r], bf);
+      }
+    }
+  };
+  // Rounds of D blocks.  While two more full rounds remain, every slot is
+  // consumed and refilled on every path, so each wait counts loads exactly
+  // and leaves the D - 1 younger slots in flight.  The last full round
+  // refills only blocks that exist, and the remainder consumes what is left.
+  int i0 = 0;
+  for (; i0 + 2 * D <= n_w; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+      consume(d);
+      load_w(d, i0 + d + D);
+      load_x(d, i0 + d + D);
+      // keep slot d's refill ahead of slot d + 1's use (the scheduler would
+      // sink it past, and the wait there would then drain every load)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (i0 + D <= n_w) {
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+      consume(d);
+      if (i0 + d + D < n_w) {
+        load_w(d, i0 + d + D);
+        load_x(d, i0 + d + D);
+      }
+    }
+    i0 += D;
+  }
+#pragma unroll
+  for (int d = 0; d < D - 1; d++)
+    if (i0 + d < n_w) consume(d);
 
   if (NW > 1) {
     if (wave > 0) {

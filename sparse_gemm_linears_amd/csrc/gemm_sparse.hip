@@ -447,7 +447,7 @@ static hipError_t launch_decode_for(X xop, const uint8_t *wv, const uint8_t *wm,
   if constexpr (CT == 1)
     if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wv, wm, ws, M, N, K, y, stream);
   if constexpr (CT <= 2)
-    if (N >= 16384) return launch_decode<X, 4, CT, 8, 2>(xop, wv, wm, ws, M, N, K, y, stream);
+    if (N >= 16384) return launch_decode<X, 4, CT, 8, 3>(xop, wv, wm, ws, M, N, K, y, stream);
   if (N >= 6144) return launch_decode<X, 2, CT, 8, 2>(xop, wv, wm, ws, M, N, K, y, stream);
   return launch_decode<X, 1, CT, 8, 1>(xop, wv, wm, ws, M, N, K, y, stream);
 }
