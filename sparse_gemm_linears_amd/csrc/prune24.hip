@@ -72,7 +72,14 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
                                                       float* __restrict__ s) {
   __shared__ uint32_t wave_max[4];
   const int t = threadIdx.x;
-  const int KB = (int)(K / kGroup), nb = (int)blockIdx.x / KB, kb = (int)blockIdx.x % KB;
+  // Block b runs on XCD b % 8.  Each XCD takes a contiguous range of blocks
+  // (consecutive K blocks of a row band), so the lines of vals and meta, which
+  // neighbouring K blocks write in 64- and 16-byte pieces, are completed in
+  // one L2 instead of being merged from eight.
+  const int KB = (int)(K / kGroup);
+  const int b = (int)blockIdx.x, total = (int)gridDim.x;
+  const int L = total % 8 == 0 ? (b % 8) * (total / 8) + b / 8 : b;
+  const int nb = L / KB, kb = L % KB;
   const int col = 8 * (t & 15);
   const int64_t row0 = (int64_t)nb * kGroup + (t >> 4);
   const int64_t kcol = (int64_t)kb * kGroup + col;
