@@ -4,10 +4,11 @@
 // flight per wave and does nothing else of note.
 //
 // Workgroup: RT row tiles of 16 weight rows (one 128-row scale block holds all
-// of them) and all of K.  Its NW waves take the K blocks round-robin (wave w:
-// kb = w, w + NW, ...), so at any time the waves read neighbouring 128-byte
-// pieces of the same rows; each wave accumulates its own partial sums, and the
-// partials meet in LDS at the end (fixed order: deterministic).
+// of them) and all of K, or a quarter of it with S = 4 splits (below).  Its NW
+// waves take the K blocks round-robin (wave w: kb = w, w + NW, ...), so at any
+// time the waves read neighbouring 128-byte pieces of the same rows; each wave
+// accumulates its own partial sums, and the partials meet in LDS at the end
+// (fixed order: deterministic).
 // Tokens: CT column tiles of 16 (M <= 16*CT); rows past M re-read row M-1 and
 // are never stored.
 //
@@ -145,9 +146,13 @@ inline bool staged_tokens_fit(int64_t M, int64_t K) {
          M * (K / kGroup) <= StagedTokens::kMaxPasses * 64;
 }
 
-template <class W, class X, int RT, int CT, int NW, int D>
+// S > 1 splits K over S workgroups per row band (blockIdx.y = split), for
+// long-K weights with few row bands: each split stores its fp32 sums in
+// part [S][M][N], and a separate kernel adds them in split order.
+template <class W, class X, int RT, int CT, int NW, int D, int S = 1>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typename X::Scale *__restrict__ ws,
-                                                         int M, int N, int K, uint16_t *__restrict__ y) {
+                                                         int M, int N, int K, uint16_t *__restrict__ y,
+                                                         float *__restrict__ part) {
   static_assert(128 % (16 * RT) == 0, "a workgroup's rows must sit in one 128-row scale block");
   __shared__ v4f red[NW > 1 ? NW - 1 : 1][RT * CT][64];
   const int lane = threadIdx.x & 63;
@@ -156,7 +161,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
   const int KB = K / kGroup;
   const int n0 = blockIdx.x * 16 * RT;
   const typename X::Scale *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
-  const int n_w = wave < KB ? (KB - wave + NW - 1) / NW : 0;  // K blocks of this wave
+  // this split's K blocks: [kb0, kb0 + KBr)
+  const int KBs = (KB + S - 1) / S, kb0 = S > 1 ? (int)blockIdx.y * KBs : 0;
+  const int KBr = S > 1 ? max(0, min(KB, kb0 + KBs) - kb0) : KB;
+  const int n_w = wave < KBr ? (KBr - wave + NW - 1) / NW : 0;  // K blocks of this wave
 
   int mrow[CT];
 #pragma unroll
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
   // flight (scalar loads complete out of order and would need a full wait).
   const rsrc_t rws = make_rsrc(ws_row, (uint32_t)(KB * sizeof(typename X::Scale)));
   auto load_w = [&](int slot, int i) {
-    const int kb = wave + i * NW;
+    const int kb = kb0 + wave + i * NW;
 #pragma unroll
     for (int r = 0; r < RT; r++) a[slot][r] = wop.load(n0 + 16 * r + lr, kb, g);
     if constexpr (X::kE8)
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
       sw[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws, 0, kb * 4, 0));
   };
   auto load_x = [&](int slot, int i) {
-    const int kb = wave + i * NW;
+    const int kb = kb0 + wave + i * NW;
 #pragma unroll
     for (int c = 0; c < CT; c++) b[slot][c] = xop.load(mrow[c], kb, g);
   };
@@ -275,6 +283,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
       for (int r = 0; r < RT; r++)
 #pragma unroll
         for (int c = 0; c < CT; c++) acc[r][c] += red[w][r * CT + c][lane];
+  }
+  if constexpr (S > 1) {
+    const int sp = (int)blockIdx.y;
+#pragma unroll
+    for (int c = 0; c < CT; c++) {
+      const int m = 16 * c + lr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int r = 0; r < RT; r++)
+        *reinterpret_cast<v4f *>(part + ((int64_t)sp * M + m) * N + n0 + 16 * r + 4 * g) = acc[r][c];
+    }
+    return;
   }
 #pragma unroll
   for (int c = 0; c < CT; c++) {

@@ -577,13 +577,28 @@ static hipError_t tile_gemm(const uint8_t *xq, const S *xs, const uint8_t *wq, c
   return e;
 }
 
-template <class X, int RT, int CT, int NW, int D>
+template <class X, int RT, int CT, int NW, int D, int S = 1>
 static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
                                 uint16_t *y, hipStream_t stream) {
   const size_t lds = X::kStaged ? StagedTokens::lds_bytes(M, K) : 0;
-  hipLaunchKernelGGL((decode_kernel<DenseWeight, X, RT, CT, NW, D>), dim3(N / (16 * RT)), dim3(NW * 64), lds, stream,
-                     DenseWeight{wq, K}, xop, ws, M, N, K, y);
-  return hipGetLastError();
+  const int bands = N / (16 * RT);
+  if constexpr (S == 1) {
+    hipLaunchKernelGGL((decode_kernel<DenseWeight, X, RT, CT, NW, D>), dim3(bands), dim3(NW * 64), lds, stream,
+                       DenseWeight{wq, K}, xop, ws, M, N, K, y, nullptr);
+    return hipGetLastError();
+  } else {
+    Workspace scratch;
+    hipError_t e =
+        workspace_acquire(&scratch, kSlotPartials, (size_t)S * (size_t)M * (size_t)N * sizeof(float), stream);
+    if (e != hipSuccess) return e;
+    float *part = static_cast<float *>(scratch.p);
+    hipLaunchKernelGGL((decode_kernel<DenseWeight, X, RT, CT, NW, D, S>), dim3(bands, S), dim3(NW * 64), lds, stream,
+                       DenseWeight{wq, K}, xop, ws, M, N, K, y, part);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = launch_splitk_reduce(part, S, (int64_t)M * N, y, stream);
+    const hipError_t f = workspace_release(&scratch);
+    return e == hipSuccess ? f : e;
+  }
 }
 
 
@@ -593,6 +608,13 @@ static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scal
 template <class X, int CT>
 static hipError_t launch_decode_for(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
                                     uint16_t *y, hipStream_t stream) {
+  // Long K on few row bands (N < 6144): 64-row bands read the tokens a
+  // quarter as often per weight byte, and K split four ways (partials added
+  // by a second kernel) fills the chip.  Measured on MI355X (4096 x 14336
+  // weight, graph replay from HBM): 15 % faster at 16 tokens and 21-24 % at
+  // 20, level at 8; with K = 4096 the second launch costs more than it saves.
+  if constexpr (!X::kStaged && CT <= 2)
+    if (M > 8 && N < 6144 && K >= 8192) return launch_decode<X, 4, CT, 8, 2, 4>(xop, wq, ws, M, N, K, y, stream);
   if constexpr (CT == 1)
     if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wq, ws, M, N, K, y, stream);
   if constexpr (CT <= 2)
