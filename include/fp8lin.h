@@ -12,7 +12,8 @@
  * and compute-unit counts, it keeps scratch memory of its own for the calls
  * that need one, until the process ends:
  *   fp8_block_gemm and fp8_sparse24_gemm on the tile kernel (M > 64, or
- *   M > 20 with N * K >= 2^25) with too few output tiles to cover half of the
+ *   M > 20 with N * K >= 2^25, except M <= 32 when N < 6144 and K >= 8192)
+ *   with too few output tiles to cover half of the
  *   compute units split K, with S * M * N * 4 bytes of fp32 partials
  *   (S <= 16, at most 256 tiles' worth);
  *   the same two GEMMs on the weight-streaming kernel split K four ways for
@@ -177,8 +178,8 @@ fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N
  *   y [M,N] bf16   y[m,n] = bf16_rne( sum_kb xs[m,kb] * ws[n/128,kb] *
  *                                     sum_{k in kb} dec(xq[m,k]) * dec(wq[n,k]) )
  * The inner block sums are exact FP8 products accumulated in fp32.  Small
- * batches (M <= 20, or M <= 64 when N * K < 2^25) run a weight-streaming
- * kernel; the rest run the tile kernel.  With few output tiles (tile kernel),
+ * batches (M <= 20, or M <= 32 when N < 6144 and K >= 8192, or M <= 64 when
+ * N * K < 2^25) run a weight-streaming kernel; the rest run the tile kernel.  With few output tiles (tile kernel),
  * or 9 to 32 tokens on a weight with N < 6144 and K >= 8192 (weight-streaming
  * kernel, four parts), the K blocks are summed in up to 16 fp32 partials
  * (each in K order) that are then added in a fixed order, which changes only

@@ -25,8 +25,13 @@ TilePlan plan_tiles(int M, int N, int K, int cus);
 // the decode kernel is faster, at 21 the two tie or the tile kernel leads by
 // up to 11 %, at 32 the tile kernel leads by 6-21 %, dense and 2:4), while the
 // 6144x4096 and 4096x4096 weights stay faster in the decode kernel up to 64.
+// Long-K weights with N < 6144 take the decode kernel's split-K form up to 32
+// tokens: on the 4096x14336 weight it beats the tile kernel by 19-23 % at 21
+// to 32 tokens.
 inline bool use_tile_kernel(int64_t M, int64_t N, int64_t K) {
-  return M > 64 || (M > 20 && N * K >= (int64_t(1) << 25));
+  if (M > 64) return true;
+  if (N < 6144 && K >= 8192) return M > 32;
+  return M > 20 && N * K >= (int64_t(1) << 25);
 }
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
 // Library-owned scratch memory for the work a call puts on `stream`: kept

@@ -5,7 +5,8 @@ run 64-row bands with K split four ways: each split stores fp32 partial sums
 in library scratch memory and a second kernel adds them in split order.
 Covered here, against the oracle:
 
-  * the Llama-3-8B down weight at 9, 16 and 20 tokens, and at 8 (one split);
+  * the Llama-3-8B down weight at 9, 16, 20, 21 and 32 tokens (from 21 on
+    it would otherwise take the tile kernel), and at 8 (one split);
   * ragged splits: K = 8320 (65 K blocks: splits of 17, 17, 17 and 14), fewer
     row bands than splits (N = 128), two 16-token column tiles (M = 32), and
     M = 40, past the split configurations;
@@ -24,7 +25,8 @@ from test_parity_gpu import assert_gemm_close, dev, llama_sparse_weight, llama_w
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(9, 4096, 14336), (16, 4096, 14336), (20, 4096, 14336), (8, 4096, 14336),
+SHAPES = [(9, 4096, 14336), (16, 4096, 14336), (20, 4096, 14336), (21, 4096, 14336), (32, 4096, 14336),
+          (8, 4096, 14336),
           (12, 512, 8320), (32, 128, 8192), (24, 256, 9216), (40, 512, 8192)]
 
 
