@@ -13,12 +13,12 @@
  * that need one, until the process ends:
  *   fp8_block_gemm and fp8_sparse24_gemm on the tile kernel (M > 64, or
  *   M > 20 with N * K >= 2^25, except M <= 32 when N < 6144 and K >= 8192)
- *   with too few output tiles to cover half of the
- *   compute units split K, with S * M * N * 4 bytes of fp32 partials
- *   (S <= 16, at most 256 tiles' worth);
- *   the same two GEMMs on the weight-streaming kernel split K four ways for
- *   9 to 32 tokens on weights with N < 6144 and K >= 8192 (4 * M * N * 4
- *   bytes of partials);
+ *   with too few output tiles to cover half of the compute units split K,
+ *   with S * M * N * 4 bytes of fp32 partials (S <= 16, at most 256 tiles'
+ *   worth);
+ *   the same two GEMMs on the weight-streaming kernel split K for weights
+ *   with N < 6144: four ways at 9 to 32 tokens when K >= 8192, two ways at
+ *   33 to 64 tokens when K < 8192 (S * M * N * 4 bytes of partials);
  *   fp8_block_linear and fp8_sparse24_linear from three tokens on quantize
  *   the tokens into M * K + 4 * M * K / 128 bytes (and may split K as above);
  *   fp8_block_gemm_swiglu with few tokens keeps the fp32 partials of the
@@ -179,11 +179,12 @@ fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N
  *                                     sum_{k in kb} dec(xq[m,k]) * dec(wq[n,k]) )
  * The inner block sums are exact FP8 products accumulated in fp32.  Small
  * batches (M <= 20, or M <= 32 when N < 6144 and K >= 8192, or M <= 64 when
- * N * K < 2^25) run a weight-streaming kernel; the rest run the tile kernel.  With few output tiles (tile kernel),
- * or 9 to 32 tokens on a weight with N < 6144 and K >= 8192 (weight-streaming
- * kernel, four parts), the K blocks are summed in up to 16 fp32 partials
- * (each in K order) that are then added in a fixed order, which changes only
- * the fp32 rounding order; results are deterministic either way.
+ * N * K < 2^25) run a weight-streaming kernel; the rest run the tile kernel.
+ * With few output tiles (tile kernel), or on weights with N < 6144 at 9 to 32
+ * tokens with K >= 8192 or 33 to 64 tokens with K < 8192 (weight-streaming
+ * kernel, four or two parts), the K blocks are summed in up to 16 fp32
+ * partials (each in K order) that are then added in a fixed order, which
+ * changes only the fp32 rounding order; results are deterministic either way.
  */
 fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
                            int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);

@@ -615,6 +615,11 @@ static hipError_t launch_decode_for(X xop, const uint8_t *wq, const typename X::
   // 20, level at 8; with K = 4096 the second launch costs more than it saves.
   if constexpr (!X::kStaged && CT <= 2)
     if (M > 8 && N < 6144 && K >= 8192) return launch_decode<X, 4, CT, 8, 2, 4>(xop, wq, ws, M, N, K, y, stream);
+  // Shorter K on few row bands at 33-64 tokens: 32-row bands, K split in two
+  // (o_proj 4096 x 4096: 12-16 % faster; no gain at 32 tokens or fewer, and
+  // 25 % slower on the 6144-row QKV weight).
+  if constexpr (!X::kStaged && CT == 4)
+    if (N < 6144 && K < 8192) return launch_decode<X, 2, CT, 8, 2, 2>(xop, wq, ws, M, N, K, y, stream);
   if constexpr (CT == 1)
     if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wq, ws, M, N, K, y, stream);
   if constexpr (CT <= 2)

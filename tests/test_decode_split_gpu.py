@@ -7,6 +7,9 @@ Covered here, against the oracle:
 
   * the Llama-3-8B down weight at 9, 16, 20, 21 and 32 tokens (from 21 on
     it would otherwise take the tile kernel), and at 8 (one split);
+  * K < 8192 on few row bands at 33 to 64 tokens: 32-row bands with K split
+    in two (the o_proj weight at 48 and 64 tokens; K = 640, five K blocks:
+    splits of 3 and 2);
   * ragged splits: K = 8320 (65 K blocks: splits of 17, 17, 17 and 14), fewer
     row bands than splits (N = 128), two 16-token column tiles (M = 32), and
     M = 40, past the split configurations;
@@ -27,7 +30,8 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(9, 4096, 14336), (16, 4096, 14336), (20, 4096, 14336), (21, 4096, 14336), (32, 4096, 14336),
           (8, 4096, 14336),
-          (12, 512, 8320), (32, 128, 8192), (24, 256, 9216), (40, 512, 8192)]
+          (12, 512, 8320), (32, 128, 8192), (24, 256, 9216), (40, 512, 8192),
+          (48, 4096, 4096), (64, 4096, 4096), (40, 256, 640)]
 
 
 def operands(M, N, K, kind):
