@@ -198,24 +198,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 #pragma unroll
     for (int c = 0; c < CT; c++) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // The first D slots.  A wave with fewer than D blocks fills the rest with
+  // its last block again (in bounds; never consumed), so that every slot is
+  // loaded on every path.
   if constexpr (X::kStaged) {
     // the first weight loads go out before the tokens are staged, so their
     // HBM latency overlaps the staging
     if (n_w > 0)
 #pragma unroll
-      for (int d = 0; d < D; d++) load_w(d, d);
+      for (int d = 0; d < D; d++) load_w(d, min(d, n_w - 1));
     extern __shared__ __align__(16) uint8_t staged_lds[];
     xop.stage(staged_lds, M, threadIdx.x, NW * 64);
     __syncthreads();
     if (n_w > 0)
 #pragma unroll
-      for (int d = 0; d < D; d++) load_x(d, d);
+      for (int d = 0; d < D; d++) load_x(d, min(d, n_w - 1));
   } else if (n_w > 0) {
     // slot by slot, in the loop's order (the waits count loads by age)
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      load_w(d, d);
-      load_x(d, d);
+      load_w(d, min(d, n_w - 1));
+      load_x(d, min(d, n_w - 1));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
