@@ -24,6 +24,8 @@
 // X::make runs with all 64 lanes active (it may reduce across lane groups).
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_common.hpp"
 
 namespace fp8lin {
@@ -149,6 +151,18 @@ inline bool staged_tokens_fit(int64_t M, int64_t K) {
 // S > 1 splits K over S workgroups per row band (blockIdx.y = split), for
 // long-K weights with few row bands: each split stores its fp32 sums in
 // part [S][M][N], and a separate kernel adds them in split order.
+// A weight policy may load U consecutive K blocks at a time (W::kUnit, and
+// mma(frag, b, u) for block u of the unit); without kUnit, U = 1.  The waves
+// then take units round-robin, and K must hold a whole number of units.
+template <class W, class = void>
+struct weight_unit {
+  static constexpr int value = 1;
+};
+template <class W>
+struct weight_unit<W, std::void_t<decltype(W::kUnit)>> {
+  static constexpr int value = W::kUnit;
+};
+
 template <class W, class X, int RT, int CT, int NW, int D, int S = 1>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typename X::Scale *__restrict__ ws,
                                                          int M, int N, int K, uint16_t *__restrict__ y,
@@ -158,38 +172,44 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, lr = lane & 15;
-  const int KB = K / kGroup;
+  constexpr int U = weight_unit<W>::value;
+  const int KB = K / kGroup, KU = KB / U;  // K blocks, units of U blocks
   const int n0 = blockIdx.x * 16 * RT;
   const typename X::Scale *ws_row = ws + (int64_t)(n0 / kGroup) * KB;
-  // this split's K blocks: [kb0, kb0 + KBr)
-  const int KBs = (KB + S - 1) / S, kb0 = S > 1 ? (int)blockIdx.y * KBs : 0;
-  const int KBr = S > 1 ? max(0, min(KB, kb0 + KBs) - kb0) : KB;
-  const int n_w = wave < KBr ? (KBr - wave + NW - 1) / NW : 0;  // K blocks of this wave
+  // this split's units: [kb0, kb0 + KBr)
+  const int KBs = (KU + S - 1) / S, kb0 = S > 1 ? (int)blockIdx.y * KBs : 0;
+  const int KBr = S > 1 ? max(0, min(KU, kb0 + KBs) - kb0) : KU;
+  const int n_w = wave < KBr ? (KBr - wave + NW - 1) / NW : 0;  // units of this wave
 
   int mrow[CT];
 #pragma unroll
   for (int c = 0; c < CT; c++) mrow[c] = min(16 * c + lr, M - 1);
 
   typename W::Frag a[D][RT];
-  typename X::Raw b[D][CT];
-  typename X::Scale sw[D];
+  typename X::Raw b[D][CT][U];
+  typename X::Scale sw[D][U];
   // The weight scale comes through a vector load like the other operands:
   // vector loads complete in order, so a wait can leave younger slots in
   // flight (scalar loads complete out of order and would need a full wait).
   const rsrc_t rws = make_rsrc(ws_row, (uint32_t)(KB * sizeof(typename X::Scale)));
   auto load_w = [&](int slot, int i) {
-    const int kb = kb0 + wave + i * NW;
+    const int kb = (kb0 + wave + i * NW) * U;  // first K block of the unit
 #pragma unroll
     for (int r = 0; r < RT; r++) a[slot][r] = wop.load(n0 + 16 * r + lr, kb, g);
-    if constexpr (X::kE8)
-      sw[slot] = __builtin_amdgcn_raw_buffer_load_b8(rws, 0, kb, 0);
-    else
-      sw[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws, 0, kb * 4, 0));
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if constexpr (X::kE8)
+        sw[slot][u] = __builtin_amdgcn_raw_buffer_load_b8(rws, 0, kb + u, 0);
+      else
+        sw[slot][u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws, 0, (kb + u) * 4, 0));
+    }
   };
   auto load_x = [&](int slot, int i) {
-    const int kb = kb0 + wave + i * NW;
+    const int kb = (kb0 + wave + i * NW) * U;
 #pragma unroll
-    for (int c = 0; c < CT; c++) b[slot][c] = xop.load(mrow[c], kb, g);
+    for (int c = 0; c < CT; c++)
+#pragma unroll
+      for (int u = 0; u < U; u++) b[slot][c][u] = xop.load(mrow[c], kb + u, g);
   };
 
   v4f acc[RT][CT];
@@ -224,21 +244,29 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
   }
   auto consume = [&](int d) {
 #pragma unroll
-    for (int c = 0; c < CT; c++) {
-      v8i bf;
-      if constexpr (X::kE8) {
-        uint32_t ex;
-        xop.make(b[d][c], bf, ex);
+    for (int u = 0; u < U; u++)
 #pragma unroll
-        for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(a[d][r], bf, acc[r][c], sw[d], ex);
-      } else {
-        float sx;
-        xop.make(b[d][c], bf, sx);
-        const float scl = sx * sw[d];
+      for (int c = 0; c < CT; c++) {
+        v8i bf;
+        if constexpr (X::kE8) {
+          static_assert(U == 1, "scaled MFMAs take one K block at a time");
+          uint32_t ex;
+          xop.make(b[d][c][u], bf, ex);
 #pragma unroll
-        for (int r = 0; r < RT; r++) acc[r][c] += scl * wop.mma(a[d][r], bf);
+          for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(a[d][r], bf, acc[r][c], sw[d][u], ex);
+        } else {
+          float sx;
+          xop.make(b[d][c][u], bf, sx);
+          const float scl = sx * sw[d][u];
+#pragma unroll
+          for (int r = 0; r < RT; r++) {
+            if constexpr (U == 1)
+              acc[r][c] += scl * wop.mma(a[d][r], bf);
+            else
+              acc[r][c] += scl * wop.mma(a[d][r], bf, u);
+          }
+        }
       }
-    }
   };
   // Rounds of D blocks.  While two more full rounds remain, every slot is
   // consumed and refilled on every path, so each wait counts loads exactly

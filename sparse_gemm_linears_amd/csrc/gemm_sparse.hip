@@ -402,6 +402,48 @@ struct SparseWeight {
   __device__ __forceinline__ v4f mma(const Frag &a, const v8i &b) const { return smfmac_16x16x128_fp8(a.v, b, a.idx); }
 };
 
+// The same operand four K blocks at a time, for the weight-streaming kernel.
+// One block's index words are 16 bytes per row, so loading them block by
+// block costs as many memory requests as the values while carrying a quarter
+// of the bytes (measured on MI355X: the 2:4 decode GEMMs ran 20-27 % faster
+// with no index loads at all).  Here one 16-byte load per lane brings the
+// words of four consecutive blocks: lane group g receives block kb + g's four
+// words and needs word g of each block, so the four lane groups of a row
+// exchange them (a 4x4 transpose in four cross-lane steps).
+struct SparseFrag4 {
+  v4i v[4];
+  int idx[4];
+};
+struct SparseWeight4 {
+  typedef SparseFrag4 Frag;
+  static constexpr int kUnit = 4;
+  const uint8_t *wv, *wm;
+  int K;
+  // kb: first of the four blocks.  All 64 lanes must call it together.
+  __device__ __forceinline__ Frag load(int64_t row, int kb, int g) const {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) f.v[j] = make_v4i(ldg16(wv + row * (K / 2) + (int64_t)(kb + j) * 64 + 16 * g));
+    const uint4 m = ldg16(wm + row * (K / 8) + (int64_t)kb * 16 + 16 * g);
+    const int lr = (int)(threadIdx.x & 15);
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      // lane group j sends its word (j + t) % 4; this lane (group g) takes it
+      // from group (g - t) % 4, whose word g is block ((g - t) % 4)'s
+      const int s = (g + t) & 3, j = (g - t) & 3;
+      const int send = (int)(s == 0 ? m.x : s == 1 ? m.y : s == 2 ? m.z : m.w);
+      const int got = __shfl(send, lr + 16 * j, 64);
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        if (q == j) f.idx[q] = got;
+    }
+    return f;
+  }
+  __device__ __forceinline__ v4f mma(const Frag &a, const v8i &b, int u) const {
+    return smfmac_16x16x128_fp8(a.v[u], b, a.idx[u]);
+  }
+};
+
 // ================================================================ dispatch ==
 
 template <int BN, int BM, int WN, int WM>
@@ -428,14 +470,14 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
   return hipGetLastError();
 }
 
-template <class X, int RT, int CT, int NW, int D, int S = 1>
-static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, const typename X::Scale *ws, int M,
+template <class Wt, class X, int RT, int CT, int NW, int D, int S>
+static hipError_t launch_decode_with(Wt wop, X xop, const typename X::Scale *ws, int M,
                                 int N, int K, uint16_t *y, hipStream_t stream) {
   const size_t lds = X::kStaged ? StagedTokens::lds_bytes(M, K) : 0;
   const int bands = N / (16 * RT);
   if constexpr (S == 1) {
-    hipLaunchKernelGGL((decode_kernel<SparseWeight, X, RT, CT, NW, D>), dim3(bands), dim3(NW * 64), lds, stream,
-                       SparseWeight{wv, wm, K}, xop, ws, M, N, K, y, nullptr);
+    hipLaunchKernelGGL((decode_kernel<Wt, X, RT, CT, NW, D>), dim3(bands), dim3(NW * 64), lds, stream,
+                       wop, xop, ws, M, N, K, y, nullptr);
     return hipGetLastError();
   } else {
     Workspace scratch;
@@ -443,13 +485,32 @@ static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, con
         workspace_acquire(&scratch, kSlotPartials, (size_t)S * (size_t)M * (size_t)N * sizeof(float), stream);
     if (e != hipSuccess) return e;
     float *part = static_cast<float *>(scratch.p);
-    hipLaunchKernelGGL((decode_kernel<SparseWeight, X, RT, CT, NW, D, S>), dim3(bands, S), dim3(NW * 64), lds, stream,
-                       SparseWeight{wv, wm, K}, xop, ws, M, N, K, y, part);
+    hipLaunchKernelGGL((decode_kernel<Wt, X, RT, CT, NW, D, S>), dim3(bands, S), dim3(NW * 64), lds, stream,
+                       wop, xop, ws, M, N, K, y, part);
     e = hipGetLastError();
     if (e == hipSuccess) e = launch_splitk_reduce(part, S, (int64_t)M * N, y, stream);
     const hipError_t f = workspace_release(&scratch);
     return e == hipSuccess ? f : e;
   }
+}
+
+// Four-block units (one unit in flight per wave: four blocks) where K holds a
+// whole number of units, at least one per wave, and the workgroup's outputs
+// are at most four 16x16 tiles per lane group (RT * CT <= 4; beyond that the
+// unit's registers spill).  Measured on MI355X against one block at a time
+// (graph replay from HBM, Llama-3-8B shapes): 15-20 % faster on down at 4-16
+// tokens, 15-19 % on QKV at 8-32, 13-14 % on gate/up at 8-16, 4-12 % on
+// o_proj; with spills 17-22 % slower, and with half the waves idle (gate/up
+// at 1-4 tokens, 16 waves over 8 units) 3-8 % slower.
+template <class X, int RT, int CT, int NW, int D, int S = 1>
+static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, const typename X::Scale *ws, int M,
+                                int N, int K, uint16_t *y, hipStream_t stream) {
+  constexpr int U = SparseWeight4::kUnit;
+  if constexpr (RT * CT <= 4)
+    if ((K / kGroup) % U == 0 && (K / kGroup) / U >= NW)
+      return launch_decode_with<SparseWeight4, X, RT, CT, NW, 1, S>(SparseWeight4{wv, wm, K}, xop, ws, M, N, K, y,
+                                                                    stream);
+  return launch_decode_with<SparseWeight, X, RT, CT, NW, D, S>(SparseWeight{wv, wm, K}, xop, ws, M, N, K, y, stream);
 }
 
 
