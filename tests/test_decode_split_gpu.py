@@ -14,6 +14,9 @@ Covered here, against the oracle:
     row bands than splits (N = 128), two 16-token column tiles (M = 32), and
     M = 40, past the split configurations;
   * dense, 2:4 and UE8M0 weights (the three GEMMs share the decode kernel);
+  * the 2:4 kernel's four-block units: exactly one unit per wave (3 tokens
+    over 64 K blocks with 16 waves; 32 blocks over 8 waves) and ragged unit
+    counts per split (K = 12800: 25 units split 7, 7, 7 and 4);
   * bit-identical results over repeated calls, and in a captured graph
     replayed several times with eager calls in between."""
 from __future__ import annotations
@@ -31,7 +34,8 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(9, 4096, 14336), (16, 4096, 14336), (20, 4096, 14336), (21, 4096, 14336), (32, 4096, 14336),
           (8, 4096, 14336),
           (12, 512, 8320), (32, 128, 8192), (24, 256, 9216), (40, 512, 8192),
-          (48, 4096, 4096), (64, 4096, 4096), (40, 256, 640)]
+          (48, 4096, 4096), (64, 4096, 4096), (40, 256, 640),
+          (3, 384, 8192), (16, 512, 4096), (12, 256, 12800)]
 
 
 def operands(M, N, K, kind):
