@@ -277,7 +277,6 @@ void oracle_gemm_rows(const uint8_t *xq, const float *xs, const uint8_t *wq, con
     for (int64_t r = 0; r < R; r++) gemm_row(xq, xs, wq, ws, rows[r], N, K, dec, y + r * N);
 }
 
-/* Threads OpenMP will use for the GEMM (reported with CPU timings). */
 /* ------------------------------------- per-tensor and static act scales -- */
 
 /*
@@ -369,6 +368,7 @@ void oracle_quant_wblock_ue8m0(const uint16_t *w, int64_t N, int64_t K, uint8_t 
     }
 }
 
+/* Threads OpenMP will use for the GEMM (reported with CPU timings). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);

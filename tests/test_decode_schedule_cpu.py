@@ -1,16 +1,19 @@
 """The decode kernel's load schedule, emulated on the CPU.
 
-decode_kernel (gemm_decode.hpp) gives each wave the K blocks
-kb0 + wave + i*NW, i < n_w, of its split, and cycles them through D register
-slots: the first D slots are filled up front, full rounds refill every slot
+decode_kernel (gemm_decode.hpp) gives each wave the K units
+kb0 + wave + i*NW, i < n_w, of its split (a unit is U consecutive K blocks:
+U = 4 for the 2:4 weight loaded four blocks at a time, else 1), and cycles
+them through D register slots: the first D slots are filled up front, full rounds refill every slot
 while two more rounds remain, the last full round refills only blocks that
 exist, and a remainder consumes what is left.  This test mirrors that control
 flow (it must change with the kernel) and checks, over every small
 configuration and the ones the library launches, that
 
   * every load stays inside the wave's K range (so inside the row), also
-    when a wave has fewer blocks than slots;
-  * the blocks consumed are exactly the wave's blocks, each once, in order.
+    when a wave has fewer units than slots or none at all (a split with fewer
+    units than waves);
+  * the blocks consumed are exactly the wave's blocks, each once, in order,
+    and over all waves and splits every K block of the row exactly once.
 
 A schedule that filled the first slots with their own block indices, as an
 earlier form did, fails the first check."""
@@ -19,19 +22,24 @@ from __future__ import annotations
 import pytest
 
 
-def schedule(KB: int, NW: int, D: int, S: int, split: int, wave: int, clamp_first: bool = True):
-    """(loaded blocks, consumed blocks, the wave's blocks) for one wave."""
-    KBs = (KB + S - 1) // S
+def schedule(KB: int, NW: int, D: int, S: int, split: int, wave: int, clamp_first: bool = True, U: int = 1):
+    """(loaded blocks, consumed blocks, the wave's blocks, its split's block range)
+    for one wave; KB must be a multiple of U."""
+    KU = KB // U
+    KBs = (KU + S - 1) // S
     kb0 = split * KBs if S > 1 else 0
-    KBr = max(0, min(KB, kb0 + KBs) - kb0) if S > 1 else KB
+    KBr = max(0, min(KU, kb0 + KBs) - kb0) if S > 1 else KU
     n_w = (KBr - wave + NW - 1) // NW if wave < KBr else 0
     slot = [None] * D
     loads, consumed = [], []
 
+    def blocks(i):
+        unit = kb0 + wave + i * NW
+        return [unit * U + u for u in range(U)]
+
     def load(d, i):
-        kb = kb0 + wave + i * NW
-        loads.append(kb)
-        slot[d] = kb
+        loads.extend(blocks(i))
+        slot[d] = blocks(i)
 
     if n_w > 0:
         for d in range(D):
@@ -39,29 +47,33 @@ def schedule(KB: int, NW: int, D: int, S: int, split: int, wave: int, clamp_firs
     i0 = 0
     while i0 + 2 * D <= n_w:
         for d in range(D):
-            consumed.append(slot[d])
+            consumed.extend(slot[d])
             load(d, i0 + d + D)
         i0 += D
     if i0 + D <= n_w:
         for d in range(D):
-            consumed.append(slot[d])
+            consumed.extend(slot[d])
             if i0 + d + D < n_w:
                 load(d, i0 + d + D)
         i0 += D
     for d in range(D - 1):
         if i0 + d < n_w:
-            consumed.append(slot[d])
-    mine = [kb0 + wave + i * NW for i in range(n_w)]
-    return loads, consumed, mine, (kb0, kb0 + KBr)
+            consumed.extend(slot[d])
+    mine = [b for i in range(n_w) for b in blocks(i)]
+    return loads, consumed, mine, (kb0 * U, (kb0 + KBr) * U)
 
 
-def violations(KB, NW, D, S, clamp_first=True):
+def violations(KB, NW, D, S, clamp_first=True, U=1):
     bad = []
+    every = []
     for split in range(S):
         for wave in range(NW):
-            loads, consumed, mine, (lo, hi) = schedule(KB, NW, D, S, split, wave, clamp_first)
-            if any(not lo <= kb < hi for kb in loads) or consumed != mine:
+            loads, consumed, mine, (lo, hi) = schedule(KB, NW, D, S, split, wave, clamp_first, U)
+            if any(not (lo <= kb < hi and kb < KB) for kb in loads) or consumed != mine:
                 bad.append((split, wave))
+            every.extend(consumed)
+    if sorted(every) != list(range(KB)):
+        bad.append("coverage")
     return bad
 
 
@@ -78,3 +90,22 @@ def test_unclamped_first_slots_read_out_of_range():
     range (e.g. two K blocks over 16 waves with two slots)."""
     assert violations(2, 16, 2, 1, clamp_first=False)
     assert not violations(2, 16, 2, 1)
+
+
+@pytest.mark.parametrize("S", [1, 2, 4])
+@pytest.mark.parametrize("NW", [8, 16])
+def test_four_block_units_in_range_and_complete(NW, S):
+    """The 2:4 weight loaded four K blocks at a time (D = 1 slot of one unit), with
+    splits that leave some waves without a unit: e.g. the 4096 x 14336 weight (112
+    blocks = 28 units) split four ways gives 7 units per split over 8 waves, and
+    K = 12800 (25 units) gives 7/7/7/4."""
+    for KB in [4 * u for u in range(1, 40)] + [112, 100, 144, 224]:
+        assert not violations(KB, NW, 1, S, U=4), (KB, NW, S)
+
+
+def test_idle_waves_with_units():
+    """Waves past a split's unit count load nothing."""
+    loads, consumed, mine, _ = schedule(112, 8, 1, 4, split=0, wave=7, U=4)
+    assert loads == [] and consumed == [] and mine == []
+    loads, _, _, (lo, hi) = schedule(100, 8, 1, 4, split=3, wave=3, U=4)
+    assert loads == list(range(96, 100)) and (lo, hi) == (84, 100)

@@ -152,6 +152,75 @@ def test_quant_act_exact_small():
     assert 0 < s[2, 0] < np.finfo(np.float32).tiny   # subnormal fp32 scale
 
 
+def _nearest_code_of_quotient(x: Fraction, s: Fraction, negative: bool) -> int:
+    """E4M3 code nearest to the exact quotient x / s (one rounding, ties to the even
+    code, saturating): bisection over the 127 non-negative values, then an exact
+    comparison with the midpoint of the two neighbours."""
+    a = abs(x) / s
+    sign = 0x80 if negative else 0x00
+    if a >= 448:
+        return sign | 0x7E
+    lo, hi = 0, len(E4M3_POS) - 1          # E4M3_POS is sorted by value
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if E4M3_POS[mid][1] <= a:
+            lo = mid
+        else:
+            hi = mid
+    (c0, v0), (c1, v1) = E4M3_POS[lo], E4M3_POS[hi]
+    d0, d1 = a - v0, v1 - a
+    if d0 < d1 or (d0 == d1 and c0 % 2 == 0):
+        return sign | c0
+    return sign | c1
+
+
+def test_quant_act_codes_round_the_fp32_quotient_not_the_exact_one():
+    """Which quotient the codes round.  The codes are enc(fl32(x / s)): the IEEE fp32
+    quotient, then one rounding to e4m3.  That is the exact quotient rounded once
+    except where fl32(x / s) lands exactly on an e4m3 rounding midpoint while the
+    exact quotient lies off it (a double rounding: x has 8 significant bits and s 24,
+    so x / s can sit within 2^-25 of a midpoint).  Checked with exact rational
+    arithmetic on random bf16 groups with maxima from 2^-120 to 2^120, and on crafted
+    groups whose quotients sit within a few fp32 ulps of midpoints: every code equals
+    the rounding of the correctly rounded fp32 quotient, and every code that differs
+    from the single rounding of the exact quotient is such a double-rounding case."""
+    rng = np.random.default_rng(23)
+    mids = [(E4M3_POS[i][1] + E4M3_POS[i + 1][1]) / 2 for i in range(len(E4M3_POS) - 1)]
+    mid_set = set(mids)
+    groups = []
+    for _ in range(96):                                # random groups
+        g = rng.standard_normal(128) * 2.0 ** rng.uniform(-120, 120)
+        groups.append(g.astype(np.float32))
+    for _ in range(160):                               # crafted: quotients next to midpoints
+        amax = np.float32(2.0 ** rng.uniform(-60, 60))
+        s32 = np.float32(amax / np.float32(448))
+        picks = rng.choice(len(mids), 127)
+        x = np.array([float(mids[i]) * float(s32) for i in picks]) * (1 + rng.integers(-4, 5, 127) * 2.0 ** -9)
+        x = np.clip(x, -float(amax), float(amax)) * rng.choice([-1.0, 1.0], 127)
+        groups.append(np.concatenate([[amax], x]).astype(np.float32))
+    xb = _bf16_bits(np.stack(groups))                  # [groups, 128] bf16, one group per row
+    q, s = oracle.quant_act(xb)
+    near = double_rounded = 0
+    for r in range(xb.shape[0]):
+        sr = Fraction(float(s[r, 0]))
+        assert sr == f32_round(Fraction(max(abs(bf16_value(int(b))) for b in xb[r])) / 448)
+        for k in range(128):
+            xv = bf16_value(int(xb[r, k]))
+            if xv == 0.0 or sr == 0:
+                continue
+            exact = Fraction(xv) / sr
+            q32 = Fraction(f32_round(exact))
+            assert q[r, k] == _nearest_code_of_quotient(q32, Fraction(1), xv < 0), (r, k, xv, float(sr))
+            once = _nearest_code_of_quotient(exact, Fraction(1), xv < 0)
+            if q[r, k] != once:
+                assert abs(q32) in mid_set and abs(q32) != abs(exact), (r, k, xv, float(sr))
+                double_rounded += 1
+            a, c = abs(exact), once & 0x7F
+            near += any(abs(a - m) <= m * Fraction(1, 2 ** 20) for m in mids[max(0, c - 1):c + 1])
+    assert near > 300             # the crafted groups do reach the midpoints
+    assert double_rounded > 0     # and the two readings do differ there
+
+
 def test_quant_act_division_is_not_reciprocal():
     """Codes follow x/s, which differs from x*(448/amax) in rare cases."""
     xb = si.activations(64, 4096, outliers=False)
@@ -290,19 +359,28 @@ def test_prune_activation_aware_exact_scores():
     assert keep[0, :4].tolist() == [False, False, True, True]
 
 
-def test_prune_matches_page_topk_snippet_on_tie_free_groups():
-    """The top-2-by-|w| snippet of the 2:4 cookbook (practical example 1), on groups without ties."""
+def test_prune_matches_best_pair_over_many_random_groups():
+    """Over whole random weights (magnitude and activation-aware), every group keeps
+    the pair of positions with the largest score sum, the first such pair in
+    lexicographic order when sums tie: an enumeration of the six pairs with exact
+    fp64 sums, a different procedure from the oracle's ranking."""
+    pairs = [(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)]
     w = si.weights(128, 1024)
-    keep = oracle.prune24_mask(w)
-    wt = torch.from_numpy(si.bf16_bits_to_f32(w))
-    g = wt.reshape(128, 256, 4).abs()
-    top2 = g.topk(k=2, dim=-1).indices
-    mask = torch.zeros_like(g, dtype=torch.bool)
-    mask.scatter_(-1, top2, True)
-    srt = g.sort(dim=-1, descending=True).values
-    tie_free = (srt[..., 1] != srt[..., 2]).numpy()
-    assert tie_free.mean() > 0.99
-    assert np.array_equal(keep.reshape(128, 256, 4)[tie_free], mask.numpy()[tie_free])
+    c = si.column_norms(si.calibration_batch(1024))
+    for cn in (None, c):
+        keep = oracle.prune24_mask(w, cn).reshape(128, 256, 4)
+        score = np.abs(si.bf16_bits_to_f32(w).astype(np.float64))
+        if cn is not None:
+            score = score * cn.astype(np.float64)[None, :]
+        score = score.reshape(128, 256, 4)
+        sums = np.stack([score[..., i] + score[..., j] for i, j in pairs], axis=-1)
+        best = np.argmax(sums, axis=-1)  # first maximum: the lexicographically smallest pair
+        want = np.zeros_like(keep)
+        for p, (i, j) in enumerate(pairs):
+            sel = best == p
+            want[..., i] |= sel
+            want[..., j] |= sel
+        assert np.array_equal(keep, want)
 
 
 def test_compress_roundtrip_and_cross_path_identity():

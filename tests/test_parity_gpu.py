@@ -53,11 +53,31 @@ def assert_gemm_close(y_dev: torch.Tensor, ref: np.ndarray, what: str = ""):
     assert not bad.any(), f"{what}: {bad.sum()} elements out of bound, first at {np.argwhere(bad)[0]}"
 
 
+TILE_ROWS = 128  # the smallest token tile of the tile kernels (they run 256- and 128-token tiles)
+
+
 def sample_tile_rows(M: int, count: int = 12, seed: int = 5) -> np.ndarray:
-    """Rows that touch the first and last row of the matrix, 16-row tile edges and a seeded sample."""
+    """Rows that reach every 128-token tile: its first and last row and one seeded row
+    inside it, plus the 16-row MFMA tile edges at the top and a seeded sample of
+    `count` rows over the whole matrix.  Compared across all N columns, these rows
+    put at least three rows of every output tile of every launch under the oracle
+    (48+ rows at M = 4096 per 256-token tile, 96+ per 128-token tile)."""
     fixed = {0, M - 1, min(15, M - 1), min(16, M - 1), M // 2}
+    rng = np.random.default_rng(seed)
+    for t0 in range(0, M, TILE_ROWS):
+        t1 = min(M, t0 + TILE_ROWS) - 1
+        fixed |= {t0, t1, int(rng.integers(t0, t1 + 1))}
     rest = si.sample_rows(M, count, seed=seed)
     return np.array(sorted(fixed | set(rest.tolist())), dtype=np.int64)
+
+
+def test_sample_rows_reach_every_tile():
+    """Every 128- and 256-token tile of a full-size launch has rows under comparison."""
+    for M in (4096, 8192, 1000, 65):
+        rows = sample_tile_rows(M)
+        for bm in (128, 256):
+            assert set(range((M + bm - 1) // bm)) == set((rows // bm).tolist()), (M, bm)
+        assert len(rows) >= 3 * (M // TILE_ROWS)
 
 
 @functools.lru_cache(maxsize=None)
