@@ -230,11 +230,12 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
+    dsv3, dsv3_rows = bench_dsv3(sgl, si, torch, np, dev, bf16, args.steps)
     swiglu = bench_swiglu(sgl, si, torch, np, dev, bf16, args.steps)
     ue8m0 = bench_ue8m0(sgl, si, torch, np, dev, bf16, args.steps)
     decode = None if args.no_decode else bench_decode(sgl, si, torch, np, dev, bf16)
     mid_m = None if args.no_decode else bench_mid_m(sgl, si, torch, np, dev, bf16, args.steps)
-    cpu = None if args.no_cpu else cpu_baseline(si, np, args.cpu_rows)
+    cpu = None if args.no_cpu else cpu_baseline(si, np, args.cpu_rows, dsv3_rows)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -247,6 +248,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": per_kernel,
+        "dsv3": dsv3,
         "swiglu": swiglu,
         "ue8m0": ue8m0,
         "decode": decode,
@@ -267,6 +269,34 @@ def time_calls(torch, f, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def bench_dsv3(sgl, si, torch, np, dev, bf16, steps):
+    """The DeepSeek-V3 dense FFN linears at M = 8192 tokens (7168 -> 18432 and
+    18432 -> 7168), Student-t (3 degrees of freedom) activations and N(0, 0.01)
+    weights: the activation quantizer and the dense block-scaled GEMM, each the
+    median of three batches of back-to-back calls (HIP events on the stream)."""
+    M = si.DSV3_M
+    res, sampled = {}, {}
+    rows = si.sample_rows(M, 256, seed=5)
+    for name, K, N in si.DSV3_FFN:
+        xh = si.activations(M, K, dist="student_t3", outliers=False)
+        sampled[name] = np.ascontiguousarray(xh[rows])  # the CPU oracle's sample of the same batch
+        x = bf16(xh)
+        del xh
+        xq, xs = sgl.fp8_quant_act(x)
+        wq, ws = sgl.fp8_quant_weight_block(bf16(si.weights(N, K, std=0.01)))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t_q = sorted(time_calls(torch, lambda: sgl.fp8_quant_act(x, xq, xs), steps) for _ in range(3))[1]
+        t_g = sorted(time_calls(torch, lambda: sgl.fp8_block_gemm(xq, xs, wq, ws, y), steps) for _ in range(3))[1]
+        tf = 2 * M * N * K / t_g / 1e6
+        qbytes = 2 * M * K + M * K + 4 * M * (K // 128)
+        res[name] = {"M": M, "K": K, "N": N, "gemm_us": round(t_g, 2), "gemm_tflops": round(tf, 1),
+                     "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "quant_act_us": round(t_q, 2),
+                     "quant_act_gbs": round(qbytes / t_q / 1e3, 1)}
+        del x, xq, xs, wq, ws, y
+    torch.cuda.empty_cache()
+    return res, sampled
 
 
 def bench_ue8m0(sgl, si, torch, np, dev, bf16, steps):
@@ -430,12 +460,27 @@ def time_graph(torch, f, copies, reps=3):
     return e0.elapsed_time(e1) * 1e3 / (reps * copies)
 
 
-def cpu_baseline(si, np, rows):
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(si, np, rows, dsv3_sampled):
     """The CPU oracle on a bounded sample of the step: for each of the four
     shapes, activation quant of `rows` tokens, weight block quant and 2:4
     prune/compress of the whole weight, and the dense and 2:4 GEMMs of those
     `rows` tokens.  Reported in the step's unit (algorithmic GEMM TFLOP/s);
-    input generation is not timed."""
+    input generation is not timed.  Beside it, the DeepSeek-V3 FFN GEMMs on the
+    seeded 256-row sample of the 8192 tokens in `dsv3_sampled` (activation
+    quant of those rows, weight block quant, the GEMM of those rows), with the
+    full-size time extrapolated by rows and labelled so."""
     import oracle
 
     oracle.build()
@@ -451,10 +496,30 @@ def cpu_baseline(si, np, rows):
         oracle.sparse24_gemm(xq, xs, v, m, s2)
         flops += 3 * rows * N * K
     total = time.perf_counter() - t0
+
+    dsv3 = {}
+    for name, K, N in si.DSV3_FFN:
+        x = dsv3_sampled[name]  # rows of the 8192-token Student-t batch the GPU leg used
+        dsv3_rows = x.shape[0]
+        w = si.weights(N, K, std=0.01)
+        t1 = time.perf_counter()
+        wq, ws = oracle.quant_wblock(w)
+        t2 = time.perf_counter()
+        xq, xs = oracle.quant_act(x)
+        oracle.gemm(xq, xs, wq, ws)
+        t3 = time.perf_counter()
+        rows_sec = t3 - t2
+        dsv3[name] = {"rows": int(dsv3_rows), "weight_quant_seconds": round(t2 - t1, 2),
+                      "rows_seconds": round(rows_sec, 2),
+                      "gemm_tflops": round(2 * dsv3_rows * N * K / rows_sec / 1e12, 6),
+                      "full_seconds_extrapolated": round((t2 - t1) + rows_sec * si.DSV3_M / dsv3_rows, 1),
+                      "note": f"extrapolated: the whole weight quantization plus {si.DSV3_M // dsv3_rows} times the "
+                              f"act quant + GEMM of the {dsv3_rows}-row sample"}
     return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(total, 2),
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(total, 2),
             "sample": f"each Llama-3-8B shape: quant of {rows} token rows, block quant and 2:4 prune of the "
-                      f"whole weight, dense + 2:4 GEMM of the {rows} rows (fp64 oracle, OpenMP over rows)"}
+                      f"whole weight, dense + 2:4 GEMM of the {rows} rows (fp64 oracle, OpenMP over rows)",
+            "dsv3_ffn_m8192": dsv3}
 
 
 if __name__ == "__main__":

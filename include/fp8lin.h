@@ -26,23 +26,28 @@
  * The scratch memory is held per device, stream and capture:
  *   - outside stream capture, one buffer per stream, from a stream-ordered
  *     pool the library creates once per device (hipMallocFromPoolAsync on
- *     `stream`; a larger need frees the old buffer with hipFreeAsync on the
- *     same stream first).  Calls on one stream share it, so calls on one
- *     stream must be issued in order from one host thread at a time; calls
- *     on different streams, from any threads, do not interact;
+ *     `stream`; a larger need allocates the new buffer first, then frees the
+ *     old one with hipFreeAsync on the same stream).  hipStreamPerThread names
+ *     a different stream in each thread, so its buffers are kept per thread;
  *   - under stream capture, buffers of the capture's own (hipMalloc, made
- *     with the thread's capture mode relaxed for that call), kept until the
- *     process ends because the graph holds their address: a replay shares
- *     no scratch memory with eager calls or with other graphs, and may run on
- *     any stream.  Past 1 GiB kept for captures, a capture allocates in the
- *     graph instead (stream-ordered pool allocation and free nodes).
+ *     with the thread's capture mode relaxed for that call), kept because the
+ *     graph holds their address: a replay shares no scratch memory with eager
+ *     calls or with other graphs, and may run on any stream.  At most 1 GiB is
+ *     kept for captures in all (buffers a capture outgrew included); past it a
+ *     capture allocates inside the graph instead (stream-ordered pool
+ *     allocation and free nodes).  fp8lin_release_graph_scratch frees the kept
+ *     buffers once the caller has destroyed every such graph.
+ * A call that needs scratch finds or makes all of it before its first launch
+ * and holds the library's scratch lock until its last launch is enqueued, so
+ * calls on one stream may come from any threads: they run in the order they
+ * took the lock.  Calls on different streams never share scratch memory.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (NULL = the default stream) and returns without
  * synchronising.  A fault inside a kernel surfaces at the caller's next
  * synchronisation, as for any HIP launch.
  *
- * Errors: on any error nothing is enqueued and every output is left untouched.
+ * Errors: on any error no kernel is enqueued and every output is left untouched.
  *   FP8L_ERR_NULL    a required pointer is NULL;
  *   FP8L_ERR_SHAPE   M < 0, N <= 0, K <= 0, K % 128 != 0, N % 128 != 0, or a
  *                    dimension above 2^24, or a matrix above 2^36 elements
@@ -316,6 +321,15 @@ fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *
  */
 fp8l_status fp8_sparse24_linear(const uint16_t *x, const uint8_t *wvals, const uint8_t *wmeta, const float *ws,
                                 int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+
+/*
+ * Frees the scratch memory the library keeps for calls made under stream
+ * capture (on every device).  Call it only once no graph and no executable
+ * graph that captured a library call exists, and no capture is in progress;
+ * it synchronises the devices it frees memory on.  Returns FP8L_OK, or
+ * FP8L_ERR_LAUNCH if the runtime refused a free.
+ */
+fp8l_status fp8lin_release_graph_scratch(void);
 
 /* Static, never NULL, English text for a status code. */
 const char *fp8lin_status_str(fp8l_status status);

@@ -31,7 +31,8 @@ FP8L_ERR_MEMORY = 7
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
            "fp8_sparse24_gemm", "fp8_quant_act_ue8m0", "fp8_quant_weight_block_ue8m0", "fp8_block_gemm_ue8m0",
            "fp8_grouped_gemm", "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear",
-           "fp8_quant_act_tensor", "fp8_quant_act_static", "fp8_quant_weight_tensor", "fp8lin_status_str")
+           "fp8_quant_act_tensor", "fp8_quant_act_static", "fp8_quant_weight_tensor",
+           "fp8lin_release_graph_scratch", "fp8lin_status_str")
 MAX_LINEAR_M = 64  # the fused-quantization calls take decode-sized batches
 
 _lock = threading.Lock()
@@ -65,6 +66,7 @@ def load_library():
             "fp8_quant_weight_tensor": [P, I, I, P, P, P],
             "prune24_compress": [P, P, I, I, P, P, P, P],
             "fp8_block_gemm": [P, P, P, P, I, I, I, P, P],
+            "fp8lin_release_graph_scratch": [],
             "fp8_sparse24_gemm": [P, P, P, P, P, I, I, I, P, P],
             "fp8_quant_act_ue8m0": [P, I, I, P, P, P],
             "fp8_quant_weight_block_ue8m0": [P, I, I, P, P, P],
@@ -213,6 +215,11 @@ def fp8_block_gemm(xq, xs, wq, ws, y: torch.Tensor | None = None):
     _check("fp8_block_gemm", load_library().fp8_block_gemm(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _stream(xq)))
     return y
+
+
+def fp8lin_release_graph_scratch():
+    """Free the scratch memory kept for captured calls (no graph holding it may remain)."""
+    _check("fp8lin_release_graph_scratch", load_library().fp8lin_release_graph_scratch())
 
 
 def fp8_sparse24_gemm(xq, xs, wvals, wmeta, ws, y: torch.Tensor | None = None):

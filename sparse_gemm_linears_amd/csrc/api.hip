@@ -1,6 +1,8 @@
-// C entry points: host-side validation, then one launch on the caller's stream.
-// Validation order: NULL pointers, shapes, alignment, aliasing, device.  No
-// call enqueues anything before every check has passed.
+// C entry points: host-side validation, then the launches on the caller's
+// stream.  Validation order: shapes (M == 0 returns here), NULL pointers,
+// alignment, aliasing, device; then the call's scratch memory, all of it
+// before the first launch.  No call enqueues a kernel before every check has
+// passed.
 #include <atomic>
 #include <cstring>
 
@@ -76,6 +78,13 @@ fp8l_status launched(hipError_t e) {
     return e == hipErrorOutOfMemory ? FP8L_ERR_MEMORY : FP8L_ERR_LAUNCH;
   }
   return FP8L_OK;
+}
+
+// Status of a call that held scratch memory: the launches' status first, then
+// that of handing the scratch back (a one-off allocation's stream-ordered free).
+fp8l_status finished(hipError_t e, fp8lin::CallScratch &sc) {
+  const hipError_t f = sc.release();
+  return launched(e != hipSuccess ? e : f);
 }
 
 }  // namespace
@@ -168,7 +177,11 @@ fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq
   const Range outs[] = {{y, M * N * 2}};
   if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
-  return launched(fp8lin::launch_dense_gemm(xq, xs, wq, ws, M, N, K, y, stream));
+  fp8lin::CallScratch sc;
+  if (hipError_t e = sc.acquire(fp8lin::gemm_partial_bytes(M, N, K, fp8lin::device_cu_count()), 0, stream))
+    return launched(e);
+  const hipError_t e = fp8lin::launch_dense_gemm(xq, xs, wq, ws, M, N, K, y, sc.partials(), stream);
+  return finished(e, sc);
 }
 
 fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t *wvals, const uint8_t *wmeta,
@@ -184,7 +197,11 @@ fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   const Range outs[] = {{y, M * N * 2}};
   if (any_alias(outs, 1, ins, 5)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
-  return launched(fp8lin::launch_sparse_gemm(xq, xs, wvals, wmeta, ws, M, N, K, y, stream));
+  fp8lin::CallScratch sc;
+  if (hipError_t e = sc.acquire(fp8lin::gemm_partial_bytes(M, N, K, fp8lin::device_cu_count()), 0, stream))
+    return launched(e);
+  const hipError_t e = fp8lin::launch_sparse_gemm(xq, xs, wvals, wmeta, ws, M, N, K, y, sc.partials(), stream);
+  return finished(e, sc);
 }
 
 fp8l_status fp8_quant_act_ue8m0(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, uint8_t *e, hipStream_t stream) {
@@ -221,7 +238,11 @@ fp8l_status fp8_block_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uin
   const Range outs[] = {{y, M * N * 2}};
   if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
-  return launched(fp8lin::launch_dense_gemm_ue8m0(xq, xe, wq, we, M, N, K, y, stream));
+  fp8lin::CallScratch sc;
+  if (hipError_t e = sc.acquire(fp8lin::gemm_partial_bytes(M, N, K, fp8lin::device_cu_count()), 0, stream))
+    return launched(e);
+  const hipError_t e = fp8lin::launch_dense_gemm_ue8m0(xq, xe, wq, we, M, N, K, y, sc.partials(), stream);
+  return finished(e, sc);
 }
 
 fp8l_status fp8_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
@@ -246,7 +267,7 @@ fp8l_status fp8_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *
 
 fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
                                   int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs, hipStream_t stream) {
-  if (I <= 0 || bad_mk(M, K) || bad_nk(2 * I, K) || bad_mn(M, I)) return FP8L_ERR_SHAPE;
+  if (I <= 0 || I % 128 != 0 || bad_mk(M, K) || bad_nk(2 * I, K) || bad_mn(M, I)) return FP8L_ERR_SHAPE;
   if (M == 0) return FP8L_OK;
   if (!xq || !xs || !wq || !ws || !h || (!hq != !hs)) return FP8L_ERR_NULL;
   if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(h) ||
@@ -256,7 +277,11 @@ fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint
   const Range outs[] = {{h, M * I * 2}, {hq, hq ? M * I : 0}, {hs, hs ? M * (I / 128) * 4 : 0}};
   if (any_alias(outs, 3, ins, 4)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
-  return launched(fp8lin::launch_dense_gemm_swiglu(xq, xs, wq, ws, M, I, K, h, hq, hs, stream));
+  fp8lin::CallScratch sc;
+  if (hipError_t e = sc.acquire(fp8lin::swiglu_partial_bytes(M, I, K, fp8lin::device_cu_count()), 0, stream))
+    return launched(e);
+  const hipError_t e = fp8lin::launch_dense_gemm_swiglu(xq, xs, wq, ws, M, I, K, h, hq, hs, sc.partials(), stream);
+  return finished(e, sc);
 }
 
 fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N, int64_t K,
@@ -269,7 +294,12 @@ fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *
   const Range outs[] = {{y, M * N * 2}};
   if (any_alias(outs, 1, ins, 3)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
-  return launched(fp8lin::launch_dense_linear(x, wq, ws, M, N, K, y, stream));
+  fp8lin::CallScratch sc;
+  const size_t tokens = fp8lin::linear_token_bytes(M, N, K);
+  if (hipError_t e = sc.acquire(fp8lin::gemm_partial_bytes(M, N, K, fp8lin::device_cu_count()), tokens, stream))
+    return launched(e);
+  const hipError_t e = fp8lin::launch_dense_linear(x, wq, ws, M, N, K, y, sc.tokens(), sc.partials(), stream);
+  return finished(e, sc);
 }
 
 fp8l_status fp8_sparse24_linear(const uint16_t *x, const uint8_t *wvals, const uint8_t *wmeta, const float *ws,
@@ -283,7 +313,22 @@ fp8l_status fp8_sparse24_linear(const uint16_t *x, const uint8_t *wvals, const u
   const Range outs[] = {{y, M * N * 2}};
   if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
-  return launched(fp8lin::launch_sparse_linear(x, wvals, wmeta, ws, M, N, K, y, stream));
+  fp8lin::CallScratch sc;
+  const size_t tokens = fp8lin::linear_token_bytes(M, N, K);
+  if (hipError_t e = sc.acquire(fp8lin::gemm_partial_bytes(M, N, K, fp8lin::device_cu_count()), tokens, stream))
+    return launched(e);
+  const hipError_t e = fp8lin::launch_sparse_linear(x, wvals, wmeta, ws, M, N, K, y, sc.tokens(), sc.partials(),
+                                                    stream);
+  return finished(e, sc);
+}
+
+fp8l_status fp8lin_release_graph_scratch(void) {
+  const hipError_t e = fp8lin::release_graph_scratch();
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8L_ERR_LAUNCH;
+  }
+  return FP8L_OK;
 }
 
 const char *fp8lin_status_str(fp8l_status status) {

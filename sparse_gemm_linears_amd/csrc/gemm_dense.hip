@@ -551,35 +551,27 @@ static hipError_t launch_tile(const uint8_t *xq, const S *xs, const uint8_t *wq,
   return hipGetLastError();
 }
 
-// Tile-kernel GEMM with the planned tile height and K split (workspace and
-// reduction included).
+// Tile-kernel GEMM with the planned tile height and K split (the reduction of
+// the partials included; part holds them when K is split).
 template <bool E8, class S>
 static hipError_t tile_gemm(const uint8_t *xq, const S *xs, const uint8_t *wq, const S *ws, int m, int n, int k,
-                            uint16_t *y, hipStream_t stream) {
+                            uint16_t *y, float *part, hipStream_t stream) {
   const TilePlan p = plan_tiles(m, n, k, device_cu_count());
-  Workspace scratch;
-  if (p.splits > 1) {
-    const hipError_t e =
-        workspace_acquire(&scratch, kSlotPartials, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
-    if (e != hipSuccess) return e;
-  }
-  float *part = static_cast<float *>(scratch.p);
+  if (p.splits > 1 && !part) return hipErrorInvalidValue;
   hipError_t e =
       p.bm == 128
-          ? launch_tile<256, 128, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
-          : launch_tile<256, 256, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
-  // (part is NULL when splits == 1: launch_tile then writes y)
-  if (p.splits > 1) {
-    if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
-    const hipError_t f = workspace_release(&scratch);
-    if (e == hipSuccess) e = f;
-  }
+          ? launch_tile<256, 128, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split,
+                                            p.splits > 1 ? part : nullptr, stream)
+          : launch_tile<256, 256, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split,
+                                            p.splits > 1 ? part : nullptr, stream);
+  // (launch_tile writes y itself when it gets no partials)
+  if (p.splits > 1 && e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
   return e;
 }
 
 template <class X, int RT, int CT, int NW, int D, int S = 1>
 static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
-                                uint16_t *y, hipStream_t stream) {
+                                uint16_t *y, float *part, hipStream_t stream) {
   const size_t lds = X::kStaged ? StagedTokens::lds_bytes(M, K) : 0;
   const int bands = N / (16 * RT);
   if constexpr (S == 1) {
@@ -587,17 +579,11 @@ static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scal
                        DenseWeight{wq, K}, xop, ws, M, N, K, y, nullptr);
     return hipGetLastError();
   } else {
-    Workspace scratch;
-    hipError_t e =
-        workspace_acquire(&scratch, kSlotPartials, (size_t)S * (size_t)M * (size_t)N * sizeof(float), stream);
-    if (e != hipSuccess) return e;
-    float *part = static_cast<float *>(scratch.p);
+    if (!part) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_kernel<DenseWeight, X, RT, CT, NW, D, S>), dim3(bands, S), dim3(NW * 64), lds, stream,
                        DenseWeight{wq, K}, xop, ws, M, N, K, y, part);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = launch_splitk_reduce(part, S, (int64_t)M * N, y, stream);
-    const hipError_t f = workspace_release(&scratch);
-    return e == hipSuccess ? f : e;
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? launch_splitk_reduce(part, S, (int64_t)M * N, y, stream) : e;
   }
 }
 
@@ -607,61 +593,81 @@ static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scal
 // workgroup re-reads the M x K activations from L2.
 template <class X, int CT>
 static hipError_t launch_decode_for(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
-                                    uint16_t *y, hipStream_t stream) {
+                                    uint16_t *y, float *part, hipStream_t stream) {
   // Long K on few row bands (N < 6144): 64-row bands read the tokens a
   // quarter as often per weight byte, and K split four ways (partials added
   // by a second kernel) fills the chip.  Measured on MI355X (4096 x 14336
   // weight, graph replay from HBM): 15 % faster at 16 tokens and 21-24 % at
   // 20, level at 8; with K = 4096 the second launch costs more than it saves.
-  if constexpr (!X::kStaged && CT <= 2)
-    if (M > 8 && N < 6144 && K >= 8192) return launch_decode<X, 4, CT, 8, 2, 4>(xop, wq, ws, M, N, K, y, stream);
   // Shorter K on few row bands at 33-64 tokens: 32-row bands, K split in two
   // (o_proj 4096 x 4096: 12-16 % faster; no gain at 32 tokens or fewer, and
-  // 25 % slower on the 6144-row QKV weight).
+  // 25 % slower on the 6144-row QKV weight).  decode_splits says which.
+  const int splits = X::kStaged ? 1 : decode_splits(M, N, K);
+  if constexpr (!X::kStaged && CT <= 2)
+    if (splits == 4) return launch_decode<X, 4, CT, 8, 2, 4>(xop, wq, ws, M, N, K, y, part, stream);
   if constexpr (!X::kStaged && CT == 4)
-    if (N < 6144 && K < 8192) return launch_decode<X, 2, CT, 8, 2, 2>(xop, wq, ws, M, N, K, y, stream);
+    if (splits == 2) return launch_decode<X, 2, CT, 8, 2, 2>(xop, wq, ws, M, N, K, y, part, stream);
   if constexpr (CT == 1)
-    if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wq, ws, M, N, K, y, stream);
+    if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wq, ws, M, N, K, y, part, stream);
   if constexpr (CT <= 2)
-    if (N >= 16384) return launch_decode<X, 4, CT, 8, 2>(xop, wq, ws, M, N, K, y, stream);
-  if (N >= 6144) return launch_decode<X, 2, CT, 8, 2>(xop, wq, ws, M, N, K, y, stream);
-  return launch_decode<X, 1, CT, 8, 1>(xop, wq, ws, M, N, K, y, stream);
+    if (N >= 16384) return launch_decode<X, 4, CT, 8, 2>(xop, wq, ws, M, N, K, y, part, stream);
+  if (N >= 6144) return launch_decode<X, 2, CT, 8, 2>(xop, wq, ws, M, N, K, y, part, stream);
+  return launch_decode<X, 1, CT, 8, 1>(xop, wq, ws, M, N, K, y, part, stream);
 }
 
 template <class X>
 static hipError_t launch_dense_decode(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
-                                      uint16_t *y, hipStream_t stream) {
+                                      uint16_t *y, float *part, hipStream_t stream) {
   if constexpr (X::kStaged) {
-    return launch_decode_for<X, 1>(xop, wq, ws, M, N, K, y, stream);  // M <= 8
+    return launch_decode_for<X, 1>(xop, wq, ws, M, N, K, y, part, stream);  // M <= 8
   } else {
-    if (M <= 16) return launch_decode_for<X, 1>(xop, wq, ws, M, N, K, y, stream);
-    if (M <= 32) return launch_decode_for<X, 2>(xop, wq, ws, M, N, K, y, stream);
-    return launch_decode_for<X, 4>(xop, wq, ws, M, N, K, y, stream);
+    if (M <= 16) return launch_decode_for<X, 1>(xop, wq, ws, M, N, K, y, part, stream);
+    if (M <= 32) return launch_decode_for<X, 2>(xop, wq, ws, M, N, K, y, part, stream);
+    return launch_decode_for<X, 4>(xop, wq, ws, M, N, K, y, part, stream);
   }
 }
 
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int cus) {
+  int splits = 1;
+  if (use_tile_kernel(M, N, K)) {
+    splits = plan_tiles((int)M, (int)N, (int)K, cus).splits;
+  } else {
+    splits = decode_splits(M, N, K);
+  }
+  return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+size_t swiglu_partial_bytes(int64_t M, int64_t I, int64_t K, int cus) {
+  const TilePlan p = plan_tiles((int)M, (int)(2 * I), (int)K, cus);
+  if (p.bm == 256 && p.splits == 1) return 0;  // the fused kernel
+  return (size_t)p.splits * (size_t)M * (size_t)(2 * I) * sizeof(float);
+}
+
+size_t linear_token_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!use_tile_kernel(M, N, K) && staged_tokens_fit(M, K)) return 0;  // quantized inside the decode kernel
+  return token_codes_bytes(M, K) + (size_t)M * (size_t)(K / kGroup) * sizeof(float);
+}
+
 hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
-                             int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+                             int64_t N, int64_t K, uint16_t *y, float *part, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (!use_tile_kernel(m, n, k)) return launch_dense_decode(QuantTokens{xq, xs, k}, wq, ws, m, n, k, y, stream);
-  return tile_gemm<false>(xq, xs, wq, ws, m, n, k, y, stream);
+  if (!use_tile_kernel(m, n, k))
+    return launch_dense_decode(QuantTokens{xq, xs, k}, wq, ws, m, n, k, y, part, stream);
+  return tile_gemm<false>(xq, xs, wq, ws, m, n, k, y, part, stream);
 }
 
 hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
                                    int64_t M, int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs,
-                                   hipStream_t stream) {
+                                   float *part, hipStream_t stream) {
   using C = DenseTile<256, 256, 2, 4>;
   const int m = (int)M, k = (int)K, n2 = (int)(2 * I);
   const TilePlan p = plan_tiles(m, n2, k, device_cu_count());
   if (p.bm != 256 || p.splits > 1) {
     // few output tiles: the tile GEMM of the stacked weight into fp32 partials
     // (K split as planned), then SwiGLU and the quantization in one pass
-    Workspace scratch;
+    if (!part) return hipErrorInvalidValue;
     hipError_t e =
-        workspace_acquire(&scratch, kSlotPartials, (size_t)p.splits * (size_t)m * (size_t)n2 * sizeof(float), stream);
-    if (e != hipSuccess) return e;
-    float *part = static_cast<float *>(scratch.p);
-    e = p.bm == 128
+        p.bm == 128
             ? launch_tile<256, 128, 2, 4, false>(xq, xs, wq, ws, m, n2, k, nullptr, p.splits, p.kb_split, part, stream)
             : launch_tile<256, 256, 2, 4, false>(xq, xs, wq, ws, m, n2, k, nullptr, p.splits, p.kb_split, part, stream);
     if (e == hipSuccess) {
@@ -670,8 +676,7 @@ hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const ui
                          p.splits, m, (int)I, h, hq, hs);
       e = hipGetLastError();
     }
-    const hipError_t f = workspace_release(&scratch);
-    return e == hipSuccess ? f : e;
+    return e;
   }
   const int tiles_m = (m + 255) / 256, tiles_n = (int)(I / 128);
   const TileExtra so{hq, hs, (int)I, nullptr, 0};
@@ -685,10 +690,11 @@ hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const ui
 }
 
 hipError_t launch_dense_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uint8_t *wq, const uint8_t *we,
-                                   int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+                                   int64_t M, int64_t N, int64_t K, uint16_t *y, float *part, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (!use_tile_kernel(m, n, k)) return launch_dense_decode(QuantTokensE8{xq, xe, k}, wq, we, m, n, k, y, stream);
-  return tile_gemm<true>(xq, xe, wq, we, m, n, k, y, stream);
+  if (!use_tile_kernel(m, n, k))
+    return launch_dense_decode(QuantTokensE8{xq, xe, k}, wq, we, m, n, k, y, part, stream);
+  return tile_gemm<true>(xq, xe, wq, we, m, n, k, y, part, stream);
 }
 
 hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
@@ -711,11 +717,13 @@ hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const u
 // fp8_quant_act into library scratch memory, then fp8_block_gemm (measured faster
 // from three tokens on: every decode workgroup would re-quantize all M x K).
 hipError_t launch_dense_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
-                               int64_t K, uint16_t *y, hipStream_t stream) {
+                               int64_t K, uint16_t *y, uint8_t *tokens, float *part, hipStream_t stream) {
   if (!use_tile_kernel(M, N, K) && staged_tokens_fit(M, K))
-    return launch_dense_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wq, ws, (int)M, (int)N, (int)K, y, stream);
-  return quantize_then(x, M, K, stream, [&](const uint8_t *xq, const float *xs) {
-    return launch_dense_gemm(xq, xs, wq, ws, M, N, K, y, stream);
+    return launch_dense_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wq, ws, (int)M, (int)N, (int)K, y, part,
+                               stream);
+  if (!tokens) return hipErrorInvalidValue;
+  return quantize_then(x, M, K, tokens, stream, [&](const uint8_t *xq, const float *xs) {
+    return launch_dense_gemm(xq, xs, wq, ws, M, N, K, y, part, stream);
   });
 }
 

@@ -472,7 +472,7 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
 
 template <class Wt, class X, int RT, int CT, int NW, int D, int S>
 static hipError_t launch_decode_with(Wt wop, X xop, const typename X::Scale *ws, int M,
-                                int N, int K, uint16_t *y, hipStream_t stream) {
+                                int N, int K, uint16_t *y, float *part, hipStream_t stream) {
   const size_t lds = X::kStaged ? StagedTokens::lds_bytes(M, K) : 0;
   const int bands = N / (16 * RT);
   if constexpr (S == 1) {
@@ -480,110 +480,97 @@ static hipError_t launch_decode_with(Wt wop, X xop, const typename X::Scale *ws,
                        wop, xop, ws, M, N, K, y, nullptr);
     return hipGetLastError();
   } else {
-    Workspace scratch;
-    hipError_t e =
-        workspace_acquire(&scratch, kSlotPartials, (size_t)S * (size_t)M * (size_t)N * sizeof(float), stream);
-    if (e != hipSuccess) return e;
-    float *part = static_cast<float *>(scratch.p);
+    if (!part) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_kernel<Wt, X, RT, CT, NW, D, S>), dim3(bands, S), dim3(NW * 64), lds, stream,
                        wop, xop, ws, M, N, K, y, part);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = launch_splitk_reduce(part, S, (int64_t)M * N, y, stream);
-    const hipError_t f = workspace_release(&scratch);
-    return e == hipSuccess ? f : e;
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? launch_splitk_reduce(part, S, (int64_t)M * N, y, stream) : e;
   }
 }
 
 // Four-block units (one unit in flight per wave: four blocks) where K holds a
-// whole number of units, at least one per wave, and the workgroup's outputs
-// are at most four 16x16 tiles per lane group (RT * CT <= 4; beyond that the
-// unit's registers spill).  Measured on MI355X against one block at a time
-// (graph replay from HBM, Llama-3-8B shapes): 15-20 % faster on down at 4-16
-// tokens, 15-19 % on QKV at 8-32, 13-14 % on gate/up at 8-16, 4-12 % on
-// o_proj; with spills 17-22 % slower, and with half the waves idle (gate/up
-// at 1-4 tokens, 16 waves over 8 units) 3-8 % slower.
+// whole number of units, at least as many units as waves over the whole row,
+// and the workgroup's outputs are at most four 16x16 tiles per lane group
+// (RT * CT <= 4; beyond that the unit's registers spill).  A K split can still
+// leave waves of a split without a unit: the 4096 x 14336 weight has 28 units,
+// so its four splits get 7 each over 8 waves.  Measured on MI355X against one
+// block at a time (graph replay from HBM, Llama-3-8B shapes): 15-20 % faster
+// on down at 4-16 tokens (split four ways from 9 tokens, one wave per split
+// idle), 15-19 % on QKV at 8-32, 13-14 % on gate/up at 8-16, 4-12 % on
+// o_proj; with spills 17-22 % slower, and with half the waves idle over the
+// whole row (gate/up at 1-4 tokens, 16 waves over 8 units) 3-8 % slower.
 template <class X, int RT, int CT, int NW, int D, int S = 1>
 static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, const typename X::Scale *ws, int M,
-                                int N, int K, uint16_t *y, hipStream_t stream) {
+                                int N, int K, uint16_t *y, float *part, hipStream_t stream) {
   constexpr int U = SparseWeight4::kUnit;
   if constexpr (RT * CT <= 4)
     if ((K / kGroup) % U == 0 && (K / kGroup) / U >= NW)
       return launch_decode_with<SparseWeight4, X, RT, CT, NW, 1, S>(SparseWeight4{wv, wm, K}, xop, ws, M, N, K, y,
-                                                                    stream);
-  return launch_decode_with<SparseWeight, X, RT, CT, NW, D, S>(SparseWeight{wv, wm, K}, xop, ws, M, N, K, y, stream);
+                                                                    part, stream);
+  return launch_decode_with<SparseWeight, X, RT, CT, NW, D, S>(SparseWeight{wv, wm, K}, xop, ws, M, N, K, y, part,
+                                                               stream);
 }
 
 
 // Decode configuration (measured on MI355X over the Llama-3-8B shapes): more
 // rows per workgroup when N is large enough to keep every CU busy, since each
-// workgroup re-reads the M x K activations from L2.
+// workgroup re-reads the M x K activations from L2.  K splits as in the dense
+// GEMM (decode_splits).
 template <class X, int CT>
 static hipError_t launch_decode_for(X xop, const uint8_t *wv, const uint8_t *wm, const float *ws, int M, int N,
-                                    int K, uint16_t *y, hipStream_t stream) {
-  // Long K on few row bands (N < 6144): 64-row bands read the tokens a
-  // quarter as often per weight byte, and K split four ways (partials added
-  // by a second kernel) fills the chip.  Measured on MI355X (4096 x 14336
-  // weight, graph replay from HBM): 15 % faster at 16 tokens and 21-24 % at
-  // 20, level at 8; with K = 4096 the second launch costs more than it saves.
+                                    int K, uint16_t *y, float *part, hipStream_t stream) {
+  const int splits = X::kStaged ? 1 : decode_splits(M, N, K);
   if constexpr (!X::kStaged && CT <= 2)
-    if (M > 8 && N < 6144 && K >= 8192) return launch_decode<X, 4, CT, 8, 2, 4>(xop, wv, wm, ws, M, N, K, y, stream);
-  // Shorter K on few row bands at 33-64 tokens: 32-row bands, K split in two
-  // (o_proj 4096 x 4096: 12-16 % faster; no gain at 32 tokens or fewer, and
-  // 25 % slower on the 6144-row QKV weight).
+    if (splits == 4) return launch_decode<X, 4, CT, 8, 2, 4>(xop, wv, wm, ws, M, N, K, y, part, stream);
   if constexpr (!X::kStaged && CT == 4)
-    if (N < 6144 && K < 8192) return launch_decode<X, 2, CT, 8, 2, 2>(xop, wv, wm, ws, M, N, K, y, stream);
+    if (splits == 2) return launch_decode<X, 2, CT, 8, 2, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);
   if constexpr (CT == 1)
-    if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wv, wm, ws, M, N, K, y, stream);
+    if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);
   if constexpr (CT <= 2)
-    if (N >= 16384) return launch_decode<X, 4, CT, 8, 3>(xop, wv, wm, ws, M, N, K, y, stream);
-  if (N >= 6144) return launch_decode<X, 2, CT, 8, 2>(xop, wv, wm, ws, M, N, K, y, stream);
-  return launch_decode<X, 1, CT, 8, 1>(xop, wv, wm, ws, M, N, K, y, stream);
+    if (N >= 16384) return launch_decode<X, 4, CT, 8, 3>(xop, wv, wm, ws, M, N, K, y, part, stream);
+  if (N >= 6144) return launch_decode<X, 2, CT, 8, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);
+  return launch_decode<X, 1, CT, 8, 1>(xop, wv, wm, ws, M, N, K, y, part, stream);
 }
 
 template <class X>
 static hipError_t launch_sparse_decode(X xop, const uint8_t *wv, const uint8_t *wm, const float *ws, int M, int N,
-                                       int K, uint16_t *y, hipStream_t stream) {
+                                       int K, uint16_t *y, float *part, hipStream_t stream) {
   if constexpr (X::kStaged) {
-    return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, stream);  // M <= 8
+    return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, part, stream);  // M <= 8
   } else {
-    if (M <= 16) return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, stream);
-    if (M <= 32) return launch_decode_for<X, 2>(xop, wv, wm, ws, M, N, K, y, stream);
-    return launch_decode_for<X, 4>(xop, wv, wm, ws, M, N, K, y, stream);
+    if (M <= 16) return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, part, stream);
+    if (M <= 32) return launch_decode_for<X, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);
+    return launch_decode_for<X, 4>(xop, wv, wm, ws, M, N, K, y, part, stream);
   }
 }
 
 hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
-                              const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+                              const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, float *part,
+                              hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (!use_tile_kernel(m, n, k)) return launch_sparse_decode(QuantTokens{xq, xs, k}, wv, wm, ws, m, n, k, y, stream);
+  if (!use_tile_kernel(m, n, k))
+    return launch_sparse_decode(QuantTokens{xq, xs, k}, wv, wm, ws, m, n, k, y, part, stream);
   const TilePlan p = plan_tiles(m, n, k, device_cu_count());
-  Workspace scratch;
-  if (p.splits > 1) {
-    const hipError_t e =
-        workspace_acquire(&scratch, kSlotPartials, (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float), stream);
-    if (e != hipSuccess) return e;
-  }
-  float *part = static_cast<float *>(scratch.p);
+  if (p.splits > 1 && !part) return hipErrorInvalidValue;
+  float *pp = p.splits > 1 ? part : nullptr;
   hipError_t e = p.bm == 128
-                     ? launch_tile<256, 128, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, p.splits, p.kb_split, part, stream)
-                     : launch_tile<256, 256, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, p.splits, p.kb_split, part, stream);
-  if (p.splits > 1) {
-    if (e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
-    const hipError_t f = workspace_release(&scratch);
-    if (e == hipSuccess) e = f;
-  }
+                     ? launch_tile<256, 128, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, p.splits, p.kb_split, pp, stream)
+                     : launch_tile<256, 256, 2, 4>(xq, xs, wv, wm, ws, m, n, k, y, p.splits, p.kb_split, pp, stream);
+  if (p.splits > 1 && e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
   return e;
 }
 
 // As the dense linear: in-kernel quantization for one or two tokens, else
-// fp8_quant_act into library scratch memory and fp8_sparse24_gemm.
+// fp8_quant_act into the call's scratch tokens and fp8_sparse24_gemm.
 hipError_t launch_sparse_linear(const uint16_t *x, const uint8_t *wv, const uint8_t *wm, const float *ws, int64_t M,
-                                int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+                                int64_t N, int64_t K, uint16_t *y, uint8_t *tokens, float *part,
+                                hipStream_t stream) {
   if (!use_tile_kernel(M, N, K) && staged_tokens_fit(M, K))
     return launch_sparse_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wv, wm, ws, (int)M, (int)N, (int)K, y,
-                                stream);
-  return quantize_then(x, M, K, stream, [&](const uint8_t *xq, const float *xs) {
-    return launch_sparse_gemm(xq, xs, wv, wm, ws, M, N, K, y, stream);
+                                part, stream);
+  if (!tokens) return hipErrorInvalidValue;
+  return quantize_then(x, M, K, tokens, stream, [&](const uint8_t *xq, const float *xs) {
+    return launch_sparse_gemm(xq, xs, wv, wm, ws, M, N, K, y, part, stream);
   });
 }
 

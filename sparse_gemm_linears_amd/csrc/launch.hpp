@@ -33,37 +33,75 @@ inline bool use_tile_kernel(int64_t M, int64_t N, int64_t K) {
   if (N < 6144 && K >= 8192) return M > 32;
   return M > 20 && N * K >= (int64_t(1) << 25);
 }
+// K split of the weight-streaming kernel (1 = none).  Long K on few row bands
+// (N < 6144, K >= 8192) at 9 to 32 tokens splits four ways; shorter K on few
+// row bands at 33 to 64 tokens two ways (both measured on MI355X; the
+// launchers pick the matching kernel instance).  Never for one or two
+// tokens, the range quantized inside the kernel.
+inline int decode_splits(int64_t M, int64_t N, int64_t K) {
+  if (M > 8 && M <= 32 && N < 6144 && K >= 8192) return 4;
+  if (M > 32 && N < 6144 && K < 8192) return 2;
+  return 1;
+}
+// Bytes of fp32 split-K partials that fp8_block_gemm, fp8_sparse24_gemm and
+// fp8_block_gemm_ue8m0 need for this shape on a device with `cus` compute
+// units (0 when K is not split): splits * M * N * 4.
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int cus);
+// The same for fp8_block_gemm_swiglu (the stacked [gate; up] GEMM of 2I rows
+// when it runs on smaller tiles or split K).
+size_t swiglu_partial_bytes(int64_t M, int64_t I, int64_t K, int cus);
+// Scratch of the fused linear calls: the quantized tokens (codes, then fp32
+// scales at a 256-byte aligned offset; 0 bytes when the tokens are quantized
+// inside the decode kernel) and the partials of the GEMM that follows.
+size_t linear_token_bytes(int64_t M, int64_t N, int64_t K);
+inline size_t token_codes_bytes(int64_t M, int64_t K) { return ((size_t)M * (size_t)K + 255) / 256 * 256; }
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
-// Library-owned scratch memory for the work a call puts on `stream`: kept
-// between calls per (device, stream, slot), and per capture for calls under
-// stream capture (a captured graph keeps its own).  Calls on one stream share
-// it, so they must be issued in stream order (not from several host threads
-// at once on one stream).  workspace_release returns it (a no-op unless the
-// memory was a one-off allocation).
-enum WorkspaceSlot { kSlotPartials = 0, kSlotTokens = 1 };
-struct Workspace {
-  void *p = nullptr;
-  hipStream_t stream = nullptr;
-  bool transient = false;
-};
-hipError_t workspace_acquire(Workspace *w, WorkspaceSlot slot, size_t bytes, hipStream_t stream);
-hipError_t workspace_release(Workspace *w);
 
-// Tokens quantized into library scratch memory, then the GEMM on them: exactly
-// fp8_quant_act followed by gemm(xq, xs).
+// Scratch memory of one call, held from acquire() until release() (or the
+// destructor): the split-K partials and the quantized tokens a call needs,
+// found or made before the call's first launch, so that a failed acquisition
+// enqueues no kernel.  While held it keeps the library's scratch lock, so that
+// calls on one stream may come from several host threads: their launches and
+// the stream-ordered frees of outgrown buffers are enqueued in call order.
+//   * outside stream capture: one buffer per (device, stream, slot), from a
+//     stream-ordered pool the library owns (hipStreamPerThread is keyed by the
+//     calling thread too, since that one handle names a different stream in
+//     each thread); a larger need allocates the new buffer first and then frees
+//     the old one on the same stream, after the work queued on it;
+//   * under stream capture: buffers of that capture (hipMalloc outside the
+//     graph, kept until the process ends or fp8lin_release_graph_scratch),
+//     at most 1 GiB in all; past it, allocation and free nodes in the graph.
+class CallScratch {
+ public:
+  CallScratch() = default;
+  CallScratch(const CallScratch &) = delete;
+  CallScratch &operator=(const CallScratch &) = delete;
+  ~CallScratch() { (void)release(); }
+  hipError_t acquire(size_t partial_bytes, size_t token_bytes, hipStream_t stream);
+  hipError_t release();
+  float *partials() const { return static_cast<float *>(p_[0]); }
+  uint8_t *tokens() const { return static_cast<uint8_t *>(p_[1]); }
+
+ private:
+  void *p_[2] = {nullptr, nullptr};
+  bool transient_[2] = {false, false};
+  hipStream_t stream_ = nullptr;
+  bool locked_ = false;
+};
+// Frees the buffers kept for captured calls (all devices).  Only valid when no
+// graph or executable graph that captured a library call exists any more.
+hipError_t release_graph_scratch();
+
+// fp8_quant_act into `tokens` (linear_token_bytes of scratch: codes, then the
+// scales at token_codes_bytes), then gemm(xq, xs) on them: exactly the two
+// calls fp8_quant_act and the GEMM.
 template <class Gemm>
-inline hipError_t quantize_then(const uint16_t *x, int64_t M, int64_t K, hipStream_t stream, Gemm gemm) {
-  const size_t q_bytes = ((size_t)M * (size_t)K + 255) / 256 * 256;
-  const size_t s_bytes = (size_t)M * (size_t)(K / 128) * sizeof(float);
-  Workspace ws;
-  hipError_t e = workspace_acquire(&ws, kSlotTokens, q_bytes + s_bytes, stream);
-  if (e != hipSuccess) return e;
-  uint8_t *xq = static_cast<uint8_t *>(ws.p);
-  float *xs = reinterpret_cast<float *>(xq + q_bytes);
-  e = launch_quant_act(x, M, K, xq, xs, stream);
-  if (e == hipSuccess) e = gemm(xq, xs);
-  const hipError_t f = workspace_release(&ws);
-  return e == hipSuccess ? f : e;
+inline hipError_t quantize_then(const uint16_t *x, int64_t M, int64_t K, uint8_t *tokens, hipStream_t stream,
+                                Gemm gemm) {
+  uint8_t *xq = tokens;
+  float *xs = reinterpret_cast<float *>(tokens + token_codes_bytes(M, K));
+  const hipError_t e = launch_quant_act(x, M, K, xq, xs, stream);
+  return e == hipSuccess ? gemm(xq, xs) : e;
 }
 
 // One scale for a whole tensor of n bf16 values (n a multiple of 8), written
@@ -78,13 +116,16 @@ hipError_t launch_quant_act_ue8m0(const uint16_t *x, int64_t M, int64_t K, uint8
 hipError_t launch_quant_wblock_ue8m0(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, uint8_t *e,
                                      hipStream_t stream);
 hipError_t launch_dense_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uint8_t *wq, const uint8_t *we,
-                                   int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+                                   int64_t M, int64_t N, int64_t K, uint16_t *y, float *part, hipStream_t stream);
 hipError_t launch_prune24(const uint16_t *w, const float *col_norm, int64_t N, int64_t K, uint8_t *vals,
                           uint8_t *meta, float *s, hipStream_t stream);
+// part: fp32 partials of gemm_partial_bytes(M, N, K, device_cu_count()) bytes
+// (may be NULL when that is 0).
 hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
-                             int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+                             int64_t N, int64_t K, uint16_t *y, float *part, hipStream_t stream);
 hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t *wv, const uint8_t *wm,
-                              const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+                              const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, float *part,
+                              hipStream_t stream);
 
 // Grouped (MoE) dense GEMM: expert g multiplies rows offsets[g] .. offsets[g+1]-1
 // (device int32 offsets, nondecreasing, offsets[0] = 0, offsets[G] = M).
@@ -96,13 +137,15 @@ hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const u
 // h = bf16(silu(g) * u), plus fp8_quant_act(h) when hq is not NULL.
 hipError_t launch_dense_gemm_swiglu(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
                                    int64_t M, int64_t I, int64_t K, uint16_t *h, uint8_t *hq, float *hs,
-                                   hipStream_t stream);
+                                   float *part, hipStream_t stream);
 
 // Decode-sized (M <= 64) GEMMs on bf16 activations, quantized inside the kernel
 // with the arithmetic of fp8_quant_act.
+// tokens: linear_token_bytes(M, N, K) bytes; part: gemm_partial_bytes(M, N, K, ..).
 hipError_t launch_dense_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
-                               int64_t K, uint16_t *y, hipStream_t stream);
+                               int64_t K, uint16_t *y, uint8_t *tokens, float *part, hipStream_t stream);
 hipError_t launch_sparse_linear(const uint16_t *x, const uint8_t *wv, const uint8_t *wm, const float *ws, int64_t M,
-                                int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+                                int64_t N, int64_t K, uint16_t *y, uint8_t *tokens, float *part,
+                                hipStream_t stream);
 
 }  // namespace fp8lin

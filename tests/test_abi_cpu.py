@@ -129,6 +129,16 @@ def test_gemm_validation(lib):
     assert h(P(A), P(B), P(C), P(D), P(E), 16, 128, 128, P(D), None) == sgl.FP8L_ERR_ALIAS
 
 
+def test_swiglu_validation(lib):
+    f = lib.fp8_block_gemm_swiglu
+    # I must be a multiple of 128 itself (2I = 128 is not enough)
+    assert f(P(A), P(B), P(C), P(D), 16, 64, 128, P(E), None, None, None) == sgl.FP8L_ERR_SHAPE
+    assert f(P(A), P(B), P(C), P(D), 16, 0, 128, P(E), None, None, None) == sgl.FP8L_ERR_SHAPE
+    assert f(P(A), P(B), P(C), P(D), 16, 128, 128, P(E), P(F), None, None) == sgl.FP8L_ERR_NULL  # hq without hs
+    assert f(P(A), P(B), P(C), P(D), 16, 128, 128, P(E + 2), None, None, None) == sgl.FP8L_ERR_ALIGN
+    assert f(P(A), P(B), P(C), P(D), 16, 128, 128, P(D), None, None, None) == sgl.FP8L_ERR_ALIAS
+
+
 def test_linear_validation(lib):
     """The fused-quantization calls: same checks as the GEMMs, plus M <= 64."""
     f = lib.fp8_block_linear
@@ -155,6 +165,8 @@ def test_valid_call_without_gpu_reports_device(lib):
     assert lib.fp8_quant_act(P(A), 4, 128, P(B), P(C), None) == sgl.FP8L_ERR_DEVICE
     assert lib.fp8_block_gemm(P(A), P(B), P(C), P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_DEVICE
     assert lib.fp8_block_linear(P(A), P(C), P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_DEVICE
+    # nothing kept for graphs: releasing is a no-op that needs no device
+    assert lib.fp8lin_release_graph_scratch() == sgl.FP8L_OK
 
 
 def test_binding_rejects_host_tensors():

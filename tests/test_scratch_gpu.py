@@ -198,3 +198,90 @@ def test_captures_past_the_kept_limit(gpu_lib, setup):
         torch.cuda.synchronize()
         for j, y in enumerate(ys):
             assert torch.equal(bits(y), bits(ref)), f"pass {i}, graph {j}"
+    del graphs
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    # every graph that held the kept buffers is gone: they can be freed, and a
+    # new capture afterwards keeps (and uses) fresh ones
+    gpu_lib.fp8lin_release_graph_scratch()
+    y = torch.zeros_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpu_lib.fp8_block_gemm(a, b, c, d, y)
+    for _ in range(2):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y), bits(ref)), "capture after the release"
+
+
+def test_threads_sharing_one_stream(gpu_lib, setup):
+    """Two host threads issue scratch-using calls on one stream at once: a call
+    holds the scratch lock until its launches are enqueued, so each call's
+    kernels use a buffer no other call frees or reuses in between."""
+    import threading
+    inp, refs = setup
+    a, b = make_cases(gpu_lib, inp), make_cases(gpu_lib, inp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    errors = []
+
+    def run(cases, order):
+        try:
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    for fn, _ in (cases if order else cases[::-1]):
+                        fn()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    ts = [threading.Thread(target=run, args=(a, True)), threading.Thread(target=run, args=(b, False))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    check(a, refs, "thread 1")
+    check(b, refs, "thread 2")
+
+
+def test_per_thread_default_stream(gpu_lib, setup):
+    """hipStreamPerThread is one handle value naming a different stream in each
+    thread: two threads passing it run on two streams, and their calls must not
+    share a scratch buffer."""
+    import ctypes
+    import threading
+    inp, refs = setup
+    lib = gpu_lib.load_library()
+    per_thread = ctypes.c_void_p(2)  # hipStreamPerThread
+    _, K, N = shape("down")
+    _, (xq, xs) = llama_acts(256, K)
+    _, (wq, ws) = llama_weight(K, N)
+    a, b_, c, d = dev(xq), dev(xs), dev(wq), dev(ws)
+    ref = gpu_lib.fp8_block_gemm(a, b_, c, d)
+    _, (xq2, xs2) = llama_acts(128, K)
+    a2, b2 = dev(xq2), dev(xs2)
+    ref2 = gpu_lib.fp8_block_gemm(a2, b2, c, d)
+    torch.cuda.synchronize()
+    outs = [[torch.zeros_like(ref) for _ in range(4)], [torch.zeros_like(ref2) for _ in range(4)]]
+    status = []
+
+    def run(x, s, ys):
+        for y in ys:
+            status.append(lib.fp8_block_gemm(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(s.data_ptr()),
+                                             ctypes.c_void_p(c.data_ptr()), ctypes.c_void_p(d.data_ptr()),
+                                             x.shape[0], N, K, ctypes.c_void_p(y.data_ptr()), per_thread))
+
+    ts = [threading.Thread(target=run, args=(a, b_, outs[0])), threading.Thread(target=run, args=(a2, b2, outs[1]))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert status == [0] * 8, status
+    for y in outs[0]:
+        assert torch.equal(bits(y), bits(ref))
+    for y in outs[1]:
+        assert torch.equal(bits(y), bits(ref2))
