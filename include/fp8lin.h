@@ -41,6 +41,8 @@
  * and holds the library's scratch lock until its last launch is enqueued, so
  * calls on one stream may come from any threads: they run in the order they
  * took the lock.  Calls on different streams never share scratch memory.
+ * fp8_block_gemm_noalloc takes its partials from a fixed device array of the
+ * library's instead and allocates nothing.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (NULL = the default stream) and returns without
@@ -58,7 +60,9 @@
  *   FP8L_ERR_DEVICE  the current HIP device is missing or is not gfx950;
  *   FP8L_ERR_LAUNCH  the kernel launch was rejected by the runtime;
  *   FP8L_ERR_MEMORY  scratch memory for the call could not be allocated (no
- *                    kernel runs).
+ *                    kernel runs);
+ *   FP8L_ERR_SCRATCH fp8_block_gemm_noalloc: the call needs more scratch than
+ *                    the fixed array holds (no kernel runs).
  * M == 0 (an empty batch) returns FP8L_OK without launching and without
  * looking at the M-sized buffers.  There is no fallback path: an unsupported
  * case is an error, never a silently slower kernel.
@@ -82,7 +86,8 @@ enum {
     FP8L_ERR_ALIAS = 4,
     FP8L_ERR_DEVICE = 5,
     FP8L_ERR_LAUNCH = 6,
-    FP8L_ERR_MEMORY = 7
+    FP8L_ERR_MEMORY = 7,
+    FP8L_ERR_SCRATCH = 8
 };
 
 /*
@@ -193,6 +198,24 @@ fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N
  */
 fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
                            int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
+
+/*
+ * fp8_block_gemm for callers that cannot allocate memory: code that must not
+ * call hipMalloc (or add memory nodes to a graph being captured), tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, kernels
+ * and results as fp8_block_gemm, bit for bit.  Where fp8_block_gemm splits K
+ * (see above), the fp32 partials go to a fixed device array of the library
+ * (32 MiB per device, a file-scope device variable that exists while the
+ * library is loaded; enough for every split plan on a 256-CU MI355X) instead
+ * of allocated scratch; every other case needs no scratch at all.  A call
+ * whose partials would not fit returns FP8L_ERR_SCRATCH and launches nothing.
+ * The array keeps the last call's partials and is overwritten before it is
+ * read, so nothing needs clearing.  All calls on one device share it: calls
+ * that can overlap on the GPU (different streams, or graphs replayed
+ * concurrently) race on it and must be ordered by the caller.
+ */
+fp8l_status fp8_block_gemm_noalloc(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                                   int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream);
 
 /*
  * The same GEMM with a 2:4-compressed weight from prune24_compress ("Deployer

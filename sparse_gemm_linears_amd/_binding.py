@@ -27,11 +27,12 @@ FP8L_ERR_ALIAS = 4
 FP8L_ERR_DEVICE = 5
 FP8L_ERR_LAUNCH = 6
 FP8L_ERR_MEMORY = 7
+FP8L_ERR_SCRATCH = 8
 
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
            "fp8_sparse24_gemm", "fp8_quant_act_ue8m0", "fp8_quant_weight_block_ue8m0", "fp8_block_gemm_ue8m0",
            "fp8_grouped_gemm", "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear",
-           "fp8_quant_act_tensor", "fp8_quant_act_static", "fp8_quant_weight_tensor",
+           "fp8_quant_act_tensor", "fp8_quant_act_static", "fp8_quant_weight_tensor", "fp8_block_gemm_noalloc",
            "fp8lin_release_graph_scratch", "fp8lin_status_str")
 MAX_LINEAR_M = 64  # the fused-quantization calls take decode-sized batches
 
@@ -66,6 +67,7 @@ def load_library():
             "fp8_quant_weight_tensor": [P, I, I, P, P, P],
             "prune24_compress": [P, P, I, I, P, P, P, P],
             "fp8_block_gemm": [P, P, P, P, I, I, I, P, P],
+            "fp8_block_gemm_noalloc": [P, P, P, P, I, I, I, P, P],
             "fp8lin_release_graph_scratch": [],
             "fp8_sparse24_gemm": [P, P, P, P, P, I, I, I, P, P],
             "fp8_quant_act_ue8m0": [P, I, I, P, P, P],
@@ -213,6 +215,23 @@ def fp8_block_gemm(xq, xs, wq, ws, y: torch.Tensor | None = None):
     _want(ws, "ws", torch.float32, (N // GROUP, K // GROUP))
     y = _out(y, "y", (M, N), torch.bfloat16, xq)
     _check("fp8_block_gemm", load_library().fp8_block_gemm(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _stream(xq)))
+    return y
+
+
+def fp8_block_gemm_noalloc(xq, xs, wq, ws, y: torch.Tensor):
+    """fp8_block_gemm with its split-K partials in the library's fixed device array
+    (no allocation by the library; the caller passes the output y [M,N] bf16)."""
+    xq, wq = _codes(xq), _codes(wq)
+    _want(xq, "xq", torch.uint8)
+    _want(wq, "wq", torch.uint8)
+    M, K = xq.shape
+    N = wq.shape[0]
+    _want(wq, "wq", torch.uint8, (N, K))
+    _want(xs, "xs", torch.float32, (M, K // GROUP))
+    _want(ws, "ws", torch.float32, (N // GROUP, K // GROUP))
+    _want(y, "y", torch.bfloat16, (M, N))
+    _check("fp8_block_gemm_noalloc", load_library().fp8_block_gemm_noalloc(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _stream(xq)))
     return y
 

@@ -184,6 +184,32 @@ fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq
   return finished(e, sc);
 }
 
+fp8l_status fp8_block_gemm_noalloc(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws,
+                                   int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
+  if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N)) return FP8L_ERR_SHAPE;
+  if (M == 0) return FP8L_OK;
+  if (!xq || !xs || !wq || !ws || !y) return FP8L_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y)) return FP8L_ERR_ALIGN;
+  const Range ins[] = {{xq, M * K}, {xs, M * (K / 128) * 4}, {wq, N * K}, {ws, (N / 128) * (K / 128) * 4}};
+  const Range outs[] = {{y, M * N * 2}};
+  if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  const size_t need = fp8lin::gemm_partial_bytes(M, N, K, fp8lin::device_cu_count());
+  float *part = nullptr;
+  if (need > 0) {
+    // the device's copy of the fixed array (address looked up once per device)
+    void *p = nullptr;
+    size_t cap = 0;
+    if (fp8lin::fixed_scratch(&p, &cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return FP8L_ERR_DEVICE;
+    }
+    if (need > cap) return FP8L_ERR_SCRATCH;
+    part = static_cast<float *>(p);
+  }
+  return launched(fp8lin::launch_dense_gemm(xq, xs, wq, ws, M, N, K, y, part, stream));
+}
+
 fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t *wvals, const uint8_t *wmeta,
                               const float *ws, int64_t M, int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N)) return FP8L_ERR_SHAPE;
@@ -343,6 +369,7 @@ const char *fp8lin_status_str(fp8l_status status) {
     case FP8L_ERR_DEVICE: return "no gfx950 (MI355X) device is current";
     case FP8L_ERR_LAUNCH: return "kernel launch failed";
     case FP8L_ERR_MEMORY: return "scratch memory for the call could not be allocated";
+    case FP8L_ERR_SCRATCH: return "the call needs more scratch memory than the library's fixed array holds";
     default: return "unknown status";
   }
 }

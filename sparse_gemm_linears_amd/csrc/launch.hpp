@@ -91,6 +91,9 @@ class CallScratch {
 // Frees the buffers kept for captured calls (all devices).  Only valid when no
 // graph or executable graph that captured a library call exists any more.
 hipError_t release_graph_scratch();
+// The per-device address and size of the library's fixed scratch array (a
+// file-scope device array, no allocation), looked up once per device.
+hipError_t fixed_scratch(void **p, size_t *bytes);
 
 // fp8_quant_act into `tokens` (linear_token_bytes of scratch: codes, then the
 // scales at token_codes_bytes), then gemm(xq, xs) on them: exactly the two

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in range(8):
+    for st in range(9):
         assert sgl.status_str(st) != "unknown status"
     assert sgl.status_str(999) == "unknown status"
 
@@ -122,6 +122,12 @@ def test_gemm_validation(lib):
     assert g(P(A), P(B), P(C), P(D), 16, 128, 128, P(E + 2), None) == sgl.FP8L_ERR_ALIGN
     assert g(P(A), P(B), P(C), P(D), 16, 128, 128, P(C + 16), None) == sgl.FP8L_ERR_ALIAS
     assert g(None, None, P(C), P(D), 0, 128, 128, None, None) == sgl.FP8L_OK
+    n = lib.fp8_block_gemm_noalloc  # the same checks, in the same order
+    assert n(P(A), P(B), P(C), P(D), 16, 100, 128, P(E), None) == sgl.FP8L_ERR_SHAPE
+    assert n(P(A), P(B), P(C), None, 16, 128, 128, P(E), None) == sgl.FP8L_ERR_NULL
+    assert n(P(A), P(B), P(C), P(D), 16, 128, 128, P(E + 2), None) == sgl.FP8L_ERR_ALIGN
+    assert n(P(A), P(B), P(C), P(D), 16, 128, 128, P(C + 16), None) == sgl.FP8L_ERR_ALIAS
+    assert n(None, None, P(C), P(D), 0, 128, 128, None, None) == sgl.FP8L_OK
     h = lib.fp8_sparse24_gemm
     assert h(P(A), P(B), P(C), P(D), P(E), 16, 128, 100, P(F), None) == sgl.FP8L_ERR_SHAPE
     assert h(P(A), P(B), None, P(D), P(E), 16, 128, 128, P(F), None) == sgl.FP8L_ERR_NULL
@@ -165,6 +171,7 @@ def test_valid_call_without_gpu_reports_device(lib):
     assert lib.fp8_quant_act(P(A), 4, 128, P(B), P(C), None) == sgl.FP8L_ERR_DEVICE
     assert lib.fp8_block_gemm(P(A), P(B), P(C), P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_DEVICE
     assert lib.fp8_block_linear(P(A), P(C), P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_DEVICE
+    assert lib.fp8_block_gemm_noalloc(P(A), P(B), P(C), P(D), 16, 128, 128, P(E), None) == sgl.FP8L_ERR_DEVICE
     # nothing kept for graphs: releasing is a no-op that needs no device
     assert lib.fp8lin_release_graph_scratch() == sgl.FP8L_OK
 

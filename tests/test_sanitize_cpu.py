@@ -24,7 +24,7 @@ HERE = os.path.join(ROOT, "tests", "sanitize")
 CSRC = os.path.join(ROOT, "sparse_gemm_linears_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANGXX = "/opt/rocm/llvm/bin/clang++"
-LIB_SOURCES = ["api", "quant", "prune24", "gemm_dense", "gemm_sparse", "workspace"]
+LIB_SOURCES = ["api", "quant", "prune24", "gemm_dense", "gemm_sparse", "workspace", "fixed_scratch"]
 
 
 def _run(cmd, env=None, timeout=600):
