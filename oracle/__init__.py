@@ -73,6 +73,7 @@ def _load():
             lib.oracle_quant_wblock_ue8m0.argtypes = [P, I, I, P, P]
             lib.oracle_prune24_mask.argtypes = [P, P, I, I, P]
             lib.oracle_prune24_compress.argtypes = [P, P, I, I, P, P, P]
+            lib.oracle_prune24_compress_tensor.argtypes = [P, P, I, I, P, P, P]
             lib.oracle_decompress24.argtypes = [P, P, I, I, P]
             lib.oracle_gemm.argtypes = [P, P, P, P, I, I, I, P]
             lib.oracle_gemm_rows.argtypes = [P, P, P, P, I, I, I, P, I, P]
@@ -80,7 +81,8 @@ def _load():
             for f in ("oracle_quant_act", "oracle_quant_wblock", "oracle_quant_act_ue8m0",
                       "oracle_quant_act_static", "oracle_quant_act_tensor",
                       "oracle_quant_wblock_ue8m0", "oracle_prune24_mask",
-                      "oracle_prune24_compress", "oracle_decompress24", "oracle_gemm",
+                      "oracle_prune24_compress", "oracle_prune24_compress_tensor", "oracle_decompress24",
+                      "oracle_gemm",
                       "oracle_gemm_rows"):
                 getattr(lib, f).restype = None
             _lib = lib
@@ -180,6 +182,25 @@ def prune24_compress(w_bf16: np.ndarray, col_norm: np.ndarray | None = None):
     s = np.empty((N // GROUP, K // GROUP), np.float32)
     _load().oracle_prune24_compress(_ptr(w), None if c is None else _ptr(c), N, K,
                                     _ptr(vals), _ptr(meta), _ptr(s))
+    return vals, meta, s
+
+
+def prune24_compress_tensor(w_bf16: np.ndarray, col_norm: np.ndarray | None = None):
+    """Prune 2:4 and compress as ``prune24_compress``, with one scale for the whole tensor:
+    amax over all kept values / 448, written to every entry of the [N/128,K/128] scale array.
+
+    Returns (vals [N,K/2] u8, meta [N,K/8] u8, scales [N/128,K/128] f32, all equal).
+    """
+    _check_bf16(w_bf16, "w")
+    w = np.ascontiguousarray(w_bf16)
+    N, K = w.shape
+    assert N % GROUP == 0 and K % GROUP == 0
+    c = None if col_norm is None else np.ascontiguousarray(col_norm, dtype=np.float32)
+    vals = np.empty((N, K // 2), np.uint8)
+    meta = np.empty((N, K // 8), np.uint8)
+    s = np.empty((N // GROUP, K // GROUP), np.float32)
+    _load().oracle_prune24_compress_tensor(_ptr(w), None if c is None else _ptr(c), N, K,
+                                           _ptr(vals), _ptr(meta), _ptr(s))
     return vals, meta, s
 
 

@@ -224,6 +224,40 @@ void oracle_prune24_compress(const uint16_t *w, const float *c, int64_t N, int64
     free(keep);
 }
 
+/*
+ * The same prune and compression with one scale for the whole tensor
+ * ("Deployer la parcimonie 2:4 avec FP8 sur Hopper": pipeline step 3, FP8 with
+ * a per-tensor scale; step 6, the scale re-derived after pruning): amax over
+ * every kept value of W, s = amax / 448 (fp32), kept codes enc(fp32(w / s)),
+ * s written to every entry of the [N/128, K/128] scale array.
+ */
+void oracle_prune24_compress_tensor(const uint16_t *w, const float *c, int64_t N, int64_t K,
+                                    uint8_t *vals, uint8_t *meta, float *s) {
+    int64_t NB = N / G, KB = K / G;
+    uint8_t *keep = (uint8_t *)malloc((size_t)(N * K));
+    oracle_prune24_mask(w, c, N, K, keep);
+    float amax = 0.0f;
+    for (int64_t i = 0; i < N * K; i++) {
+        float a = keep[i] ? fabsf(bf16_to_f32(w[i])) : 0.0f;
+        if (a > amax) amax = a;
+    }
+    float sc = amax / 448.0f;
+    for (int64_t i = 0; i < NB * KB; i++) s[i] = sc;
+    memset(meta, 0, (size_t)(N * K / 8));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t g = 0; g < K / 4; g++) {
+            int kept[2], nk = 0;
+            for (int j = 0; j < 4; j++)
+                if (keep[n * K + 4 * g + j]) kept[nk++] = j;
+            vals[n * (K / 2) + 2 * g] = quantize_one(bf16_to_f32(w[n * K + 4 * g + kept[0]]), sc);
+            vals[n * (K / 2) + 2 * g + 1] = quantize_one(bf16_to_f32(w[n * K + 4 * g + kept[1]]), sc);
+            uint8_t nib = (uint8_t)(kept[0] | (kept[1] << 2));
+            meta[n * (K / 8) + g / 2] |= (uint8_t)(nib << (4 * (g % 2)));
+        }
+    free(keep);
+}
+
 /* Inverse of the packing: dense codes [N,K] with 0x00 at the pruned places. */
 void oracle_decompress24(const uint8_t *vals, const uint8_t *meta, int64_t N, int64_t K, uint8_t *q) {
     memset(q, 0, (size_t)(N * K));

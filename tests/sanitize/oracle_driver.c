@@ -19,6 +19,8 @@ void oracle_quant_wblock(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, fl
 void oracle_prune24_mask(const uint16_t *w, const float *c, int64_t N, int64_t K, uint8_t *keep);
 void oracle_prune24_compress(const uint16_t *w, const float *c, int64_t N, int64_t K, uint8_t *vals, uint8_t *meta,
                              float *s);
+void oracle_prune24_compress_tensor(const uint16_t *w, const float *c, int64_t N, int64_t K, uint8_t *vals,
+                                    uint8_t *meta, float *s);
 void oracle_decompress24(const uint8_t *vals, const uint8_t *meta, int64_t N, int64_t K, uint8_t *q);
 void oracle_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
                  int64_t K, double *y);
@@ -83,6 +85,9 @@ static int run_shape(int64_t M, int64_t N, int64_t K) {
     for (int pass = 0; pass < 2; pass++) {
         const float *cn = pass ? c : NULL;
         oracle_prune24_mask(w, cn, N, K, keep);
+        oracle_prune24_compress_tensor(w, cn, N, K, vals, meta, s2);
+        for (int64_t i = 1; i < (N / 128) * (K / 128); i++)
+            if (s2[i] != s2[0]) bad |= fail("one tensor scale");
         oracle_prune24_compress(w, cn, N, K, vals, meta, s2);
         oracle_decompress24(vals, meta, N, K, dq);
         for (int64_t i = 0; i < N * K; i += 4) {

@@ -407,6 +407,50 @@ def test_compress_roundtrip_and_cross_path_identity():
         assert np.array_equal(vals.reshape(256, 128, 2)[..., 0], qd.reshape(256, 128, 4)[rows, grp, i0])
 
 
+def test_compress_tensor_equals_tensor_quantization_of_the_pruned_weight():
+    """Per-tensor 2:4 compression is the per-tensor quantization of mask * W, packed:
+    the same mask as the block form, one scale (amax over the kept values / 448), and
+    codes equal to those the per-tensor weight quantizer gives the pruned weight."""
+    w = si.weights(384, 640)
+    c = si.column_norms(si.calibration_batch(640))
+    for cn in (None, c):
+        vals, meta, s = oracle.prune24_compress_tensor(w, cn)
+        keep = oracle.prune24_mask(w, cn)
+        vb, mb, _ = oracle.prune24_compress(w, cn)
+        assert np.array_equal(meta, mb)                      # the mask does not depend on the scale
+        wp = np.where(keep, w, np.uint16(0)).astype(np.uint16)
+        q, st = oracle.quant_weight_tensor(wp)
+        assert np.all(s == s.flat[0]) and np.array_equal(s, st)
+        kept_amax = np.abs(si.bf16_bits_to_f32(w)[keep]).max()
+        assert s.flat[0] == np.float32(kept_amax) / np.float32(448)
+        assert np.array_equal(oracle.decompress24(vals, meta), q)
+
+
+def test_compress_tensor_exact_small():
+    """Exact rational arithmetic on one 128 x 128 weight: the tensor scale and every kept code."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((128, 128)) * 2.0 ** rng.integers(-8, 8, (128, 1))).astype(np.float32)
+    w = _bf16_bits(x)
+    vals, meta, s = oracle.prune24_compress_tensor(w)
+    keep = oracle.prune24_mask(w)
+    kept = [bf16_value(int(b)) for b in w[keep]]
+    s_ref, codes = quantize_exact(kept, amax=max(abs(v) for v in kept))
+    assert s[0, 0] == np.float32(s_ref)
+    assert oracle.decompress24(vals, meta)[keep].tolist() == codes
+
+
+def test_compress_tensor_equals_block_form_when_blocks_share_the_amax():
+    """Where every 128 x 128 block's kept maximum is the tensor's, the two forms agree."""
+    w = si.weights(256, 512).copy()
+    big = _bf16_bits([3.0])[0]
+    for nb in range(2):
+        for kb in range(4):
+            w[nb * 128 + 5, kb * 128 + 8] = big                    # a kept value (largest of its group)
+    vb, mb, sb = oracle.prune24_compress(w)
+    vt, mt, st = oracle.prune24_compress_tensor(w)
+    assert np.array_equal(sb, st) and np.array_equal(vb, vt) and np.array_equal(mb, mt)
+
+
 def test_compress_nibble_order_by_hand():
     w = np.zeros((128, 128), np.float32)
     w[0, 0:4] = [0, 5, 0, 7]       # group 0 keeps (1,3) -> nibble 1 | 3<<2 = 13
