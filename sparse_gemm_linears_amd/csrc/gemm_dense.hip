@@ -60,72 +60,96 @@ struct TileExtra {
 
 // SwiGLU epilogue.  The two waves with the same token slice hold the gate
 // (wn0 = 0) and up (wn0 = 128) sums of the same 128 outputs in the same
-// register layout; per token tile the up wave hands its fp32 sums to the gate
-// wave through LDS, and the gate wave forms h = silu(g) * u = g * u / (1 +
-// exp(-g)) in fp32, stores bf16(h) and, if asked, quantizes bf16(h) as
-// fp8_quant_act would: the tile's 128 outputs are exactly one 1x128 group of a
-// token, held by the four lane groups of the token's lanes (two xor-shuffles
-// give the group amax).
+// register layout.  The work is split between them by token tile: in round p
+// the gate wave finishes token tile 2p and the up wave token tile 2p + 1, each
+// after receiving the other wave's sums of its tile through LDS (xch_g holds
+// gate sums sent to the up wave, xch_u up sums sent to the gate wave).  A wave
+// forms h = silu(g) * u = g * u / (1 + exp(-g)) in fp32, stores bf16(h) and, if
+// asked, quantizes bf16(h) as fp8_quant_act would: the tile's 128 outputs are
+// exactly one 1x128 group of a token, held by the four lane groups of the
+// token's lanes (two xor-shuffles give the group amax).
 template <class C>
-__device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *xch, uint8_t *scratch, uint16_t *h,
-                                                const TileExtra &so, int M, int m_wave, int tn, int wave, int wn0,
-                                                int lane) {
-  const int lr = lane & 15, g = lane >> 4, slot = wave % C::kWavesPerSlice;
+__device__ __forceinline__ void swiglu_finish(const v4f (&gv)[C::RT], const v4f (&uv)[C::RT], uint8_t *scratch,
+                                              uint16_t *h, const TileExtra &so, int M, int m0, int tn, int lane) {
+  const int lr = lane & 15, g = lane >> 4;
+  v4f hv[C::RT];
+#pragma unroll
+  for (int r = 0; r < C::RT; r++) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      // silu with the hardware exp2 and reciprocal (a few ulp in fp32, far
+      // below the bf16 rounding that follows); the bf16 value is what h holds
+      // in memory and what the codes are made from
+      const float gg = gv[r][e];
+      hv[r][e] = bf16_to_f32(f32_to_bf16_rne(gg * uv[r][e] * __builtin_amdgcn_rcpf(1.0f + __expf(-gg))));
+    }
+  }
+  store_token_tile<C::RT>(scratch, hv, h, M, so.I, m0, 128 * tn, lane);
+  if (!so.hq) return;
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int r = 0; r < C::RT; r++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) amax_bits = max(amax_bits, __float_as_uint(hv[r][e]) & 0x7FFFFFFFu);
+  amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 16, 64));
+  amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 32, 64));
+  const GroupScale gs = group_scale(amax_bits);
+  uint32_t words[C::RT];
+#pragma unroll
+  for (int r = 0; r < C::RT; r++) {
+    const float v[4] = {hv[r][0], hv[r][1], hv[r][2], hv[r][3]};
+    words[r] = quantize4_group(v, gs);
+  }
+  // codes through the wave's LDS scratch (16 rows x 128 bytes, 16-byte chunks
+  // XOR-swizzled by row) so that each row goes out as 128 contiguous bytes
+#pragma unroll
+  for (int r = 0; r < C::RT; r++)
+    *reinterpret_cast<uint32_t *>(scratch + lr * 128 + ((r ^ (lr & 7)) << 4) + 4 * g) = words[r];
+  if (g == 0 && m0 + lr < M) so.hs[(int64_t)(m0 + lr) * (so.I / kGroup) + tn] = gs.s;
+#pragma unroll
+  for (int p = 0; p < 2; p++) {
+    const int row = 8 * p + (lane >> 3), chunk = lane & 7;
+    const v4i v = *reinterpret_cast<const v4i *>(scratch + row * 128 + ((chunk ^ (row & 7)) << 4));
+    if (m0 + row < M) *reinterpret_cast<v4i *>(so.hq + (int64_t)(m0 + row) * so.I + 128 * tn + 16 * chunk) = v;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[C::RT][C::CT], v4f *xch_g, v4f *xch_u, uint8_t *scratch,
+                                                uint16_t *h, const TileExtra &so, int M, int m_wave, int tn, int wave,
+                                                int wn0, int lane) {
+  static_assert(C::CT % 2 == 0, "token tiles are shared out in pairs");
+  static_assert(C::kWavesPerSlice * C::RT * 64 * 16 <= C::kBTile, "one exchange direction fits in a token stage");
+  const int slot = wave % C::kWavesPerSlice;
   const bool gate = wn0 == 0;
 #pragma unroll
-  for (int c = 0; c < C::CT; c++) {
-    if (!gate) {
+  for (int p = 0; p < C::CT / 2; p++) {
+    constexpr int kRow = C::RT * 64;
+    v4f *mine = (gate ? xch_g : xch_u) + slot * kRow + lane;  // what this wave sends
+    const v4f *theirs = (gate ? xch_u : xch_g) + slot * kRow + lane;
+    // the gate wave sends tile 2p + 1, the up wave tile 2p (compile-time
+    // register indices in both branches)
+    if (gate) {
 #pragma unroll
-      for (int r = 0; r < C::RT; r++) xch[(slot * C::RT + r) * 64 + lane] = acc[r][c];
+      for (int r = 0; r < C::RT; r++) mine[r * 64] = acc[r][2 * p + 1];
+    } else {
+#pragma unroll
+      for (int r = 0; r < C::RT; r++) mine[r * 64] = acc[r][2 * p];
     }
     __syncthreads();
+    v4f other[C::RT];
+#pragma unroll
+    for (int r = 0; r < C::RT; r++) other[r] = theirs[r * 64];
     if (gate) {
-      v4f hv[C::RT];
+      v4f gv[C::RT];
 #pragma unroll
-      for (int r = 0; r < C::RT; r++) {
-        const v4f u = xch[(slot * C::RT + r) * 64 + lane];
+      for (int r = 0; r < C::RT; r++) gv[r] = acc[r][2 * p];
+      swiglu_finish<C>(gv, other, scratch, h, so, M, m_wave + 32 * p, tn, lane);
+    } else {
+      v4f uv[C::RT];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float gv = acc[r][c][e];
-          // silu with the hardware exp2 and reciprocal (a few ulp in fp32,
-          // far below the bf16 rounding that follows); the bf16 value is
-          // what h holds in memory and what the codes are made from
-          hv[r][e] = bf16_to_f32(f32_to_bf16_rne(gv * u[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv))));
-        }
-      }
-      const int m0 = m_wave + 16 * c;
-      store_token_tile<C::RT>(scratch, hv, h, M, so.I, m0, 128 * tn, lane);
-      if (so.hq) {
-        uint32_t amax_bits = 0;
-#pragma unroll
-        for (int r = 0; r < C::RT; r++)
-#pragma unroll
-          for (int e = 0; e < 4; e++) amax_bits = max(amax_bits, __float_as_uint(hv[r][e]) & 0x7FFFFFFFu);
-        amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 16, 64));
-        amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 32, 64));
-        const GroupScale gs = group_scale(amax_bits);
-        const float sc = gs.s;
-        uint32_t words[C::RT];
-#pragma unroll
-        for (int r = 0; r < C::RT; r++) {
-          const float v[4] = {hv[r][0], hv[r][1], hv[r][2], hv[r][3]};
-          words[r] = quantize4_group(v, gs);
-        }
-        // codes through the wave's LDS scratch (16 rows x 128 bytes, 16-byte
-        // chunks XOR-swizzled by row) so that each row goes out as 128
-        // contiguous bytes
-#pragma unroll
-        for (int r = 0; r < C::RT; r++)
-          *reinterpret_cast<uint32_t *>(scratch + lr * 128 + ((r ^ (lr & 7)) << 4) + 4 * g) = words[r];
-        if (g == 0 && m0 + lr < M) so.hs[(int64_t)(m0 + lr) * (so.I / kGroup) + tn] = sc;
-#pragma unroll
-        for (int p = 0; p < 2; p++) {
-          const int row = 8 * p + (lane >> 3), chunk = lane & 7;
-          const v4i v = *reinterpret_cast<const v4i *>(scratch + row * 128 + ((chunk ^ (row & 7)) << 4));
-          if (m0 + row < M)
-            *reinterpret_cast<v4i *>(so.hq + (int64_t)(m0 + row) * so.I + 128 * tn + 16 * chunk) = v;
-        }
-      }
+      for (int r = 0; r < C::RT; r++) uv[r] = acc[r][2 * p + 1];
+      swiglu_finish<C>(other, uv, scratch, h, so, M, m_wave + 32 * p + 16, tn, lane);
     }
     __syncthreads();
   }
@@ -390,8 +414,8 @@ __global__ __launch_bounds__(WN *WM * 64) void dense_tile_kernel(
       store_token_tile<C::RT>(scratch, col, y, M, N, m_base + wm0 + 16 * c, n_base + wn0, lane);
     }
   } else {
-    swiglu_epilogue<C>(acc, reinterpret_cast<v4f *>(lds_b0), scratch, y, so, M, m_base + wm0, tn, wave, wn0,
-                       lane);
+    swiglu_epilogue<C>(acc, reinterpret_cast<v4f *>(lds_b0), reinterpret_cast<v4f *>(lds_b1), scratch, y, so, M,
+                       m_base + wm0, tn, wave, wn0, lane);
   }
 }
 
@@ -558,12 +582,10 @@ static hipError_t tile_gemm(const uint8_t *xq, const S *xs, const uint8_t *wq, c
                             uint16_t *y, float *part, hipStream_t stream) {
   const TilePlan p = plan_tiles(m, n, k, device_cu_count());
   if (p.splits > 1 && !part) return hipErrorInvalidValue;
-  hipError_t e =
-      p.bm == 128
-          ? launch_tile<256, 128, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split,
-                                            p.splits > 1 ? part : nullptr, stream)
-          : launch_tile<256, 256, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split,
-                                            p.splits > 1 ? part : nullptr, stream);
+  float *pp = p.splits > 1 ? part : nullptr;
+  hipError_t e = p.bm == 128
+                     ? launch_tile<256, 128, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, pp, stream)
+                     : launch_tile<256, 256, 2, 4, E8>(xq, xs, wq, ws, m, n, k, y, p.splits, p.kb_split, pp, stream);
   // (launch_tile writes y itself when it gets no partials)
   if (p.splits > 1 && e == hipSuccess) e = launch_splitk_reduce(part, p.splits, (int64_t)m * n, y, stream);
   return e;
