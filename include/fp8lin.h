@@ -179,6 +179,20 @@ fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N
                              uint8_t *vals, uint8_t *meta, float *s, hipStream_t stream);
 
 /*
+ * The same 2:4 prune and compression with one scale for the whole tensor
+ * ("Deployer la parcimonie 2:4 avec FP8 sur Hopper": pipeline step 3, FP8 with
+ * a per-tensor scale; step 6, the scale re-derived after pruning).  The mask,
+ * vals and meta follow prune24_compress; the scale is s = fp32(amax / 448)
+ * with amax the largest kept magnitude of all of W, the kept codes are
+ * enc(fp32(w / s)), and s is written to every entry of the [N/128,K/128] scale
+ * array, so fp8_sparse24_gemm takes the result unchanged.  Three launches on
+ * the stream; s[0] holds partial maxima between them, so s must not be read
+ * before the call's work on the stream is done.
+ */
+fp8l_status prune24_compress_tensor(const uint16_t *w, const float *col_norm, int64_t N, int64_t K,
+                                    uint8_t *vals, uint8_t *meta, float *s, hipStream_t stream);
+
+/*
  * Block-scaled FP8 GEMM with fp32 accumulation ("FP8 a granularite fine",
  * section "Chemin rapide de DeepGEMM": every FP8 linear with (128,128) weight
  * blocks and dynamic activations runs as a block-scaled FP8 GEMM).
@@ -229,9 +243,12 @@ fp8l_status fp8_block_gemm_noalloc(const uint8_t *xq, const float *xs, const uin
  * keep its running sums in units of the current K block's scale (rescaled by
  * the ratio of consecutive scales, the last scale applied at the end) when
  * every scale product it uses is a normal fp32 number in [2^-100, 2^100], all
- * within 2^60 of each other, and no scale is zero; otherwise it adds scaled
- * partials.  The two differ only in fp32 rounding (about one ulp per K block
- * for the rescaling); results are deterministic either way.
+ * within 2^60 of each other, and no scale is zero; where every scale product
+ * a wave uses is the same in all of those K blocks (per-tensor scales, as
+ * from fp8_quant_act_tensor and prune24_compress_tensor), it sums the
+ * unscaled block products and applies the one scale at the end; otherwise it
+ * adds scaled partials.  The forms differ only in fp32 rounding (about one ulp
+ * per K block for the rescaling); results are deterministic either way.
  */
 fp8l_status fp8_sparse24_gemm(const uint8_t *xq, const float *xs, const uint8_t *wvals,
                               const uint8_t *wmeta, const float *ws, int64_t M, int64_t N,

@@ -32,7 +32,8 @@ FP8L_ERR_SCRATCH = 8
 EXPORTS = ("fp8_quant_act", "fp8_quant_weight_block", "prune24_compress", "fp8_block_gemm",
            "fp8_sparse24_gemm", "fp8_quant_act_ue8m0", "fp8_quant_weight_block_ue8m0", "fp8_block_gemm_ue8m0",
            "fp8_grouped_gemm", "fp8_block_gemm_swiglu", "fp8_block_linear", "fp8_sparse24_linear",
-           "fp8_quant_act_tensor", "fp8_quant_act_static", "fp8_quant_weight_tensor", "fp8_block_gemm_noalloc",
+           "fp8_quant_act_tensor", "fp8_quant_act_static", "fp8_quant_weight_tensor", "prune24_compress_tensor",
+           "fp8_block_gemm_noalloc",
            "fp8lin_release_graph_scratch", "fp8lin_status_str")
 MAX_LINEAR_M = 64  # the fused-quantization calls take decode-sized batches
 
@@ -66,6 +67,7 @@ def load_library():
             "fp8_quant_act_static": [P, P, I, I, P, P, P],
             "fp8_quant_weight_tensor": [P, I, I, P, P, P],
             "prune24_compress": [P, P, I, I, P, P, P, P],
+            "prune24_compress_tensor": [P, P, I, I, P, P, P, P],
             "fp8_block_gemm": [P, P, P, P, I, I, I, P, P],
             "fp8_block_gemm_noalloc": [P, P, P, P, I, I, I, P, P],
             "fp8lin_release_graph_scratch": [],
@@ -199,6 +201,20 @@ def prune24_compress(w: torch.Tensor, col_norm: torch.Tensor | None = None, vals
     meta = _out(meta, "meta", (N, K // 8), torch.uint8, w)
     s = _out(s, "s", (N // GROUP, K // GROUP), torch.float32, w)
     _check("prune24_compress", load_library().prune24_compress(
+        _ptr(w), _ptr(col_norm), N, K, _ptr(vals), _ptr(meta), _ptr(s), _stream(w)))
+    return vals, meta, s
+
+
+def prune24_compress_tensor(w: torch.Tensor, col_norm: torch.Tensor | None = None, vals=None, meta=None, s=None):
+    """prune24_compress with one per-tensor scale (broadcast into s [N/128,K/128])."""
+    _want(w, "w", torch.bfloat16)
+    N, K = w.shape
+    if col_norm is not None:
+        _want(col_norm, "col_norm", torch.float32, (K,))
+    vals = _out(vals, "vals", (N, K // 2), torch.uint8, w)
+    meta = _out(meta, "meta", (N, K // 8), torch.uint8, w)
+    s = _out(s, "s", (N // GROUP, K // GROUP), torch.float32, w)
+    _check("prune24_compress_tensor", load_library().prune24_compress_tensor(
         _ptr(w), _ptr(col_norm), N, K, _ptr(vals), _ptr(meta), _ptr(s), _stream(w)))
     return vals, meta, s
 

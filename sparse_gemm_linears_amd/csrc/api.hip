@@ -167,6 +167,20 @@ fp8l_status prune24_compress(const uint16_t *w, const float *col_norm, int64_t N
   return launched(fp8lin::launch_prune24(w, col_norm, N, K, vals, meta, s, stream));
 }
 
+fp8l_status prune24_compress_tensor(const uint16_t *w, const float *col_norm, int64_t N, int64_t K, uint8_t *vals,
+                                    uint8_t *meta, float *s, hipStream_t stream) {
+  if (bad_nk(N, K)) return FP8L_ERR_SHAPE;
+  if (!w || !vals || !meta || !s) return FP8L_ERR_NULL;
+  if (!aligned16(w) || !aligned16(vals) || !aligned16(meta) || !aligned16(s) ||
+      (col_norm && !aligned16(col_norm)))
+    return FP8L_ERR_ALIGN;
+  const Range ins[] = {{w, N * K * 2}, {col_norm, col_norm ? K * 4 : 0}};
+  const Range outs[] = {{vals, N * K / 2}, {meta, N * K / 8}, {s, (N / 128) * (K / 128) * 4}};
+  if (any_alias(outs, 3, ins, 2)) return FP8L_ERR_ALIAS;
+  if (fp8l_status st = check_device()) return st;
+  return launched(fp8lin::launch_prune24_tensor(w, col_norm, N, K, vals, meta, s, stream));
+}
+
 fp8l_status fp8_block_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,
                            int64_t N, int64_t K, uint16_t *y, hipStream_t stream) {
   if (bad_mk(M, K) || bad_nk(N, K) || bad_mn(M, N)) return FP8L_ERR_SHAPE;

@@ -77,6 +77,7 @@ void sparse_tile_kernel(const uint8_t *__restrict__ xq,
   __shared__ __align__(16) uint8_t lds_b0[C::kBTile], lds_b1[C::kBTile];
   __shared__ __align__(16) float lds_s[2 * SB * BM];
   __shared__ uint32_t xs_range[BM];  // per token: exponent range of its scales (see below)
+  __shared__ uint32_t xs_const[BM];  // per token: all its scales over the K range equal
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
@@ -178,14 +179,21 @@ void sparse_tile_kernel(const uint8_t *__restrict__ xq,
   // and the last scale is applied once at the end.  The plain form needs a
   // cleared partial per MFMA (the sparse MFMA accumulates into its
   // destination, so two register moves) and an FMA per output.
-  bool ratio_form = false;
+  // Unit form: where every scale product the wave uses is the same in every
+  // K block (per-tensor scales, or per-token activation scales with one
+  // weight scale per row block), the sparse MFMAs accumulate the unscaled
+  // block sums straight into acc and the one scale is applied at the end: no
+  // VALU work per MFMA at all.
+  bool ratio_form = false, unit_form = false;
   float unit[C::CT];
 #pragma unroll
   for (int c = 0; c < C::CT; c++) unit[c] = 1.f;
 
+  // form_tag: 0 plain, 1 ratio, 2 unit
   auto step = [&](int kb, auto st_tag, auto form_tag) {
     constexpr int ST = decltype(st_tag)::value;
-    constexpr bool kRatio = decltype(form_tag)::value;
+    constexpr int kForm = decltype(form_tag)::value;
+    constexpr bool kRatio = kForm == 1, kUnit = kForm == 2;
     const bool more = kb + 1 < KB;
     const bool scale_load = (kb % SB == 0) && (kb + SB < KB);
     if (scale_load) scales.load(kb / SB + 1);
@@ -204,9 +212,30 @@ void sparse_tile_kernel(const uint8_t *__restrict__ xq,
 #pragma unroll
     for (int c = 0; c < C::CT; c++) {
       bf[c] = load_frag_at(ST ? lds_b1 : lds_b0, b_lo, b_hi, c * 2048);
-      scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
+      if constexpr (!kUnit) scl[c] = scales.get(kb, wm0 + 16 * c + lr) * sw;
     }
-    if constexpr (kRatio) {
+    if constexpr (kUnit) {
+#pragma unroll
+      for (int r = 0; r < C::RT; r++) {
+        if (more && r < kCopyRows) {
+#pragma unroll
+          for (int j = r * kCopiesPerRow; j < (r + 1) * kCopiesPerRow && j < kCopies; j++)
+            issue_copy(kb + 1, ST ^ 1, j);
+        }
+        const v4i af = af_next;
+        const int ix = ix_next;
+        if (r + 1 < C::RT) {
+          af_next = make_v4i(*reinterpret_cast<const uint4 *>(Vt + v_off + (r + 1) * 1024));
+          ix_next = *reinterpret_cast<const int *>(Mt + m_off + (r + 1) * 256);
+        }
+#pragma unroll
+        for (int c = 0; c < C::CT; c++) {
+          acc[r][c] = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(af, bf[c], acc[r][c], ix, 0, 0);
+          pin(acc[r][c]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (kRatio) {
       float ratio[C::CT];
 #pragma unroll
       for (int c = 0; c < C::CT; c++) {
@@ -285,21 +314,25 @@ void sparse_tile_kernel(const uint8_t *__restrict__ xq,
   // While the first copies are in flight: the exponent range of every token
   // scale of the tile over this K range, per token (kTpt threads per token,
   // combined in consecutive lanes), into xs_range as (min << 8) | max of the
-  // biased exponents, or ~0 when a scale is zero, subnormal or not finite.
+  // biased exponents, or ~0 when a scale is zero, subnormal or not finite;
+  // and into xs_const whether all of the token's scales are the same bits.
   {
     constexpr int kTpt = C::kThreads / BM;
     static_assert(kTpt == 2 || kTpt == 4, "threads per token in the scale scan");
     const int tt = tid / kTpt, part = tid % kTpt;
-    uint32_t lo = 255u, hi = 0u, odd = 0u;
+    uint32_t lo = 255u, hi = 0u, odd = 0u, blo = ~0u, bhi = 0u;
     if (try_ratio && m_base + tt < M) {
       const float *row = xs + (int64_t)(m_base + tt) * KBs;
       const int chunk = (KB + kTpt - 1) / kTpt, k0 = part * chunk, k1 = min(KB, k0 + chunk);
 #pragma unroll 8
       for (int kb = k0; kb < k1; kb++) {
-        const uint32_t e = (__float_as_uint(row[kb]) & 0x7FFFFFFFu) >> 23;
+        const uint32_t bits = __float_as_uint(row[kb]);
+        const uint32_t e = (bits & 0x7FFFFFFFu) >> 23;
         odd |= (uint32_t)(e == 0u || e == 255u);
         lo = min(lo, e);
         hi = max(hi, e);
+        blo = min(blo, bits);
+        bhi = max(bhi, bits);
       }
     }
 #pragma unroll
@@ -307,22 +340,32 @@ void sparse_tile_kernel(const uint8_t *__restrict__ xq,
       lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
       hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
       odd |= (uint32_t)__shfl_xor((int)odd, off, 64);
+      blo = min(blo, (uint32_t)__shfl_xor((int)blo, off, 64));
+      bhi = max(bhi, (uint32_t)__shfl_xor((int)bhi, off, 64));
     }
-    if (part == 0) xs_range[tt] = odd ? ~0u : (lo << 8) | hi;
+    if (part == 0) {
+      xs_range[tt] = odd ? ~0u : (lo << 8) | hi;
+      xs_const[tt] = blo == bhi ? 1u : 0u;
+    }
   }
   // the same for this wave's weight scale row (every lane of the wave)
-  uint32_t wlo = 255u, whi = 0u, wodd = 0u;
+  uint32_t wlo = 255u, whi = 0u, wodd = 0u, wblo = ~0u, wbhi = 0u;
   for (int kb = try_ratio ? lane : KB; kb < KB; kb += 64) {
-    const uint32_t e = (__float_as_uint(ws_row[kb]) & 0x7FFFFFFFu) >> 23;
+    const uint32_t bits = __float_as_uint(ws_row[kb]);
+    const uint32_t e = (bits & 0x7FFFFFFFu) >> 23;
     wodd |= (uint32_t)(e == 0u || e == 255u);
     wlo = min(wlo, e);
     whi = max(whi, e);
+    wblo = min(wblo, bits);
+    wbhi = max(wbhi, bits);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     wlo = min(wlo, (uint32_t)__shfl_xor((int)wlo, off, 64));
     whi = max(whi, (uint32_t)__shfl_xor((int)whi, off, 64));
     wodd |= (uint32_t)__shfl_xor((int)wodd, off, 64);
+    wblo = min(wblo, (uint32_t)__shfl_xor((int)wblo, off, 64));
+    wbhi = max(wbhi, (uint32_t)__shfl_xor((int)wbhi, off, 64));
   }
   wait_global_loads();
   scales.store(0);
@@ -349,18 +392,37 @@ void sparse_tile_kernel(const uint8_t *__restrict__ xq,
       }
     }
     ratio_form = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64(!ok) == 0)) != 0;
+    // the unit form: every scale of the wave's tokens and of its weight block
+    // row the same over the K range (any value, zero included: the sums are
+    // exact block sums, scaled once)
+    bool same = try_ratio && wblo == wbhi;
+#pragma unroll
+    for (int c = 0; c < C::CT; c++) {
+      const int tok = wm0 + 16 * c + lr;
+      if (m_base + tok < M) same = same && xs_const[tok] != 0u;
+    }
+    unit_form = __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_ballot_w64(!same) == 0)) != 0;
+    if (unit_form) {
+#pragma unroll
+      for (int c = 0; c < C::CT; c++) unit[c] = scales.get(0, wm0 + 16 * c + lr) * sw_cur;
+    }
   }
-  // two separate loops, one per form, so that each is register-allocated on
-  // its own; every wave passes the same barriers in either
-  if (ratio_form) {
+  // separate loops, one per form, so that each is register-allocated on its
+  // own; every wave passes the same barriers in any of them
+  if (unit_form) {
     for (int kb = 0; kb < KB; kb += 2) {
-      step(kb, std::integral_constant<int, 0>{}, std::true_type{});
-      if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{}, std::true_type{});
+      step(kb, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
+      if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+    }
+  } else if (ratio_form) {
+    for (int kb = 0; kb < KB; kb += 2) {
+      step(kb, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     }
   } else {
     for (int kb = 0; kb < KB; kb += 2) {
-      step(kb, std::integral_constant<int, 0>{}, std::false_type{});
-      if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
+      step(kb, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      if (kb + 1 < KB) step(kb + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
     }
   }
 
@@ -370,7 +432,7 @@ void sparse_tile_kernel(const uint8_t *__restrict__ xq,
 #pragma unroll
   for (int c = 0; c < C::CT; c++) {
     v4f col[C::RT];
-    const float u = ratio_form ? unit[c] : 1.f;
+    const float u = (ratio_form || unit_form) ? unit[c] : 1.f;
 #pragma unroll
     for (int r = 0; r < C::RT; r++) col[r] = acc[r][c] * u;
     if constexpr (PARTIAL)

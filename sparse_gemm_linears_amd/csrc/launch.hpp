@@ -122,6 +122,12 @@ hipError_t launch_dense_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const u
                                    int64_t M, int64_t N, int64_t K, uint16_t *y, float *part, hipStream_t stream);
 hipError_t launch_prune24(const uint16_t *w, const float *col_norm, int64_t N, int64_t K, uint8_t *vals,
                           uint8_t *meta, float *s, hipStream_t stream);
+// 2:4 prune with one per-tensor scale (three launches; s[0] holds partial
+// maxima between them).
+hipError_t launch_prune24_tensor(const uint16_t *w, const float *col_norm, int64_t N, int64_t K, uint8_t *vals,
+                                 uint8_t *meta, float *s, hipStream_t stream);
+// s[0] = (largest of the n_part bf16 magnitude bit patterns stored in s) / 448.
+hipError_t launch_amax_finish(float *s, int64_t n_part, hipStream_t stream);
 // part: fp32 partials of gemm_partial_bytes(M, N, K, device_cu_count()) bytes
 // (may be NULL when that is 0).
 hipError_t launch_dense_gemm(const uint8_t *xq, const float *xs, const uint8_t *wq, const float *ws, int64_t M,

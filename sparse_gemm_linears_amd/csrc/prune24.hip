@@ -65,11 +65,16 @@ __device__ __forceinline__ Kept2 select_two(float v0, float v1, float v2, float 
   return r;
 }
 
-template <bool AWARE>
+// MODE 0: block scales (the kernel above).  The per-tensor form runs in three
+// launches on the stream: MODE 1 writes each block's largest kept magnitude
+// (bf16 bits) into its entry of s; amax_finish_kernel folds them into
+// s[0] = amax / 448; MODE 2 quantizes the kept values with s[0] and writes it
+// to every other entry.
+template <bool AWARE, int MODE = 0>
 __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict__ w,
                                                       const float* __restrict__ col_norm, int64_t K,
                                                       uint8_t* __restrict__ vals, uint8_t* __restrict__ meta,
-                                                      float* __restrict__ s) {
+                                                      float* s) {
   __shared__ uint32_t wave_max[4];
   const int t = threadIdx.x;
   // Block b runs on XCD b % 8.  Each XCD takes a contiguous range of blocks
@@ -125,14 +130,36 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
   if ((t & 63) == 0) wave_max[t >> 6] = amax_bits;
   __syncthreads();
   amax_bits = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
-  const GroupScale g = group_scale(amax_bits);
-  if (t == 0) s[(int64_t)nb * KB + kb] = g.s;
+  if constexpr (MODE == 1) {
+    if (t == 0) reinterpret_cast<uint32_t*>(s)[(int64_t)nb * KB + kb] = amax_bits >> 16;  // bf16 magnitude bits
+    return;
+  }
+  GroupScale g;
+  if constexpr (MODE == 2) {
+    // the tensor scale (amax / 448 of every kept value): codes by the
+    // reciprocal with a check near e4m3 rounding midpoints, else the IEEE
+    // division (the static-scale quantizer's arithmetic)
+    g.s = s[0];
+    g.rs = __builtin_amdgcn_rcpf(g.s);
+    g.fast = scale_fast_ok(g.s);
+    if (t == 0 && (nb != 0 || kb != 0)) s[(int64_t)nb * KB + kb] = g.s;
+  } else {
+    g = group_scale(amax_bits);
+    if (t == 0) s[(int64_t)nb * KB + kb] = g.s;
+  }
 
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const int64_t n = row0 + 16 * i;
     const float kv[4] = {kept[i][0].first, kept[i][0].second, kept[i][1].first, kept[i][1].second};
-    const uint32_t word = quantize4_group(kv, g);
+    uint32_t word;
+    if constexpr (MODE == 2) {
+      uint32_t need = g.fast ? 0u : 1u;
+      word = quantize4_fast(kv, g.rs, need);
+      if (__builtin_expect(need != 0u, 0)) word = quantize4_exact(kv, g.s);
+    } else {
+      word = quantize4_group(kv, g);
+    }
     *reinterpret_cast<uint32_t*>(vals + n * (K / 2) + kcol / 2) = word;
     // the 16 lanes of a row segment hold its 16 consecutive meta bytes: the
     // first lane of each quad gathers the bytes of lanes 1, 2, 3 of its quad
@@ -143,6 +170,24 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
                         ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xFF, 0xF, 0xF, false) << 24);
     if ((t & 3) == 0) *reinterpret_cast<uint32_t*>(meta + n * (K / 8) + kcol / 8) = m4;
   }
+}
+
+hipError_t launch_prune24_tensor(const uint16_t* w, const float* col_norm, int64_t N, int64_t K, uint8_t* vals,
+                                 uint8_t* meta, float* s, hipStream_t stream) {
+  const int64_t blocks = (N / kGroup) * (K / kGroup);
+  const dim3 grid((unsigned)blocks);
+  if (col_norm)
+    hipLaunchKernelGGL((prune24_kernel<true, 1>), grid, dim3(256), 0, stream, w, col_norm, K, vals, meta, s);
+  else
+    hipLaunchKernelGGL((prune24_kernel<false, 1>), grid, dim3(256), 0, stream, w, col_norm, K, vals, meta, s);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = launch_amax_finish(s, blocks, stream);
+  if (e != hipSuccess) return e;
+  if (col_norm)
+    hipLaunchKernelGGL((prune24_kernel<true, 2>), grid, dim3(256), 0, stream, w, col_norm, K, vals, meta, s);
+  else
+    hipLaunchKernelGGL((prune24_kernel<false, 2>), grid, dim3(256), 0, stream, w, col_norm, K, vals, meta, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_prune24(const uint16_t* w, const float* col_norm, int64_t N, int64_t K, uint8_t* vals,

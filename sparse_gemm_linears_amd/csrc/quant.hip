@@ -212,6 +212,11 @@ __global__ __launch_bounds__(256) void quant_scaled_kernel(const uint16_t* __res
   if (i >= s_from && i < n_s) s[i] = sc;
 }
 
+hipError_t launch_amax_finish(float* s, int64_t n_part, hipStream_t stream) {
+  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(256), 0, stream, s, (int)n_part);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s, int64_t n_s,
                                hipStream_t stream) {
   const int64_t n_chunks = n / 8;

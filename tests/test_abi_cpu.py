@@ -114,6 +114,15 @@ def test_prune_validation(lib):
     assert f(P(A), None, 128, 128, P(B), P(B + 4096), P(D), None) == sgl.FP8L_ERR_ALIAS  # vals/meta overlap
 
 
+def test_prune_tensor_validation(lib):
+    f = lib.prune24_compress_tensor
+    assert f(P(A), None, 128, 130, P(B), P(C), P(D), None) == sgl.FP8L_ERR_SHAPE
+    assert f(P(A), None, 100, 128, P(B), P(C), P(D), None) == sgl.FP8L_ERR_SHAPE
+    assert f(P(A), None, 128, 128, P(B), P(C), None, None) == sgl.FP8L_ERR_NULL
+    assert f(P(A), P(E + 4), 128, 128, P(B), P(C), P(D), None) == sgl.FP8L_ERR_ALIGN
+    assert f(P(A), None, 128, 128, P(B), P(C), P(B + 64), None) == sgl.FP8L_ERR_ALIAS     # s inside vals
+
+
 def test_gemm_validation(lib):
     g = lib.fp8_block_gemm
     assert g(P(A), P(B), P(C), P(D), 16, 100, 128, P(E), None) == sgl.FP8L_ERR_SHAPE
