@@ -16,6 +16,7 @@ the weights rotated through enough copies to defeat the caches) and the CPU
 oracle timed on a bounded sample of the same step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+       python bench.py --profile-case NAME   (one kernel workload, for rocprofv3 counter runs)
 """
 from __future__ import annotations
 
@@ -40,8 +41,8 @@ CALIB_BYTES = 256 << 20    # size of the traffic-calibration copy
 # fp8_block_gemm_gate_up_m4096_traffic.md has the commands and the readings),
 # each scaled by the same counter's reading for the calibration copy.  It is
 # reported only while the kernel's sources hash to the value it was taken on.
-TRAFFIC = {"bytes_per_launch": 941729046,
-           "sources_sha256": "c79e894c953937ae55f510cad80290c22adb419eb982125527e68578e6df01e2"}
+TRAFFIC = {"bytes_per_launch": 941583763,
+           "sources_sha256": "d76dc72556248f98e2e28de6918babec641d9edf5ec2f916e1e1edf94c50d1c5"}
 TRAFFIC_SOURCES = ("sparse_gemm_linears_amd/csrc/gemm_dense.hip", "sparse_gemm_linears_amd/csrc/gemm_common.hpp",
                    "sparse_gemm_linears_amd/csrc/device_common.hpp")
 
@@ -69,7 +70,69 @@ def parse_args():
     p.add_argument("--no-decode", action="store_true", help="skip the decode-M and mid-M GEMM measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=1024, help="token rows in the CPU oracle sample")
+    p.add_argument("--profile-case", choices=sorted(PROFILE_CASES), default=None,
+                   help="run only one kernel workload (for rocprofv3 counter runs) and exit")
     return p.parse_args()
+
+
+# Single-kernel workloads for counter collection under rocprofv3 --pmc: each runs
+# the named call `reps` times (after one warm-up call) on the inputs of the
+# benchmark, plus the 256 MiB calibration copy, and prints one JSON line.
+#   (kind, shape name, tokens, reps); decode kinds rotate the weight through
+#   >= 1 GiB of copies so that every call reads it from HBM.
+PROFILE_CASES = {
+    "dense_gate_up_m4096": ("dense", "gate_up", 4096, 5),
+    "sparse_gate_up_m4096": ("sparse", "gate_up", 4096, 5),
+    "dense_down_m4096": ("dense", "down", 4096, 5),
+    "sparse_down_m4096": ("sparse", "down", 4096, 5),
+    "decode_dense_gate_up_m1": ("dense", "gate_up", 1, 20),
+    "decode_dense_down_m1": ("dense", "down", 1, 20),
+    "decode_dense_gate_up_m16": ("dense", "gate_up", 16, 20),
+    "decode_dense_down_m16": ("dense", "down", 16, 20),
+    "decode_sparse_gate_up_m16": ("sparse", "gate_up", 16, 20),
+    "decode_sparse_down_m16": ("sparse", "down", 16, 20),
+}
+
+
+def profile_case(name):
+    import numpy as np
+    import torch
+
+    import sparse_gemm_linears_amd as sgl
+    import synth_inputs as si
+
+    kind, shape, M, reps = PROFILE_CASES[name]
+    sgl.load_library()
+    dev = torch.device("cuda:0")
+    _, K, N = next(s for s in si.LLAMA3_8B if s[0] == shape)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    torch.empty_like(calib_src).copy_(calib_src)
+    x = bf16(si.activations(M, K))
+    w = bf16(si.weights(N, K))
+    xq, xs = sgl.fp8_quant_act(x)
+    copies = 1 if M > 64 else max(2, math.ceil((1 << 30) / (N * K)))
+    if kind == "dense":
+        wq, ws = sgl.fp8_quant_weight_block(w)
+        ops = [(wq.clone(), ws.clone()) for _ in range(copies)] if copies > 1 else [(wq, ws)]
+        f = lambda i: sgl.fp8_block_gemm(xq, xs, *ops[i % len(ops)], y)
+    else:
+        c = torch.from_numpy(si.column_norms(si.calibration_batch(K))).to(dev)
+        v, m, s2 = sgl.prune24_compress(w, c)
+        ops = [(v.clone(), m.clone(), s2.clone()) for _ in range(copies)] if copies > 1 else [(v, m, s2)]
+        f = lambda i: sgl.fp8_sparse24_gemm(xq, xs, *ops[i % len(ops)], y)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    f(len(ops) - 1)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        f(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_case": name, "kind": kind, "shape": shape, "M": M, "N": N, "K": K, "reps": reps,
+                      "weight_copies": len(ops)}))
 
 
 def main():
@@ -78,6 +141,9 @@ def main():
         print("bench.py measures one GPU: the FP8 linear layer is built and timed on a single MI355X; "
               "multi-GPU runs are not part of this library.", file=sys.stderr)
         sys.exit(2)
+    if args.profile_case:
+        profile_case(args.profile_case)
+        return
 
     import numpy as np
     import torch
@@ -231,6 +297,7 @@ def main():
     torch.cuda.empty_cache()
 
     dsv3, dsv3_rows = bench_dsv3(sgl, si, torch, np, dev, bf16, args.steps)
+    per_tensor = bench_per_tensor(sgl, si, torch, np, dev, bf16, args.steps)
     swiglu = bench_swiglu(sgl, si, torch, np, dev, bf16, args.steps)
     ue8m0 = bench_ue8m0(sgl, si, torch, np, dev, bf16, args.steps)
     decode = None if args.no_decode else bench_decode(sgl, si, torch, np, dev, bf16)
@@ -249,6 +316,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": per_kernel,
         "dsv3": dsv3,
+        "per_tensor": per_tensor,
         "swiglu": swiglu,
         "ue8m0": ue8m0,
         "decode": decode,
@@ -297,6 +365,35 @@ def bench_dsv3(sgl, si, torch, np, dev, bf16, steps):
         del x, xq, xs, wq, ws, y
     torch.cuda.empty_cache()
     return res, sampled
+
+
+def bench_per_tensor(sgl, si, torch, np, dev, bf16, steps):
+    """The dense and 2:4 GEMMs on per-tensor-scaled operands (fp8_quant_act_tensor
+    activations; fp8_quant_weight_tensor or prune24_compress_tensor weights) on the
+    four Llama-3-8B shapes at M = 4096, timed in alternating batches (medians of
+    three).  Every scale product is then the same in every K block, so the 2:4 tile
+    kernel sums unscaled block products and scales once (no VALU work per sparse
+    MFMA); the dense kernel keeps its per-block scale FMAs."""
+    M = si.PREFILL_M
+    res = {}
+    for name, K, N in si.LLAMA3_8B:
+        x, w = bf16(si.activations(M, K)), bf16(si.weights(N, K))
+        c = torch.from_numpy(si.column_norms(si.calibration_batch(K))).to(dev)
+        xq, xs = sgl.fp8_quant_act_tensor(x)
+        wq, ws = sgl.fp8_quant_weight_tensor(w)
+        v, m, s2 = sgl.prune24_compress_tensor(w, c)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t_d, t_s = [], []
+        for _ in range(3):
+            t_d.append(time_calls(torch, lambda: sgl.fp8_block_gemm(xq, xs, wq, ws, y), steps))
+            t_s.append(time_calls(torch, lambda: sgl.fp8_sparse24_gemm(xq, xs, v, m, s2, y), steps))
+        td, ts = sorted(t_d)[1], sorted(t_s)[1]
+        res[name] = {"dense_us": round(td, 2), "dense_tflops": round(2 * M * N * K / td / 1e6, 1),
+                     "sparse_us": round(ts, 2), "sparse_tflops_algorithmic": round(M * N * K / ts / 1e6, 1),
+                     "speedup_vs_dense": round(td / ts, 3)}
+        del x, w, c, xq, xs, wq, ws, v, m, s2, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_ue8m0(sgl, si, torch, np, dev, bf16, steps):

@@ -38,13 +38,20 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t *row, int g) {
 }
 
 // LDS tiles hold rows of 128 bytes as eight 16-byte chunks; chunk c of row r
-// sits at chunk position c ^ swz(r).  swz depends on r % 16 only and permutes
-// the chunks of any 8 aligned consecutive rows, and across 16 aligned rows
-// those of the even and of the odd rows, so 16-lane fragment reads of one
-// chunk column hit distinct banks whether the LDS serves 128 or 256 bytes per
-// cycle.  Depending on r % 16 only lets a fragment row r = 16*t + l%16 use one
-// per-lane address plus a compile-time offset 2048*t.
-__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+// sits at chunk position c ^ swz(r).  A 16x16 fragment read (ds_read_b128)
+// takes one chunk column g of 16 consecutive rows in lanes l % 16, with
+// g = l / 16.  The LDS serves such a read in four passes, each pass lanes
+// 8i..8i+7 together with lanes 32+8i..32+8i+7: eight consecutive rows at
+// chunk columns g and g+2.  Over 64 banks of 4 bytes, row parity picks the
+// bank half, and swz sends the four rows of each parity (bits 1, 2 of r, with
+// bit 3 for the other 8-row half) to four distinct chunk positions, so the
+// 16 lanes of a pass touch 16 distinct 16-byte bank groups.  The same holds
+// if a pass is 16 consecutive lanes.  (A plain r ^ (r >> 3) spread of the
+// low three bits costs a second cycle per pass: rows 2j and 2j+1 then share a
+// position for every chunk column g and g+2.)  swz depends on r % 16 only, so a
+// fragment row r = 16*t + l%16 uses one per-lane address plus a compile-time
+// offset 2048*t.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2); }
 
 // Fragment read at precomputed per-lane byte offsets (lo, hi chunk) plus a
 // compile-time displacement.
