@@ -643,6 +643,20 @@ static hipError_t launch_dense_decode(X xop, const uint8_t *wq, const typename X
   if constexpr (X::kStaged) {
     return launch_decode_for<X, 1>(xop, wq, ws, M, N, K, y, part, stream);  // M <= 8
   } else {
+    // 3 to 16 tokens on weights of at least 16384 rows and K < 8192: the
+    // shared-token form (tokens staged in LDS once per workgroup, several row
+    // bands per workgroup).  Measured on MI355X (gate/up 28672 x 4096, weight
+    // from HBM): 22.0 / 22.5 / 25.3 us at 3 / 8 / 16 tokens against 25.5 /
+    // 26.2 / 27.4 us.  Level or up to 5 % slower on the 4096- and 6144-row
+    // weights, and not used on long K, which splits K instead.
+    if constexpr (std::is_same<X, QuantTokens>::value) {
+      if (M >= 3 && M <= 16 && K < 8192 && N >= 16384) {
+        const int grid = shared_decode_grid(M, N, K, 1, 1, 16, 1, device_cu_count());
+        if (grid > 0)
+          return launch_decode_shared<DenseWeight, 1, 16, 2, 1>(DenseWeight{wq, K}, xop.xq, xop.xs, ws, M, N, K, y,
+                                                                nullptr, grid, stream);
+      }
+    }
     if (M <= 16) return launch_decode_for<X, 1>(xop, wq, ws, M, N, K, y, part, stream);
     if (M <= 32) return launch_decode_for<X, 2>(xop, wq, ws, M, N, K, y, part, stream);
     return launch_decode_for<X, 4>(xop, wq, ws, M, N, K, y, part, stream);

@@ -603,6 +603,18 @@ static hipError_t launch_sparse_decode(X xop, const uint8_t *wv, const uint8_t *
   if constexpr (X::kStaged) {
     return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, part, stream);  // M <= 8
   } else {
+    // 3 to 8 tokens on weights of at least 16384 rows and K < 8192: the
+    // shared-token form (measured on MI355X, gate/up 28672 x 4096, weight from
+    // HBM: 16.6 / 18.4 us at 3 / 8 tokens against 23.3 / 20.2 us; at 16 tokens,
+    // and on the smaller weights, the weight-streaming kernel is as fast)
+    if constexpr (std::is_same<X, QuantTokens>::value) {
+      if (M >= 3 && M <= 8 && K < 8192 && N >= 16384) {
+        const int grid = shared_decode_grid(M, N, K, 1, SparseWeight4::kUnit, 8, 1, device_cu_count());
+        if (grid > 0)
+          return launch_decode_shared<SparseWeight4, 1, 8, 1, 1>(SparseWeight4{wv, wm, K}, xop.xq, xop.xs, ws, M, N,
+                                                                 K, y, nullptr, grid, stream);
+      }
+    }
     if (M <= 16) return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, part, stream);
     if (M <= 32) return launch_decode_for<X, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);
     return launch_decode_for<X, 4>(xop, wv, wm, ws, M, N, K, y, part, stream);

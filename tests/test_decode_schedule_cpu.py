@@ -109,3 +109,80 @@ def test_idle_waves_with_units():
     assert loads == [] and consumed == [] and mine == []
     loads, _, _, (lo, hi) = schedule(100, 8, 1, 4, split=3, wave=3, U=4)
     assert loads == list(range(96, 100)) and (lo, hi) == (84, 100)
+
+
+# ------------------------------------------------------- shared-token form --
+#
+# decode_shared_kernel (gemm_decode.hpp): workgroup b0 of a grid of G (G a
+# multiple of the K split count S) takes split b0 % S and row bands
+# b0 / S + j * (G / S); its waves split each band's US units round-robin (a
+# wave with n_w units per band), run their items t = j * n_w + i through the
+# D-slot schedule of decode_kernel, and after the last unit of a band meet at
+# a barrier, so every wave must close the same bands in the same order.
+
+def shared_schedule(bands: int, S: int, G: int, b0: int, US: int, NW: int, D: int, wave: int):
+    first, stride = b0 // S, G // S
+    nbj = (bands - first + stride - 1) // stride if first < bands else 0
+    n_w = (US - wave + NW - 1) // NW
+    T = nbj * n_w
+    item = lambda t: (first + (t // n_w) * stride, b0 % S, wave + (t % n_w) * NW)
+    slot = [None] * D
+    loads, consumed, closed = [], [], []
+
+    def load(d, t):
+        loads.append(item(t))
+        slot[d] = item(t)
+
+    def consume(d, t):
+        assert slot[d] == item(t)
+        consumed.append(slot[d])
+        if t % n_w == n_w - 1:
+            closed.append(item(t)[0])
+
+    if T > 0:
+        for d in range(D):
+            load(d, min(d, T - 1))
+    t0 = 0
+    while t0 + 2 * D <= T:
+        for d in range(D):
+            consume(d, t0 + d)
+            load(d, t0 + d + D)
+        t0 += D
+    if t0 + D <= T:
+        for d in range(D):
+            consume(d, t0 + d)
+            if t0 + d + D < T:
+                load(d, t0 + d + D)
+        t0 += D
+    for d in range(D - 1):
+        if t0 + d < T:
+            consume(d, t0 + d)
+    return loads, consumed, closed, [item(t) for t in range(T)], nbj
+
+
+@pytest.mark.parametrize("bands,S,G,US,NW", [
+    (1792, 1, 256, 32, 16), (1792, 1, 512, 32, 16), (256, 1, 256, 32, 16), (8, 1, 8, 8, 8),
+    (1792, 1, 512, 8, 8), (1024, 1, 256, 2, 2), (100, 1, 64, 5, 4), (256, 4, 256, 28, 16),
+    (256, 4, 512, 7, 4), (256, 2, 256, 56, 16), (37, 1, 16, 3, 3), (5, 1, 8, 4, 4)])
+@pytest.mark.parametrize("D", [1, 2, 3])
+def test_shared_schedule_covers_every_unit_once(bands, S, G, US, NW, D):
+    every = []
+    for b0 in range(G):
+        per_wave_closed = []
+        for wave in range(NW):
+            loads, consumed, closed, items, nbj = shared_schedule(bands, S, G, b0, US, NW, D, wave)
+            assert all(b < bands and u < US for b, _, u in loads), (b0, wave)
+            assert consumed == items
+            per_wave_closed.append(closed)
+            every.extend(consumed)
+        # every wave meets the others at the same band barriers, in order
+        assert all(c == per_wave_closed[0] for c in per_wave_closed), b0
+        assert per_wave_closed[0] == [b0 // S + j * (G // S) for j in range(len(per_wave_closed[0]))]
+    assert sorted(every) == sorted((b, s, u) for b in range(bands) for s in range(S) for u in range(US))
+
+
+def test_shared_schedule_needs_a_unit_per_wave():
+    """With fewer units than waves a wave would close no band and miss the
+    barriers, which is why the host requires at least NW units per split."""
+    _, _, closed, _, nbj = shared_schedule(64, 1, 16, 0, 3, 4, 2, 3)
+    assert nbj > 0 and closed == []
