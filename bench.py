@@ -87,8 +87,10 @@ PROFILE_CASES = {
     "sparse_down_m4096": ("sparse", "down", 4096, 5),
     "decode_dense_gate_up_m1": ("dense", "gate_up", 1, 20),
     "decode_dense_down_m1": ("dense", "down", 1, 20),
+    "decode_dense_gate_up_m8": ("dense", "gate_up", 8, 20),
     "decode_dense_gate_up_m16": ("dense", "gate_up", 16, 20),
     "decode_dense_down_m16": ("dense", "down", 16, 20),
+    "decode_sparse_gate_up_m8": ("sparse", "gate_up", 8, 20),
     "decode_sparse_gate_up_m16": ("sparse", "gate_up", 16, 20),
     "decode_sparse_down_m16": ("sparse", "down", 16, 20),
 }

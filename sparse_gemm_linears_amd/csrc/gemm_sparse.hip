@@ -26,12 +26,12 @@ __device__ __forceinline__ v4f smfmac_16x16x128_fp8(const v4i &a, const v8i &b, 
 
 // LDS row of 64 value bytes = four 16-byte chunks; chunk c of row r sits at
 // position c ^ vswz(r).  A fragment read takes chunk column g = l / 16 of 16
-// consecutive rows; one LDS pass serves lanes 8i..8i+7 with 32+8i..32+8i+7,
-// eight consecutive rows at columns g and g+2.  Rows r, r+1, r+2, r+3 share a
-// 256-byte bank line at distinct 64-byte offsets, and vswz (bits 2, 3 of r)
-// gives each such group of four its own chunk position, so the 16 lanes of a
-// pass hit distinct banks; vswz depends on r % 16 only.
-__device__ __forceinline__ int vswz(int r) { return (r >> 2) & 3; }
+// consecutive rows r = l % 16, served in the four 16-lane passes described at
+// swz (gemm_common.hpp); four rows share a 256-byte bank line.  vswz (3 for
+// bit 2 of r, xor 2 for bit 3) gives the 16 lanes of every pass distinct bank
+// groups, also under the other two pass shapes named there; it depends on
+// r % 16 only.  (Without it, or with (r >> 2) & 3, the reads conflict.)
+__device__ __forceinline__ int vswz(int r) { return (((r >> 2) & 1) * 3) ^ (((r >> 3) & 1) << 1); }
 
 // ============================================================== tile kernel ==
 
