@@ -41,8 +41,8 @@ CALIB_BYTES = 256 << 20    # size of the traffic-calibration copy
 # fp8_block_gemm_gate_up_m4096_traffic.md has the commands and the readings),
 # each scaled by the same counter's reading for the calibration copy.  It is
 # reported only while the kernel's sources hash to the value it was taken on.
-TRAFFIC = {"bytes_per_launch": 941583763,
-           "sources_sha256": "d76dc72556248f98e2e28de6918babec641d9edf5ec2f916e1e1edf94c50d1c5"}
+TRAFFIC = {"bytes_per_launch": 941671270,
+           "sources_sha256": "d5116bc57050423a054989efb5bc9db891884a8902c2193eaef029a4941286e1"}
 TRAFFIC_SOURCES = ("sparse_gemm_linears_amd/csrc/gemm_dense.hip", "sparse_gemm_linears_amd/csrc/gemm_common.hpp",
                    "sparse_gemm_linears_amd/csrc/device_common.hpp")
 
@@ -85,6 +85,7 @@ PROFILE_CASES = {
     "sparse_gate_up_m4096": ("sparse", "gate_up", 4096, 5),
     "dense_down_m4096": ("dense", "down", 4096, 5),
     "sparse_down_m4096": ("sparse", "down", 4096, 5),
+    "ue8m0_gate_up_m4096": ("ue8m0", "gate_up", 4096, 5),
     "decode_dense_gate_up_m1": ("dense", "gate_up", 1, 20),
     "decode_dense_down_m1": ("dense", "down", 1, 20),
     "decode_dense_gate_up_m8": ("dense", "gate_up", 8, 20),
@@ -117,7 +118,12 @@ def profile_case(name):
     w = bf16(si.weights(N, K))
     xq, xs = sgl.fp8_quant_act(x)
     copies = 1 if M > 64 else max(2, math.ceil((1 << 30) / (N * K)))
-    if kind == "dense":
+    if kind == "ue8m0":
+        xq, xs = sgl.fp8_quant_act_ue8m0(x)
+        wq, ws = sgl.fp8_quant_weight_block_ue8m0(w)
+        ops = [(wq, ws)]
+        f = lambda i: sgl.fp8_block_gemm_ue8m0(xq, xs, wq, ws, y)
+    elif kind == "dense":
         wq, ws = sgl.fp8_quant_weight_block(w)
         ops = [(wq.clone(), ws.clone()) for _ in range(copies)] if copies > 1 else [(wq, ws)]
         f = lambda i: sgl.fp8_block_gemm(xq, xs, *ops[i % len(ops)], y)
