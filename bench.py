@@ -436,8 +436,9 @@ def bench_ue8m0(sgl, si, torch, np, dev, bf16, steps):
 
 def bench_swiglu(sgl, si, torch, np, dev, bf16, steps):
     """The gated-MLP up projection at M=4096 (gate/up 4096 -> 2 x 14336): the fused
-    GEMM + SwiGLU call, with and without the e4m3 output for the down projection,
-    beside the plain GEMM of the same weight and fp8_quant_act of h."""
+    GEMM + SwiGLU call with h and its e4m3 codes for the down projection, with the
+    codes only (h not stored), and with h only, beside the plain GEMM of the same
+    weight and fp8_quant_act of h."""
     M, K, I = si.PREFILL_M, 4096, 14336
     xq, xs = sgl.fp8_quant_act(bf16(si.activations(M, K)))
     wq, ws = sgl.fp8_quant_weight_block(bf16(si.weights(2 * I, K)))
@@ -447,6 +448,7 @@ def bench_swiglu(sgl, si, torch, np, dev, bf16, steps):
     hs = torch.empty((M, I // 128), dtype=torch.float32, device=dev)
     runs = {
         "gemm_swiglu_quant": lambda: sgl.fp8_block_gemm_swiglu(xq, xs, wq, ws, h, True, hq, hs),
+        "gemm_swiglu_quant_only": lambda: sgl.fp8_block_gemm_swiglu(xq, xs, wq, ws, None, True, hq, hs, keep_h=False),
         "gemm_swiglu": lambda: sgl.fp8_block_gemm_swiglu(xq, xs, wq, ws, h, False),
         "gemm_only": lambda: sgl.fp8_block_gemm(xq, xs, wq, ws, y),
         "quant_act_of_h": lambda: sgl.fp8_quant_act(h, hq, hs),

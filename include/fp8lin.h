@@ -315,8 +315,13 @@ fp8l_status fp8_block_gemm_ue8m0(const uint8_t *xq, const uint8_t *xe, const uin
  *                                   up projection (nn.Linear weights stacked)
  *   h  [M,I] bf16                   h = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)),
  *                                   g, u the fp32 block-scaled sums of fp8_block_gemm
+ *                                   (NULL: not stored; then hq and hs are required)
  *   hq [M,I] e4m3, hs [M,I/128]     fp8_quant_act(h), the next layer's input
  *                                   (both NULL: not produced)
+ * A caller that feeds only the next FP8 layer passes h = NULL and saves the
+ * M * I * 2 bytes of bf16 output; hq and hs are the same as with h stored
+ * (made from the same bf16-rounded values).  FP8L_ERR_NULL when h and hq are
+ * both NULL, or exactly one of hq, hs is.
  * I must be a positive multiple of 128.  Prefill-sized M runs the fused
  * kernel (256-token tiles, SwiGLU and the quantization in the epilogue).
  * Where that grid would leave compute units idle (few tokens), the stacked

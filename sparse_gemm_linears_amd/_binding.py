@@ -305,9 +305,12 @@ def fp8_sparse24_linear(x, wvals, wmeta, ws, y: torch.Tensor | None = None):
 
 
 def fp8_block_gemm_swiglu(xq, xs, wq, ws, h: torch.Tensor | None = None, quantize: bool = True,
-                          hq: torch.Tensor | None = None, hs: torch.Tensor | None = None):
+                          hq: torch.Tensor | None = None, hs: torch.Tensor | None = None, keep_h: bool = True):
     """(xq [M,K], xs, wq [2I,K] = [gate; up], ws [2I/128,K/128]) -> h [M,I] bf16 = silu(gate) * up, and, when
-    ``quantize``, (hq [M,I] e4m3 codes, hs [M,I/128]) = fp8_quant_act(h).  Returns (h, hq, hs)."""
+    ``quantize``, (hq [M,I] e4m3 codes, hs [M,I/128]) = fp8_quant_act(h).  Returns (h, hq, hs); with
+    ``keep_h=False`` (only with ``quantize``) h is not stored and None is returned in its place."""
+    if not keep_h and not quantize:
+        raise ValueError("fp8_block_gemm_swiglu: keep_h=False needs quantize=True")
     xq, wq = _codes(xq), _codes(wq)
     _want(xq, "xq", torch.uint8)
     _want(wq, "wq", torch.uint8)
@@ -316,7 +319,7 @@ def fp8_block_gemm_swiglu(xq, xs, wq, ws, h: torch.Tensor | None = None, quantiz
     _want(wq, "wq", torch.uint8, (2 * I, K))
     _want(xs, "xs", torch.float32, (M, K // GROUP))
     _want(ws, "ws", torch.float32, (2 * I // GROUP, K // GROUP))
-    h = _out(h, "h", (M, I), torch.bfloat16, xq)
+    h = _out(h, "h", (M, I), torch.bfloat16, xq) if keep_h else None
     if quantize:
         hq = _out(hq, "hq", (M, I), torch.uint8, xq)
         hs = _out(hs, "hs", (M, I // GROUP), torch.float32, xq)

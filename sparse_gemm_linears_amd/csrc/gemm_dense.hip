@@ -84,7 +84,7 @@ __device__ __forceinline__ void swiglu_finish(const v4f (&gv)[C::RT], const v4f 
       hv[r][e] = bf16_to_f32(f32_to_bf16_rne(gg * uv[r][e] * __builtin_amdgcn_rcpf(1.0f + __expf(-gg))));
     }
   }
-  store_token_tile<C::RT>(scratch, hv, h, M, so.I, m0, 128 * tn, lane);
+  if (h) store_token_tile<C::RT>(scratch, hv, h, M, so.I, m0, 128 * tn, lane);
   if (!so.hq) return;
   uint32_t amax_bits = 0;
 #pragma unroll
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float *__restr
     w[i] = b2[0] | (b2[1] << 16);
   }
   const uint4 raw = make_uint4(w[0], w[1], w[2], w[3]);
-  if (live) *reinterpret_cast<uint4 *>(h + m * I + col) = raw;
+  if (live && h) *reinterpret_cast<uint4 *>(h + m * I + col) = raw;
   if (hq) {
     float sc;
     const uint2 codes = quantize_group16(raw, sc);

@@ -150,6 +150,10 @@ def test_swiglu_validation(lib):
     assert f(P(A), P(B), P(C), P(D), 16, 64, 128, P(E), None, None, None) == sgl.FP8L_ERR_SHAPE
     assert f(P(A), P(B), P(C), P(D), 16, 0, 128, P(E), None, None, None) == sgl.FP8L_ERR_SHAPE
     assert f(P(A), P(B), P(C), P(D), 16, 128, 128, P(E), P(F), None, None) == sgl.FP8L_ERR_NULL  # hq without hs
+    assert f(P(A), P(B), P(C), P(D), 16, 128, 128, None, None, None, None) == sgl.FP8L_ERR_NULL  # nothing to produce
+    assert f(P(A), P(B), P(C), P(D), 16, 128, 128, None, P(F), None, None) == sgl.FP8L_ERR_NULL  # h omitted, hs missing
+    assert f(P(A), P(B), P(C), P(D), 16, 128, 128, None, P(F + 4), P(E), None) == sgl.FP8L_ERR_ALIGN
+    assert f(P(A), P(B), P(C), P(D), 16, 128, 128, None, P(F), P(D), None) == sgl.FP8L_ERR_ALIAS  # hs over ws
     assert f(P(A), P(B), P(C), P(D), 16, 128, 128, P(E + 2), None, None, None) == sgl.FP8L_ERR_ALIGN
     assert f(P(A), P(B), P(C), P(D), 16, 128, 128, P(D), None, None, None) == sgl.FP8L_ERR_ALIAS
 

@@ -151,6 +151,18 @@ def test_gemm_swiglu(gpu_lib, M, I, K):
     assert torch.equal(lq, hq) and torch.equal(ls.view(torch.int32), hs.view(torch.int32))
 
 
+@pytest.mark.parametrize("M,I,K", [(4096, 14336, 4096), (300, 256, 640), (16, 128, 128), (64, 14336, 4096)])
+def test_gemm_swiglu_quantized_only(gpu_lib, M, I, K):
+    """h not stored (NULL): the codes and scales equal, bit for bit, those of the call that stores h, on the
+    fused kernel (prefill M) and on the partials path (few tokens)."""
+    xq, xs = oracle.quant_act(si.activations(M, K, outliers=(K == 4096)))
+    wq, ws = gate_up_weight(K, I)
+    h, hq, hs = gpu_lib.fp8_block_gemm_swiglu(dev(xq), dev(xs), dev(wq), dev(ws))
+    h2, hq2, hs2 = gpu_lib.fp8_block_gemm_swiglu(dev(xq), dev(xs), dev(wq), dev(ws), keep_h=False)
+    assert h2 is None
+    assert torch.equal(hq, hq2) and torch.equal(hs.view(torch.int32), hs2.view(torch.int32))
+
+
 def test_gemm_swiglu_without_quantization(gpu_lib):
     M, I, K = 256, 256, 512
     xq, xs = oracle.quant_act(si.activations(M, K, outliers=False))
