@@ -474,7 +474,7 @@ struct SparseWeight {
 // with no index loads at all).  Here one 16-byte load per lane brings the
 // words of four consecutive blocks: lane group g receives block kb + g's four
 // words and needs word g of each block, so the four lane groups of a row
-// exchange them (a 4x4 transpose in four cross-lane steps).
+// exchange them (a 4x4 transpose by lane-permute swaps).
 struct SparseFrag4 {
   v4i v[4];
   int idx[4];
@@ -490,18 +490,21 @@ struct SparseWeight4 {
 #pragma unroll
     for (int j = 0; j < 4; j++) f.v[j] = make_v4i(ldg16(wv + row * (K / 2) + (int64_t)(kb + j) * 64 + 16 * g));
     const uint4 m = ldg16(wm + row * (K / 8) + (int64_t)kb * 16 + 16 * g);
-    const int lr = (int)(threadIdx.x & 15);
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-      // lane group j sends its word (j + t) % 4; this lane (group g) takes it
-      // from group (g - t) % 4, whose word g is block ((g - t) % 4)'s
-      const int s = (g + t) & 3, j = (g - t) & 3;
-      const int send = (int)(s == 0 ? m.x : s == 1 ? m.y : s == 2 ? m.z : m.w);
-      const int got = __shfl(send, lr + 16 * j, 64);
-#pragma unroll
-      for (int q = 0; q < 4; q++)
-        if (q == j) f.idx[q] = got;
-    }
+    // Lane group g (the 16-lane row g of the wave) holds the four words of
+    // block kb + g and needs word g of every block: a 4x4 transpose across the
+    // rows.  Two 32-lane swaps (rows 2, 3 of one register with rows 0, 1 of
+    // another), then two 16-lane swaps (odd rows with even rows), leave word g
+    // of block kb + j in register j.  The swaps are VALU lane permutes: no LDS
+    // round trip as with cross-lane shuffles (measured on MI355X: 4-10 % faster
+    // 2:4 decode at 4-32 tokens, bit-identical results).
+    const auto a = __builtin_amdgcn_permlane32_swap(m.x, m.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(m.y, m.w, false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    f.idx[0] = (int)c[0];
+    f.idx[1] = (int)c[1];
+    f.idx[2] = (int)d[0];
+    f.idx[3] = (int)d[1];
     return f;
   }
   __device__ __forceinline__ v4f mma(const Frag &a, const v8i &b, int u) const {
