@@ -307,6 +307,7 @@ def main():
     dsv3, dsv3_rows = bench_dsv3(sgl, si, torch, np, dev, bf16, args.steps)
     per_tensor = bench_per_tensor(sgl, si, torch, np, dev, bf16, args.steps)
     swiglu = bench_swiglu(sgl, si, torch, np, dev, bf16, args.steps)
+    grouped = bench_grouped(sgl, si, torch, np, dev, bf16, args.steps)
     ue8m0 = bench_ue8m0(sgl, si, torch, np, dev, bf16, args.steps)
     decode = None if args.no_decode else bench_decode(sgl, si, torch, np, dev, bf16)
     mid_m = None if args.no_decode else bench_mid_m(sgl, si, torch, np, dev, bf16, args.steps)
@@ -326,6 +327,7 @@ def main():
         "dsv3": dsv3,
         "per_tensor": per_tensor,
         "swiglu": swiglu,
+        "grouped": grouped,
         "ue8m0": ue8m0,
         "decode": decode,
         "mid_m": mid_m,
@@ -430,6 +432,35 @@ def bench_ue8m0(sgl, si, torch, np, dev, bf16, steps):
                      "gemm_tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
                      "fp32_scale_gemm_us": round(t_f, 2)}
         del x, w, xq, xe, wq, we, xq4, xs4, wq4, ws4, y
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_grouped(sgl, si, torch, np, dev, bf16, steps):
+    """The grouped (MoE) GEMM on DeepSeek-V3 routed-expert shapes: 16384 routed token
+    rows over 32 experts with a seeded uneven routing (some experts empty), beside the
+    plain GEMM of the same M x N x K, timed in alternating batches (medians of three).
+    The experts hold copies of one quantized weight at distinct addresses: the same
+    bytes move as with 32 different weights."""
+    M, G = 16384, 32
+    res = {}
+    for name, K, N in si.DSV3_EXPERTS:
+        xq, xs = sgl.fp8_quant_act(bf16(si.activations(M, K, dist="student_t3", outliers=False)))
+        wq1, ws1 = sgl.fp8_quant_weight_block(bf16(si.weights(N, K, std=0.01)))
+        wq = wq1.unsqueeze(0).repeat(G, 1, 1).contiguous()
+        ws = ws1.unsqueeze(0).repeat(G, 1, 1).contiguous()
+        offs = torch.from_numpy(si.routed_offsets(M, G, seed=7)).to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t_g, t_p = [], []
+        for _ in range(3):
+            t_g.append(time_calls(torch, lambda: sgl.fp8_grouped_gemm(xq, xs, wq, ws, offs, y), steps))
+            t_p.append(time_calls(torch, lambda: sgl.fp8_block_gemm(xq, xs, wq1, ws1, y), steps))
+        tg, tp = sorted(t_g)[1], sorted(t_p)[1]
+        tf = 2 * M * N * K / tg / 1e6
+        res[name] = {"M": M, "experts": G, "N": N, "K": K, "grouped_us": round(tg, 2), "grouped_tflops": round(tf, 1),
+                     "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "plain_gemm_us": round(tp, 2),
+                     "expert_weight_mb": round(G * N * K / 1e6, 1)}
+        del xq, xs, wq1, ws1, wq, ws, offs, y
     torch.cuda.empty_cache()
     return res
 

@@ -33,6 +33,10 @@ LLAMA3_8B = [("qkv", 4096, 6144), ("o_proj", 4096, 4096), ("gate_up", 4096, 2867
 # DeepSeek-V3 dense FFN linears, (name, K, N)
 DSV3_FFN = [("ffn_up", 7168, 18432), ("ffn_down", 18432, 7168)]
 
+# DeepSeek-V3 routed-expert linears, (name, K, N): the gate and up projections of
+# an expert stacked (7168 -> 2 x 2048) and its down projection (2048 -> 7168)
+DSV3_EXPERTS = [("expert_gate_up", 7168, 4096), ("expert_down", 2048, 7168)]
+
 DECODE_M = (1, 8, 32, 64)
 PREFILL_M = 4096
 SPARSE_M = (16, 4096)
@@ -118,3 +122,14 @@ def sample_rows(M: int, count: int = 256, seed: int = 5) -> np.ndarray:
         return np.arange(M, dtype=np.int64)
     idx = torch.randperm(M, generator=_gen(seed))[:count].numpy().astype(np.int64)
     return np.sort(idx)
+
+
+def routed_offsets(M: int, G: int, seed: int) -> np.ndarray:
+    """Seeded uneven token counts per expert (gamma-distributed, about one expert in
+    eight empty), as G + 1 int32 row offsets of the contiguous grouped layout summing to M."""
+    rng = np.random.default_rng(seed)
+    w = rng.gamma(0.6, size=G)
+    w[rng.choice(G, max(1, G // 8), replace=False)] = 0.0
+    counts = np.floor(w / w.sum() * M).astype(np.int64)
+    counts[np.argmax(counts)] += M - counts.sum()
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)

@@ -16,14 +16,7 @@ from test_parity_gpu import assert_gemm_close, dev
 pytestmark = pytest.mark.gpu
 
 
-def routed_offsets(M: int, G: int, seed: int) -> np.ndarray:
-    """Seeded uneven token counts per expert (some empty), summing to M."""
-    rng = np.random.default_rng(seed)
-    w = rng.gamma(0.6, size=G)
-    w[rng.choice(G, max(1, G // 8), replace=False)] = 0.0
-    counts = np.floor(w / w.sum() * M).astype(np.int64)
-    counts[np.argmax(counts)] += M - counts.sum()
-    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+routed_offsets = si.routed_offsets  # seeded uneven routing (some experts empty), summing to M
 
 
 def expert_weights(G: int, N: int, K: int, seed: int):
