@@ -410,10 +410,18 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
 
   typename W::Frag a[D][RT];
   float sw[D][U];
-  // item t of this wave: band first + (t / n_w) * stride, unit wave + (t % n_w) * NW
-  auto load = [&](int slot, int t) {
-    const int j = t / n_w, i = t - j * n_w;
-    const int n0 = (first + j * stride) * 16 * RT, kb = kb_lo + (wave + i * NW) * U;
+  // Item (j, i) of this wave: band first + j * stride, unit wave + i * NW of
+  // the split.  Items are walked by cursors, so the loop does no division.
+  struct Item {
+    int j, i;
+  };
+  auto next = [&](const Item &it) { return it.i + 1 == n_w ? Item{it.j + 1, 0} : Item{it.j, it.i + 1}; };
+  auto item_at = [&](int t) {
+    const int j = t / n_w;
+    return Item{j, t - j * n_w};
+  };
+  auto load = [&](int slot, const Item &it) {
+    const int n0 = (first + it.j * stride) * 16 * RT, kb = kb_lo + (wave + it.i * NW) * U;
 #pragma unroll
     for (int r = 0; r < RT; r++) a[slot][r] = wop.load(n0 + 16 * r + lr, kb, g);
 #pragma unroll
@@ -427,31 +435,49 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
   if (T > 0)
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      load(d, min(d, T - 1));
+      load(d, item_at(min(d, T - 1)));
       __builtin_amdgcn_sched_barrier(0);
     }
   {
-    // 16-byte chunks: every load of a pass is issued before its LDS writes
-    const int chunks = M * L.KBs * 8, NT = NW * 64;
+    // 16-byte chunks: every load of a pass is issued before its LDS writes.
+    // Row and chunk of a chunk index come from a float reciprocal with one
+    // correction step (indices stay below 2^13, so the estimate is off by at
+    // most one) instead of an integer division.
+    const int cpr = L.KBs * 8, chunks = M * cpr, NT = NW * 64;
+    const float inv_cpr = 1.0f / (float)cpr, inv_kbs = 1.0f / (float)L.KBs;
+    auto split = [](int q, int d, float inv, int &row, int &rem) {
+      row = (int)((float)q * inv);
+      rem = q - row * d;
+      if (rem < 0) {
+        row--;
+        rem += d;
+      } else if (rem >= d) {
+        row++;
+        rem -= d;
+      }
+    };
     for (int q0 = 0; q0 < chunks; q0 += 4 * NT) {
       uint4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; u++) {
-        const int q = min(q0 + u * NT + tid, chunks - 1);  // past the end: the last chunk again, not stored
-        const int mm = q / (L.KBs * 8), rem = q - mm * L.KBs * 8;
+        int mm, rem;
+        split(min(q0 + u * NT + tid, chunks - 1), cpr, inv_cpr, mm, rem);  // past the end: the last chunk again
         v[u] = *reinterpret_cast<const uint4 *>(xq + (int64_t)mm * K + (int64_t)kb_lo * kGroup + rem * 16);
       }
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         const int q = q0 + u * NT + tid;
         if (q < chunks) {
-          const int mm = q / (L.KBs * 8), rem = q - mm * L.KBs * 8, kb = rem >> 3, c = rem & 7;
+          int mm, rem;
+          split(q, cpr, inv_cpr, mm, rem);
+          const int kb = rem >> 3, c = rem & 7;
           *reinterpret_cast<uint4 *>(codes + mm * L.XS + kb * kGroup + ((c ^ swz(mm)) << 4)) = v[u];
         }
       }
     }
     for (int q = tid; q < M * L.KBs; q += NT) {
-      const int mm = q / L.KBs, kb = q - mm * L.KBs;
+      int mm, kb;
+      split(q, L.KBs, inv_kbs, mm, kb);
       scales[mm * L.SS + kb] = xs[(int64_t)mm * KB + kb_lo + kb];
     }
   }
@@ -463,9 +489,8 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
   const uint8_t *xrow = codes + m * L.XS;
   const float *srow = scales + m * L.SS;
   const int f_lo = (g ^ swz(m)) << 4, f_hi = ((g + 4) ^ swz(m)) << 4;
-  auto consume = [&](int d, int t) {
-    const int j = t / n_w, i = t - j * n_w;
-    const int kr = (wave + i * NW) * U;  // first K block of the unit, relative to the split
+  auto consume = [&](int d, const Item &it) {
+    const int kr = (wave + it.i * NW) * U;  // first K block of the unit, relative to the split
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const uint8_t *blk = xrow + (kr + u) * kGroup;
@@ -480,11 +505,11 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
       }
     }
   };
-  // after item t: if it closed band j, the waves' partial sums meet in LDS and
-  // wave j % NW adds them in wave order and stores the band
-  auto flush = [&](int t) {
-    const int j = t / n_w;
-    if (t - j * n_w != n_w - 1) return;
+  // after item it: if it closed band j, the waves' partial sums meet in LDS
+  // and wave j % NW adds them in wave order and stores the band
+  auto flush = [&](const Item &it) {
+    if (it.i != n_w - 1) return;
+    const int j = it.j;
     v4f *buf = red + (size_t)(j & 1) * NW * RT * 64;
 #pragma unroll
     for (int r = 0; r < RT; r++) buf[(wave * RT + r) * 64 + lane] = acc[r];
@@ -511,31 +536,38 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
 #pragma unroll
     for (int r = 0; r < RT; r++) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
   };
-  // the slot schedule of decode_kernel over this wave's T items
+  // the slot schedule of decode_kernel over this wave's T items; t0 + d counts
+  // items for the control flow, the cursors carry their (band, unit)
+  Item cons{0, 0}, ld = item_at(D);
   int t0 = 0;
   for (; t0 + 2 * D <= T; t0 += D) {
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      consume(d, t0 + d);
-      load(d, t0 + d + D);
-      flush(t0 + d);
+      consume(d, cons);
+      load(d, ld);
+      flush(cons);
+      cons = next(cons);
+      ld = next(ld);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (t0 + D <= T) {
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      consume(d, t0 + d);
-      if (t0 + d + D < T) load(d, t0 + d + D);
-      flush(t0 + d);
+      consume(d, cons);
+      if (t0 + d + D < T) load(d, ld);
+      flush(cons);
+      cons = next(cons);
+      ld = next(ld);
     }
     t0 += D;
   }
 #pragma unroll
   for (int d = 0; d < D - 1; d++)
     if (t0 + d < T) {
-      consume(d, t0 + d);
-      flush(t0 + d);
+      consume(d, cons);
+      flush(cons);
+      cons = next(cons);
     }
 }
 

@@ -186,3 +186,26 @@ def test_shared_schedule_needs_a_unit_per_wave():
     barriers, which is why the host requires at least NW units per split."""
     _, _, closed, _, nbj = shared_schedule(64, 1, 16, 0, 3, 4, 2, 3)
     assert nbj > 0 and closed == []
+
+
+def test_shared_staging_split_is_exact():
+    """The staging loop of decode_shared_kernel splits a chunk index q into
+    (row, rest) by d with a float reciprocal and one correction step instead
+    of an integer division.  Emulated in float32 for every divisor the kernel
+    can use (chunks per row 8 * KBs for 16 <= KBs < 64, and KBs itself) and
+    every index below 16 rows: always equal to divmod."""
+    import numpy as np
+
+    def split(q, d):
+        inv = np.float32(1.0) / np.float32(d)
+        row = (np.float32(q) * inv).astype(np.int64)  # truncation, as the float -> int conversion
+        rem = q - row * d
+        lo, hi = rem < 0, rem >= d
+        row = np.where(lo, row - 1, np.where(hi, row + 1, row))
+        rem = np.where(lo, rem + d, np.where(hi, rem - d, rem))
+        return row, rem
+
+    for d in sorted(set(range(16, 64)) | {8 * k for k in range(16, 64)}):
+        q = np.arange(16 * d, dtype=np.int64)
+        row, rem = split(q, d)
+        assert np.array_equal(row, q // d) and np.array_equal(rem, q % d), d
