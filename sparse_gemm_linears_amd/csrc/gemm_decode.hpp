@@ -359,9 +359,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 // Work items: band b in [0, N / (16 RT)) and K split p in [0, S); workgroup
 // w of the grid (G workgroups, G a multiple of S) takes split p = w % S and
 // bands w / S, w / S + G / S, ...  Each split covers KB / S K blocks (a whole
-// number of U-block units, at least NW units, so that every wave has work in
-// every band).  S = 1 stores y; S > 1 stores fp32 partials part[S][M][N] for
-// launch_splitk_reduce.
+// number of U-block units).  S = 1 stores y; S > 1 stores fp32 partials
+// part[S][M][N] for launch_splitk_reduce.  Two ways to share a workgroup's
+// bands among its waves:
+//   * WB = false: every band's units round-robin over the waves (at least NW
+//     units per split, so that every wave has work in every band), the waves'
+//     partial sums meeting once per band;
+//   * WB = true: whole bands round-robin over the waves (wave v takes the
+//     workgroup's bands v, v + NW, ...), each wave streaming all units of its
+//     bands and storing them itself: no partial sums, no barrier after the
+//     staging.  Waves without a band only help stage the tokens.
 //
 // LDS: codes [M][XS] with XS an odd multiple of 128 bytes (the rows of a
 // column of K blocks alternate 128-byte bank halves), chunk c of K block kb at
@@ -383,7 +390,7 @@ struct SharedTokenLayout {
   }
 };
 
-template <class W, int RT, int NW, int D, int S>
+template <class W, int RT, int NW, int D, int S, bool WB = false>
 __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uint8_t *__restrict__ xq,
                                                                 const float *__restrict__ xs,
                                                                 const float *__restrict__ ws, int M, int N, int K,
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
-  const SharedTokenLayout L(M, K, S, NW, RT);
+  const SharedTokenLayout L(M, K, S, WB ? 0 : NW, RT);
   const int KB = K / kGroup, US = L.KBs / U;  // K blocks per row, units per split
   uint8_t *codes = shared_tokens;
   float *scales = reinterpret_cast<float *>(shared_tokens + (size_t)M * L.XS);
@@ -403,8 +410,12 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
   const int sp = S > 1 ? b0 % S : 0, kb_lo = sp * L.KBs;
   const int bands = N / (16 * RT), first = b0 / S, stride = G / S;
   const int nbj = first < bands ? (bands - first + stride - 1) / stride : 0;  // bands of this workgroup
-  const int n_w = (US - wave + NW - 1) / NW;                                   // units per band of this wave (>= 1)
-  const int T = nbj * n_w;
+  // WB: each wave takes whole bands (the WG's bands wave, wave + NW, ...) and
+  // all their units, so no partial sums meet; else the waves split each band's
+  // units round-robin
+  const int n_w = WB ? US : (US - wave + NW - 1) / NW;  // units per band of this wave (>= 1)
+  const int nbw = WB ? (nbj > wave ? (nbj - wave + NW - 1) / NW : 0) : nbj;  // bands of this wave
+  const int T = nbw * n_w;
   const int m = min(lr, M - 1);
   const rsrc_t rws = make_rsrc(ws, (uint32_t)((N / kGroup) * KB * (int)sizeof(float)));
 
@@ -420,8 +431,10 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
     const int j = t / n_w;
     return Item{j, t - j * n_w};
   };
+  auto band_of = [&](const Item &it) { return WB ? wave + it.j * NW : it.j; };   // index in the WG's band list
+  auto unit_of = [&](const Item &it) { return WB ? it.i : wave + it.i * NW; };  // unit within the split
   auto load = [&](int slot, const Item &it) {
-    const int n0 = (first + it.j * stride) * 16 * RT, kb = kb_lo + (wave + it.i * NW) * U;
+    const int n0 = (first + band_of(it) * stride) * 16 * RT, kb = kb_lo + unit_of(it) * U;
 #pragma unroll
     for (int r = 0; r < RT; r++) a[slot][r] = wop.load(n0 + 16 * r + lr, kb, g);
 #pragma unroll
@@ -490,7 +503,7 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
   const float *srow = scales + m * L.SS;
   const int f_lo = (g ^ swz(m)) << 4, f_hi = ((g + 4) ^ swz(m)) << 4;
   auto consume = [&](int d, const Item &it) {
-    const int kr = (wave + it.i * NW) * U;  // first K block of the unit, relative to the split
+    const int kr = unit_of(it) * U;  // first K block of the unit, relative to the split
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const uint8_t *blk = xrow + (kr + u) * kGroup;
@@ -509,6 +522,22 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
   // and wave j % NW adds them in wave order and stores the band
   auto flush = [&](const Item &it) {
     if (it.i != n_w - 1) return;
+    if constexpr (WB) {
+      const int n0 = (first + band_of(it) * stride) * 16 * RT;
+      if (lr < M) {
+#pragma unroll
+        for (int r = 0; r < RT; r++) {
+          const int n = n0 + 16 * r + 4 * g;
+          if constexpr (S > 1)
+            *reinterpret_cast<v4f *>(part + ((int64_t)sp * M + lr) * N + n) = acc[r];
+          else
+            *reinterpret_cast<uint2 *>(y + (int64_t)lr * N + n) = pack_bf16x4(acc[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RT; r++) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
+      return;
+    }
     const int j = it.j;
     v4f *buf = red + (size_t)(j & 1) * NW * RT * 64;
 #pragma unroll
@@ -577,19 +606,20 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
 constexpr int kSharedTokenMaxLds = 160 * 1024;
 
 // Grid of the shared-token form for this shape (0: the shape does not fit it):
-// the split's K range must hold at least NW units of U blocks, and the codes
-// of the M tokens and the partial sums must fit the LDS.  One workgroup per
-// compute unit per split, or two for at most 8 tokens (whose staging is
-// cheaper; measured on MI355X), each streaming several row bands.
-inline int shared_decode_grid(int M, int N, int K, int S, int U, int NW, int RT, int cus) {
+// the split's K range must hold at least NW units of U blocks (unless each
+// wave takes whole bands, WB), and the codes of the M tokens and the partial
+// sums must fit the LDS.  One workgroup per compute unit per split, or two
+// for at most 8 tokens with the split units (whose staging is cheaper;
+// measured on MI355X), each streaming several row bands.
+inline int shared_decode_grid(int M, int N, int K, int S, int U, int NW, int RT, int cus, bool wb = false) {
   const int KB = K / kGroup;
-  if (M < 1 || M > 16 || N % (16 * RT) != 0 || KB % (S * U) != 0 || KB / S / U < NW) return 0;
-  if (SharedTokenLayout(M, K, S, NW, RT).bytes > (size_t)kSharedTokenMaxLds) return 0;
+  if (M < 1 || M > 16 || N % (16 * RT) != 0 || KB % (S * U) != 0 || (!wb && KB / S / U < NW)) return 0;
+  if (SharedTokenLayout(M, K, S, wb ? 0 : NW, RT).bytes > (size_t)kSharedTokenMaxLds) return 0;
   const int bands = N / (16 * RT);
-  return std::min(bands, (M <= 8 ? 2 : 1) * cus) * S;
+  return std::min(bands, (!wb && M <= 8 ? 2 : 1) * cus) * S;
 }
 
-template <class W, int RT, int NW, int D, int S>
+template <class W, int RT, int NW, int D, int S, bool WB = false>
 hipError_t launch_decode_shared(W wop, const uint8_t *xq, const float *xs, const float *ws, int M, int N, int K,
                                 uint16_t *y, float *part, int grid, hipStream_t stream) {
   constexpr int kMaxDevices = 64;
@@ -599,15 +629,15 @@ hipError_t launch_decode_shared(W wop, const uint8_t *xq, const float *xs, const
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   if (!raised[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_shared_kernel<W, RT, NW, D, S>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_shared_kernel<W, RT, NW, D, S, WB>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kSharedTokenMaxLds);
     if (e != hipSuccess) return e;
     raised[dev].store(true, std::memory_order_release);
   }
   if (S > 1 && !part) return hipErrorInvalidValue;
-  const SharedTokenLayout L(M, K, S, NW, RT);
-  hipLaunchKernelGGL((decode_shared_kernel<W, RT, NW, D, S>), dim3(grid), dim3(NW * 64), L.bytes, stream, wop, xq, xs,
-                     ws, M, N, K, y, part);
+  const SharedTokenLayout L(M, K, S, WB ? 0 : NW, RT);
+  hipLaunchKernelGGL((decode_shared_kernel<W, RT, NW, D, S, WB>), dim3(grid), dim3(NW * 64), L.bytes, stream, wop, xq,
+                     xs, ws, M, N, K, y, part);
   return hipGetLastError();
 }
 

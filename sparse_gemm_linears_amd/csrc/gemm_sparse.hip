@@ -606,16 +606,28 @@ static hipError_t launch_sparse_decode(X xop, const uint8_t *wv, const uint8_t *
   if constexpr (X::kStaged) {
     return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, part, stream);  // M <= 8
   } else {
-    // 3 to 8 tokens on weights of at least 16384 rows and K < 8192: the
-    // shared-token form (measured on MI355X, gate/up 28672 x 4096, weight from
-    // HBM: 16.6 / 18.4 us at 3 / 8 tokens against 23.3 / 20.2 us; at 16 tokens,
-    // and on the smaller weights, the weight-streaming kernel is as fast)
+    // 3 to 16 tokens on weights of at least 16384 rows and K < 8192: the
+    // shared-token form.  From 5 tokens each wave takes whole bands (it
+    // streams all units of its bands, so no partial sums meet and no barrier
+    // follows the staging); at 3 or 4 the waves split each band's units.
+    // Measured on MI355X, gate/up 28672 x 4096, weight from HBM (A/B):
+    //   whole bands     16 tokens 17.7 us, 12: 17.3, 8: 17.0, 4: 16.4, 3: 16.4;
+    //   split units                        12: 19.4 (*), 8: 17.4, 4: 15.9, 3: 15.8;
+    //   (*) 12 and 16 tokens ran the weight-streaming kernel: 19.4 / 20.1 us.
     if constexpr (std::is_same<X, QuantTokens>::value) {
-      if (M >= 3 && M <= 8 && K < 8192 && N >= 16384) {
-        const int grid = shared_decode_grid(M, N, K, 1, SparseWeight4::kUnit, 8, 1, device_cu_count());
-        if (grid > 0)
-          return launch_decode_shared<SparseWeight4, 1, 8, 1, 1>(SparseWeight4{wv, wm, K}, xop.xq, xop.xs, ws, M, N,
-                                                                 K, y, nullptr, grid, stream);
+      if (M >= 3 && M <= 16 && K < 8192 && N >= 16384) {
+        const int cus = device_cu_count();
+        if (M >= 5) {
+          const int grid = shared_decode_grid(M, N, K, 1, SparseWeight4::kUnit, 16, 1, cus, true);
+          if (grid > 0)
+            return launch_decode_shared<SparseWeight4, 1, 16, 2, 1, true>(SparseWeight4{wv, wm, K}, xop.xq, xop.xs,
+                                                                          ws, M, N, K, y, nullptr, grid, stream);
+        } else {
+          const int grid = shared_decode_grid(M, N, K, 1, SparseWeight4::kUnit, 8, 1, cus);
+          if (grid > 0)
+            return launch_decode_shared<SparseWeight4, 1, 8, 1, 1>(SparseWeight4{wv, wm, K}, xop.xq, xop.xs, ws, M,
+                                                                   N, K, y, nullptr, grid, stream);
+        }
       }
     }
     if (M <= 16) return launch_decode_for<X, 1>(xop, wv, wm, ws, M, N, K, y, part, stream);

@@ -209,3 +209,61 @@ def test_shared_staging_split_is_exact():
         q = np.arange(16 * d, dtype=np.int64)
         row, rem = split(q, d)
         assert np.array_equal(row, q // d) and np.array_equal(rem, q % d), d
+
+
+def wave_band_schedule(bands: int, G: int, b0: int, US: int, NW: int, D: int, wave: int):
+    """decode_shared_kernel with whole bands per wave (WB, S = 1): wave v of
+    workgroup b0 takes the workgroup's bands v, v + NW, ... (its j-th band is
+    b0 + (v + j NW) G) and all US units of each, through the D-slot schedule."""
+    nbj = (bands - b0 + G - 1) // G if b0 < bands else 0
+    nbw = (nbj - wave + NW - 1) // NW if nbj > wave else 0
+    T = nbw * US
+    item = lambda t: (b0 + (wave + (t // US) * NW) * G, t % US)
+    slot = [None] * D
+    loads, consumed, stored = [], [], []
+
+    def load(d, t):
+        loads.append(item(t))
+        slot[d] = item(t)
+
+    def consume(d, t):
+        assert slot[d] == item(t)
+        consumed.append(slot[d])
+        if t % US == US - 1:
+            stored.append(item(t)[0])
+
+    if T > 0:
+        for d in range(D):
+            load(d, min(d, T - 1))
+    t0 = 0
+    while t0 + 2 * D <= T:
+        for d in range(D):
+            consume(d, t0 + d)
+            load(d, t0 + d + D)
+        t0 += D
+    if t0 + D <= T:
+        for d in range(D):
+            consume(d, t0 + d)
+            if t0 + d + D < T:
+                load(d, t0 + d + D)
+        t0 += D
+    for d in range(D - 1):
+        if t0 + d < T:
+            consume(d, t0 + d)
+    return loads, consumed, stored, [item(t) for t in range(T)]
+
+
+@pytest.mark.parametrize("bands,G,US,NW", [(1792, 256, 8, 16), (1792, 256, 8, 8), (1024, 256, 8, 16), (37, 8, 3, 4),
+                                           (5, 8, 8, 16), (300, 64, 1, 3)])
+@pytest.mark.parametrize("D", [1, 2, 3])
+def test_wave_band_schedule_covers_every_band_once(bands, G, US, NW, D):
+    every, bands_stored = [], []
+    for b0 in range(G):
+        for wave in range(NW):
+            loads, consumed, stored, items = wave_band_schedule(bands, G, b0, US, NW, D, wave)
+            assert all(b < bands and u < US for b, u in loads), (b0, wave)
+            assert consumed == items
+            every.extend(consumed)
+            bands_stored.extend(stored)
+    assert sorted(every) == sorted((b, u) for b in range(bands) for u in range(US))
+    assert sorted(bands_stored) == list(range(bands))  # each band stored once, by the wave that summed it

@@ -2,8 +2,10 @@
 the oracle on every output element.
 
 fp8_block_gemm takes it for 3 to 16 tokens on K < 8192 when the weight has at
-least 16384 rows, fp8_sparse24_gemm for 3 to 8 tokens.  The cases cover both
-grids (two workgroups per compute unit up to 8 tokens, one above), token
+least 16384 rows (the waves split each band's units), fp8_sparse24_gemm for 3
+to 16 tokens (split units at 3 and 4 tokens, whole bands per wave from 5).  The cases cover both grids (two
+workgroups per compute unit up to 8 tokens, one above), bands per workgroup
+fewer than its waves (2:4: 4 or 7 bands over 16 waves), token
 counts that leave rows of the 16-row fragment past M (they re-read the last
 token and are not stored), K
 ranges of 1 to 4 units per wave and band (equal and unequal over the
@@ -38,7 +40,8 @@ def test_dense_shared_decode(gpu_lib, M, N, K):
     assert_gemm_close(y, oracle.gemm(xq, xs, wq, ws), f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(3, 16384, 4096), (6, 16384, 5120), (8, 28672, 4096)])
+@pytest.mark.parametrize("M,N,K", [(3, 16384, 4096), (6, 16384, 5120), (8, 28672, 4096), (12, 16384, 2048),
+                                   (16, 28672, 4096), (16, 16384, 7168)])
 def test_sparse_shared_decode(gpu_lib, M, N, K):
     _, (xq, xs) = acts(M, K, 43 + M)
     w = si.weights(N, K, seed=11 + N % 89)
