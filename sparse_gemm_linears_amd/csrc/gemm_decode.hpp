@@ -352,9 +352,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 // range in LDS once and then streams several row bands through it; the waves
 // split each band's K units round-robin as in decode_kernel, keep D units of
 // weight loads in flight across band boundaries, and meet once per band in
-// LDS.  Measured on MI355X (gate/up 28672 x 4096, weight from HBM): 3 tokens
-// 22.0 us against 25.5 us, 16 tokens 25.3 us against 27.4 us (dense); 3
-// tokens 16.6 us against 23.3 us (2:4).
+// LDS (or, with WB below, each wave takes whole bands).  Measured on MI355X
+// (gate/up 28672 x 4096, weight from HBM), against decode_kernel: dense 3
+// tokens 22.0 us against 25.5 us, 16 tokens 25.3 us against 27.4 us; 2:4 3
+// tokens 16.6 us against 23.3 us, 16 tokens (WB) 17.7 us against 20.1 us.
 //
 // Work items: band b in [0, N / (16 RT)) and K split p in [0, S); workgroup
 // w of the grid (G workgroups, G a multiple of S) takes split p = w % S and
@@ -374,10 +375,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 // column of K blocks alternate 128-byte bank halves), chunk c of K block kb at
 // kb * 128 + 16 * (c ^ swz(m)) as in the tile kernels, so 16-lane fragment
 // reads of 16 tokens hit distinct banks; then scales [M][KBs + 1] (the extra
-// word staggers the tokens' banks); then the partial sums of the waves,
-// double-buffered by band parity: the wave that adds band j's partials reads
-// buffer j & 1 before the barrier of band j + 1, and the next writes to that
-// buffer come after it.
+// word staggers the tokens' banks); then (split units only) the partial sums
+// of the waves, double-buffered by band parity: the wave that adds band j's
+// partials reads buffer j & 1 before the barrier of band j + 1, and the next
+// writes to that buffer come after it.
 struct SharedTokenLayout {
   int KBs, XS, SS;
   size_t red_off, bytes;
