@@ -33,28 +33,101 @@
 namespace fp8lin {
 
 // Tokens already quantized by fp8_quant_act: codes and one scale per K block.
-struct QuantTokens {
+// The codes come straight from global memory (L2).  Read from global memory
+// too, a fragment's scales are 16 words in 16 different 128-byte lines (one
+// line per token row) for 64 useful bytes, and cost the memory pipeline about
+// as much as the codes.  With kLds the scales of the workgroup's K range are
+// first copied into LDS by linear loads (rows of `ss` floats, ss odd, so that
+// the 16 tokens of a fragment read 16 different banks).  That staging and its
+// barrier pay only with more than one token tile and a pipeline of loads per
+// wave; launch_decode_kernel decides per launch.
+template <bool kLds>
+struct QuantTokensT {
   const uint8_t *xq;
   const float *xs;
   int K;
-  static constexpr bool kStaged = false, kE8 = false;
+  const float *sl = nullptr;  // LDS scales [M][ss] of K blocks kb_lo ..
+  int kb_lo = 0, ss = 1;
+  static constexpr bool kStaged = false, kE8 = false, kScaleLds = kLds;
   typedef float Scale;
   struct Raw {
     v8i q;
-    float s;
+    std::conditional_t<kLds, int, float> s;  // LDS index of the scale, or the scale
   };
+  static __host__ __device__ int scale_stride(int blocks) { return blocks | 1; }
+  static size_t scale_lds_bytes(int M, int blocks) { return (size_t)M * scale_stride(blocks) * sizeof(float); }
   __device__ __forceinline__ void stage(uint8_t *, int, int, int) {}
+  // Where the scales of K blocks kb0 .. kb0 + blocks - 1 go in LDS; before
+  // any load(), which records the LDS index of its scale.
+  __device__ __forceinline__ void bind_scales(float *lds, int kb0, int blocks) {
+    sl = lds;
+    kb_lo = kb0;
+    ss = scale_stride(blocks);
+  }
+  // Copies xs[m][kb_lo .. kb_lo + blocks) for every token into LDS, all
+  // threads of the workgroup taking part, in passes of kScalePass words per
+  // thread (past the end: the last word again, not stored).  The first pass
+  // is split in two: load_scales issues its loads, store_scales waits for
+  // them and writes LDS (and runs any further passes whole), so loads issued
+  // in between stay in flight across the wait.  A barrier must follow before
+  // make().
+  static constexpr int kScalePass = 4;
+  __device__ __forceinline__ void scale_pass_load(float (&v)[kScalePass], int q0, int M, int blocks, int tid,
+                                                  int nthreads) const {
+    const int KB = K / kGroup, total = M * blocks;
+#pragma unroll
+    for (int u = 0; u < kScalePass; u++) {
+      const int q = min(q0 + u * nthreads + tid, total - 1);
+      const int m = q / blocks;
+      v[u] = xs[(int64_t)m * KB + kb_lo + (q - m * blocks)];
+    }
+  }
+  __device__ __forceinline__ void scale_pass_store(const float (&v)[kScalePass], int q0, int M, int blocks, int tid,
+                                                   int nthreads) const {
+    float *lds = const_cast<float *>(sl);
+    const int total = M * blocks;
+#pragma unroll
+    for (int u = 0; u < kScalePass; u++) {
+      const int q = q0 + u * nthreads + tid;
+      if (q < total) {
+        const int m = q / blocks;
+        lds[m * ss + (q - m * blocks)] = v[u];
+      }
+    }
+  }
+  __device__ __forceinline__ void load_scales(float (&v)[kScalePass], int M, int blocks, int tid, int nthreads) const {
+    if (M * blocks > 0) scale_pass_load(v, 0, M, blocks, tid, nthreads);  // uniform
+  }
+  __device__ __forceinline__ void store_scales(const float (&v)[kScalePass], int M, int blocks, int tid,
+                                               int nthreads) const {
+    const int total = M * blocks;
+    if (total == 0) return;
+    scale_pass_store(v, 0, M, blocks, tid, nthreads);
+    for (int q0 = kScalePass * nthreads; q0 < total; q0 += kScalePass * nthreads) {
+      float w[kScalePass];
+      scale_pass_load(w, q0, M, blocks, tid, nthreads);
+      scale_pass_store(w, q0, M, blocks, tid, nthreads);
+    }
+  }
   __device__ __forceinline__ Raw load(int m, int kb, int g) const {
     Raw r;
     r.q = load_frag_global(xq + (int64_t)m * K + (int64_t)kb * kGroup, g);
-    r.s = xs[(int64_t)m * (K / kGroup) + kb];
+    if constexpr (kLds)
+      r.s = m * ss + (kb - kb_lo);
+    else
+      r.s = xs[(int64_t)m * (K / kGroup) + kb];
     return r;
   }
   __device__ __forceinline__ void make(const Raw &r, v8i &frag, float &s) const {
     frag = r.q;
-    s = r.s;
+    if constexpr (kLds)
+      s = sl[r.s];
+    else
+      s = r.s;
   }
+  QuantTokensT<false> global_scales() const { return QuantTokensT<false>{xq, xs, K}; }
 };
+using QuantTokens = QuantTokensT<true>;
 
 // Tokens quantized by fp8_quant_act_ue8m0: codes and one exponent byte per K
 // block; the MFMA applies 2^(e - 127) itself.
@@ -62,7 +135,7 @@ struct QuantTokensE8 {
   const uint8_t *xq;
   const uint8_t *xe;
   int K;
-  static constexpr bool kStaged = false, kE8 = true;
+  static constexpr bool kStaged = false, kE8 = true, kScaleLds = false;
   typedef uint8_t Scale;
   struct Raw {
     v8i q;
@@ -90,7 +163,7 @@ struct StagedTokens {
   int K;
   uint8_t *codes;
   float *scales;
-  static constexpr bool kStaged = true, kE8 = false;
+  static constexpr bool kStaged = true, kE8 = false, kScaleLds = false;
   typedef float Scale;
   struct Raw {
     v8i q;
@@ -194,8 +267,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
   // vector loads complete in order, so a wait can leave younger slots in
   // flight (scalar loads complete out of order and would need a full wait).
   const rsrc_t rws = make_rsrc(ws_row, (uint32_t)(KB * sizeof(typename X::Scale)));
+  // unit i of this wave (with staged scales the first slots are loaded on
+  // every path, also by a wave without units: its index is clamped into the
+  // row, and those loads are never consumed)
+  auto unit_of = [&](int i) { return X::kScaleLds ? min(kb0 + wave + i * NW, KU - 1) : kb0 + wave + i * NW; };
   auto load_w = [&](int slot, int i) {
-    const int kb = (kb0 + wave + i * NW) * U;  // first K block of the unit
+    const int kb = unit_of(i) * U;  // first K block of the unit
 #pragma unroll
     for (int r = 0; r < RT; r++) a[slot][r] = wop.load(n0 + 16 * r + lr, kb, g);
 #pragma unroll
@@ -207,7 +284,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
     }
   };
   auto load_x = [&](int slot, int i) {
-    const int kb = (kb0 + wave + i * NW) * U;
+    const int kb = unit_of(i) * U;
 #pragma unroll
     for (int c = 0; c < CT; c++)
 #pragma unroll
@@ -235,13 +312,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
     if (n_w > 0)
 #pragma unroll
       for (int d = 0; d < D; d++) load_x(d, min(d, n_w - 1));
-  } else if (n_w > 0) {
-    // slot by slot, in the loop's order (the waits count loads by age)
+  } else {
+    extern __shared__ __align__(16) uint8_t staged_lds[];
+    // token scales of this split's K blocks: loads issued before the first
+    // slots' loads, LDS writes after them (the wait covers only the former)
+    float sv[4];
+    if constexpr (X::kScaleLds) {
+      static_assert(X::kScalePass == 4, "sv holds one pass of scale words");
+      xop.bind_scales(reinterpret_cast<float *>(staged_lds), kb0 * U, KBr * U);
+      xop.load_scales(sv, M, KBr * U, threadIdx.x, NW * 64);
+    }
+    // slot by slot, in the loop's order (the waits count loads by age); with
+    // staged scales on every path, so that the wait for the scale loads can
+    // leave these in flight (a branch around them would make it wait for all)
+    if (X::kScaleLds || n_w > 0) {
 #pragma unroll
-    for (int d = 0; d < D; d++) {
-      load_w(d, min(d, n_w - 1));
-      load_x(d, min(d, n_w - 1));
-      __builtin_amdgcn_sched_barrier(0);
+      for (int d = 0; d < D; d++) {
+        load_w(d, max(min(d, n_w - 1), 0));
+        load_x(d, max(min(d, n_w - 1), 0));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (X::kScaleLds) {
+      xop.store_scales(sv, M, KBr * U, threadIdx.x, NW * 64);
+      __syncthreads();
     }
   }
   auto consume = [&](int d) {
@@ -599,6 +693,76 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
       flush(cons);
       cons = next(cons);
     }
+}
+
+// Host side of decode_kernel: the dynamic LDS its token policy needs (the
+// codes and scales StagedTokens quantizes, or the scales of a split's K range
+// that QuantTokens stages), and a launch that raises the kernel's LDS limit
+// once per device where that and the static reduction buffer pass 64 KB.
+template <class X>
+inline size_t decode_token_lds(int M, int K, int S, int U) {
+  if constexpr (X::kStaged) {
+    return StagedTokens::lds_bytes(M, K);
+  } else if constexpr (X::kScaleLds) {
+    const int KU = K / kGroup / U;
+    return X::scale_lds_bytes(M, (KU + S - 1) / S * U);
+  } else {
+    return 0;
+  }
+}
+
+// The fewest U-block units a wave of any split gets (floor of the smallest
+// split's units over the waves).
+inline int min_units_per_wave(int K, int S, int U, int NW) {
+  const int KU = K / kGroup / U, KBs = (KU + S - 1) / S;
+  int fewest = KU;
+  for (int sp = 0; sp < S; sp++) fewest = std::min(fewest, std::max(0, std::min(KU, (sp + 1) * KBs) - sp * KBs));
+  return fewest / NW;
+}
+
+// Quantized tokens take their scales through LDS from 17 tokens on (two or
+// more token tiles) where every wave has at least two units, so that the
+// staging and its barrier are spread over a pipeline of loads.  Measured on
+// MI355X against scales read from global memory, Llama-3-8B weights from HBM
+// (graph-free A/B, results bit-identical):
+//   6144 x 4096   20 / 32 / 64 tokens 10.6 / 12.0 / 17.9 -> 9.7 / 10.6 / 15.0 us
+//   4096 x 4096   32 / 64 tokens       9.8 / 13.1 -> 9.1 / 11.8 us
+//   4096 x 14336  20 / 32 tokens       17.6 / 18.8 -> 16.9 / 18.1 us
+//   2:4, 6144 x 4096 at 64 tokens 17.9 -> 15.0 us, 4096 x 14336 at 32 18.4 ->
+//   17.3 us.
+// At up to 16 tokens it was level to 6 % slower, and so it was with a single
+// unit per wave (the 2:4 four-block units on K = 4096: 3 to 7 % slower).
+constexpr int kScaleLdsMinTokens = 17, kScaleLdsMinUnitsPerWave = 2;
+
+template <class W, class X, int RT, int CT, int NW, int D, int S>
+hipError_t launch_decode_kernel(W wop, X xop, const typename X::Scale *ws, int M, int N, int K, uint16_t *y,
+                                float *part, hipStream_t stream) {
+  if constexpr (X::kScaleLds) {
+    if (M < kScaleLdsMinTokens || min_units_per_wave(K, S, weight_unit<W>::value, NW) < kScaleLdsMinUnitsPerWave)
+      return launch_decode_kernel<W, decltype(xop.global_scales()), RT, CT, NW, D, S>(wop, xop.global_scales(), ws, M,
+                                                                                       N, K, y, part, stream);
+  }
+  constexpr size_t kStaticLds = sizeof(v4f) * 64 * RT * CT * (NW > 1 ? NW - 1 : 1);
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> raised[kMaxDevices];
+  const size_t lds = decode_token_lds<X>(M, K, S, weight_unit<W>::value);
+  if (kStaticLds + lds > 64 * 1024) {
+    if (kStaticLds + lds > 160 * 1024) return hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!raised[dev].load(std::memory_order_acquire)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<W, X, RT, CT, NW, D, S>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - kStaticLds));
+      if (e != hipSuccess) return e;
+      raised[dev].store(true, std::memory_order_release);
+    }
+  }
+  const int bands = N / (16 * RT);
+  hipLaunchKernelGGL((decode_kernel<W, X, RT, CT, NW, D, S>), dim3(bands, S), dim3(NW * 64), lds, stream, wop, xop, ws,
+                     M, N, K, y, S > 1 ? part : nullptr);
+  return hipGetLastError();
 }
 
 // Host side of the shared-token form.  The kernel's LDS (up to 160 KB) is

@@ -541,19 +541,10 @@ static hipError_t launch_tile(const uint8_t *xq, const float *xs, const uint8_t 
 template <class Wt, class X, int RT, int CT, int NW, int D, int S>
 static hipError_t launch_decode_with(Wt wop, X xop, const typename X::Scale *ws, int M,
                                 int N, int K, uint16_t *y, float *part, hipStream_t stream) {
-  const size_t lds = X::kStaged ? StagedTokens::lds_bytes(M, K) : 0;
-  const int bands = N / (16 * RT);
-  if constexpr (S == 1) {
-    hipLaunchKernelGGL((decode_kernel<Wt, X, RT, CT, NW, D>), dim3(bands), dim3(NW * 64), lds, stream,
-                       wop, xop, ws, M, N, K, y, nullptr);
-    return hipGetLastError();
-  } else {
-    if (!part) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_kernel<Wt, X, RT, CT, NW, D, S>), dim3(bands, S), dim3(NW * 64), lds, stream,
-                       wop, xop, ws, M, N, K, y, part);
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? launch_splitk_reduce(part, S, (int64_t)M * N, y, stream) : e;
-  }
+  if (S > 1 && !part) return hipErrorInvalidValue;
+  const hipError_t e = launch_decode_kernel<Wt, X, RT, CT, NW, D, S>(wop, xop, ws, M, N, K, y, part, stream);
+  if (S == 1 || e != hipSuccess) return e;
+  return launch_splitk_reduce(part, S, (int64_t)M * N, y, stream);
 }
 
 // Four-block units (one unit in flight per wave: four blocks) where K holds a

@@ -267,3 +267,79 @@ def test_wave_band_schedule_covers_every_band_once(bands, G, US, NW, D):
             bands_stored.extend(stored)
     assert sorted(every) == sorted((b, u) for b in range(bands) for u in range(US))
     assert sorted(bands_stored) == list(range(bands))  # each band stored once, by the wave that summed it
+
+
+def scale_stride(blocks: int) -> int:
+    """QuantTokens::scale_stride: rows of an odd number of floats."""
+    return blocks | 1
+
+
+def stage_scales(xs, M: int, KB: int, kb_lo: int, blocks: int, nthreads: int, k_pass: int = 4):
+    """QuantTokens::stage_scales over all threads of a workgroup: (LDS contents by
+    index, global indices read).  Mirrors the kernel's passes: every thread loads
+    k_pass words (past the end: the last word again), then writes those in range."""
+    ss = scale_stride(blocks)
+    lds, reads = {}, []
+    total = M * blocks
+    for q0 in range(0, total, k_pass * nthreads):
+        for tid in range(nthreads):
+            vals = []
+            for u in range(k_pass):
+                q = min(q0 + u * nthreads + tid, total - 1)
+                m = q // blocks
+                g = m * KB + kb_lo + (q - m * blocks)
+                reads.append(g)
+                vals.append(xs[g])
+            for u in range(k_pass):
+                q = q0 + u * nthreads + tid
+                if q < total:
+                    m = q // blocks
+                    idx = m * ss + (q - m * blocks)
+                    assert idx not in lds, "an LDS word written twice"
+                    lds[idx] = vals[u]
+    return lds, reads
+
+
+# (M, K blocks, S, U, waves): every launched decode configuration on quantized
+# tokens (the Llama-3-8B and DeepSeek-V3 shapes, dense and 2:4) plus ragged ones
+@pytest.mark.parametrize("M,KB,S,U,NW", [
+    (1, 32, 1, 1, 16), (3, 32, 1, 1, 16), (16, 32, 1, 4, 8), (16, 32, 1, 1, 8), (32, 32, 1, 1, 8), (64, 32, 2, 1, 8),
+    (16, 112, 4, 1, 8), (32, 112, 4, 4, 8), (20, 112, 4, 1, 8), (1, 112, 1, 1, 4), (64, 56, 1, 1, 8),
+    (13, 65, 4, 1, 8), (7, 9, 4, 1, 8), (5, 3, 4, 1, 8), (64, 144, 1, 4, 8), (64, 33, 2, 1, 16)])
+def test_token_scale_staging_and_indices(M, KB, S, U, NW):
+    """Each split's workgroup stages exactly the scales of its K range: every
+    global read is inside xs and inside the split's blocks, every LDS word of
+    the range is written once with the right value, and the LDS index each
+    load records (m * ss + kb - kb_lo) points at xs[m][kb] for every block the
+    split's waves load, within the bytes the host allocates for the launch."""
+    KU = KB // U
+    KBs = (KU + S - 1) // S
+    xs = list(range(M * KB))  # distinct values: the LDS word names its source
+    alloc_words = M * scale_stride(KBs * U)
+    for split in range(S):
+        kb0 = split * KBs if S > 1 else 0
+        KBr = max(0, min(KU, kb0 + KBs) - kb0) if S > 1 else KU
+        lo, blocks = kb0 * U, KBr * U
+        lds, reads = stage_scales(xs, M, KB, lo, blocks, NW * 64)
+        ss = scale_stride(blocks)
+        assert len(lds) == M * blocks
+        for g in reads:
+            assert 0 <= g < M * KB and lo <= g % KB < lo + blocks
+        for wave in range(NW):
+            loads, _, _, (r0, r1) = schedule(KB, NW, 2, S, split, wave, U=U)
+            for kb in loads:
+                assert r0 <= kb < r1
+                for m in range(M):
+                    idx = m * ss + (kb - lo)
+                    assert idx < alloc_words
+                    assert lds[idx] == xs[m * KB + kb]
+
+
+def test_token_scale_rows_hit_distinct_banks():
+    """The 16 tokens of a fragment read their scales from 16 different LDS banks
+    (32-bit banks, 64 of them) for every K range the launches stage."""
+    for blocks in (1, 3, 7, 8, 14, 16, 28, 32, 56, 112):
+        ss = scale_stride(blocks)
+        for kb in range(blocks):
+            banks = {(m * ss + kb) % 64 for m in range(16)}
+            assert len(banks) == 16, (blocks, kb)
