@@ -33,13 +33,20 @@
 namespace fp8lin {
 
 // Tokens already quantized by fp8_quant_act: codes and one scale per K block.
-// The codes come straight from global memory (L2).  Read from global memory
-// too, a fragment's scales are 16 words in 16 different 128-byte lines (one
-// line per token row) for 64 useful bytes, and cost the memory pipeline about
-// as much as the codes.  With kLds the scales of the workgroup's K range are
-// first copied into LDS by linear loads (rows of `ss` floats, ss odd, so that
-// the 16 tokens of a fragment read 16 different banks).  That staging and its
-// barrier pay only with more than one token tile and a pipeline of loads per
+// Read as MFMA fragments, a 16-token tile of codes is 16 rows x 64 bytes per
+// load instruction, and a fragment's scales are 16 words in 16 different
+// 128-byte lines (one line per token row): both cost the memory pipeline a
+// line access per row for half a line or less.  With kLds, instead:
+//   * the scales of the workgroup's K range are first copied into LDS by
+//     linear loads (rows of `ss` floats, ss odd, so that the 16 tokens of a
+//     fragment read 16 different banks);
+//   * each code tile is loaded as two runs of 8 whole 128-byte rows (lane l:
+//     row 8h + l / 8, chunk position l % 8), written to a tile of the wave's
+//     own LDS in that order and read back as the fragment: chunk position p
+//     of row r holds logical chunk p ^ swz(r), so the fragment reads are
+//     conflict-free as in the tile kernels.  No other wave touches the tile,
+//     and one wave's LDS operations complete in order, so no barrier.
+// That pays only with more than one token tile and a pipeline of loads per
 // wave; launch_decode_kernel decides per launch.
 template <bool kLds>
 struct QuantTokensT {
@@ -47,22 +54,36 @@ struct QuantTokensT {
   const float *xs;
   int K;
   const float *sl = nullptr;  // LDS scales [M][ss] of K blocks kb_lo ..
+  uint8_t *tl = nullptr;      // this wave's code tiles in LDS, 2 KB each
   int kb_lo = 0, ss = 1;
   static constexpr bool kStaged = false, kE8 = false, kScaleLds = kLds;
   typedef float Scale;
-  struct Raw {
+  struct RawFrag {
     v8i q;
-    std::conditional_t<kLds, int, float> s;  // LDS index of the scale, or the scale
+    float s;
   };
+  struct RawLin {
+    uint4 lo, hi;  // rows 0-7 and 8-15 of the tile, chunk position lane % 8
+    int s;         // LDS index of the scale
+  };
+  typedef std::conditional_t<kLds, RawLin, RawFrag> Raw;
   static __host__ __device__ int scale_stride(int blocks) { return blocks | 1; }
-  static size_t scale_lds_bytes(int M, int blocks) { return (size_t)M * scale_stride(blocks) * sizeof(float); }
+  static __host__ __device__ size_t scale_lds_bytes(int M, int blocks) {
+    return ((size_t)M * scale_stride(blocks) * sizeof(float) + 15) / 16 * 16;
+  }
+  // dynamic LDS of a workgroup: the scales, then NW x CT code tiles
+  static size_t lds_bytes(int M, int blocks, int NW, int CT) {
+    return scale_lds_bytes(M, blocks) + (size_t)NW * CT * 2048;
+  }
   __device__ __forceinline__ void stage(uint8_t *, int, int, int) {}
-  // Where the scales of K blocks kb0 .. kb0 + blocks - 1 go in LDS; before
-  // any load(), which records the LDS index of its scale.
-  __device__ __forceinline__ void bind_scales(float *lds, int kb0, int blocks) {
-    sl = lds;
+  // Where the scales of K blocks kb0 .. kb0 + blocks - 1 and this wave's code
+  // tiles go in LDS; before any load(), which records the LDS index of its
+  // scale.
+  __device__ __forceinline__ void bind(uint8_t *lds, int kb0, int blocks, int M, int wave, int CT) {
+    sl = reinterpret_cast<const float *>(lds);
     kb_lo = kb0;
     ss = scale_stride(blocks);
+    tl = lds + scale_lds_bytes(M, blocks) + (size_t)wave * CT * 2048;
   }
   // Copies xs[m][kb_lo .. kb_lo + blocks) for every token into LDS, all
   // threads of the workgroup taking part, in passes of kScalePass words per
@@ -109,21 +130,36 @@ struct QuantTokensT {
       scale_pass_store(w, q0, M, blocks, tid, nthreads);
     }
   }
-  __device__ __forceinline__ Raw load(int m, int kb, int g) const {
-    Raw r;
+  // global-memory form: token m's fragment of K block kb, and its scale
+  __device__ __forceinline__ RawFrag load(int m, int kb, int g) const {
+    RawFrag r;
     r.q = load_frag_global(xq + (int64_t)m * K + (int64_t)kb * kGroup, g);
-    if constexpr (kLds)
-      r.s = m * ss + (kb - kb_lo);
-    else
-      r.s = xs[(int64_t)m * (K / kGroup) + kb];
+    r.s = xs[(int64_t)m * (K / kGroup) + kb];
     return r;
   }
-  __device__ __forceinline__ void make(const Raw &r, v8i &frag, float &s) const {
+  __device__ __forceinline__ void make(const RawFrag &r, v8i &frag, float &s) const {
     frag = r.q;
-    if constexpr (kLds)
-      s = sl[r.s];
-    else
-      s = r.s;
+    s = r.s;
+  }
+  // LDS form: token tile c (rows 16c .., clamped to M - 1) of K block kb in
+  // whole rows; m is this lane's token, for its scale
+  __device__ __forceinline__ RawLin load_lin(int c, int m, int kb, int M) const {
+    const int lane = threadIdx.x & 63, r = lane >> 3, p = lane & 7;
+    const uint8_t *blk = xq + (int64_t)kb * kGroup;
+    RawLin x;
+    x.lo = ldg16(blk + (int64_t)min(16 * c + r, M - 1) * K + 16 * (p ^ swz(r)));
+    x.hi = ldg16(blk + (int64_t)min(16 * c + 8 + r, M - 1) * K + 16 * (p ^ swz(r + 8)));
+    x.s = m * ss + (kb - kb_lo);
+    return x;
+  }
+  __device__ __forceinline__ void make_lin(int c, const RawLin &x, v8i &frag, float &s) const {
+    const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
+    uint8_t *t = tl + c * 2048;
+    *reinterpret_cast<uint4 *>(t + 16 * lane) = x.lo;
+    *reinterpret_cast<uint4 *>(t + 1024 + 16 * lane) = x.hi;
+    frag = make_v8i(*reinterpret_cast<const uint4 *>(t + lr * 128 + ((g ^ swz(lr)) << 4)),
+                    *reinterpret_cast<const uint4 *>(t + lr * 128 + (((g + 4) ^ swz(lr)) << 4)));
+    s = sl[x.s];
   }
   QuantTokensT<false> global_scales() const { return QuantTokensT<false>{xq, xs, K}; }
 };
@@ -288,7 +324,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 #pragma unroll
     for (int c = 0; c < CT; c++)
 #pragma unroll
-      for (int u = 0; u < U; u++) b[slot][c][u] = xop.load(mrow[c], kb + u, g);
+      for (int u = 0; u < U; u++) {
+        if constexpr (X::kScaleLds)
+          b[slot][c][u] = xop.load_lin(c, mrow[c], kb + u, M);
+        else
+          b[slot][c][u] = xop.load(mrow[c], kb + u, g);
+      }
   };
 
   v4f acc[RT][CT];
@@ -319,7 +360,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
     float sv[4];
     if constexpr (X::kScaleLds) {
       static_assert(X::kScalePass == 4, "sv holds one pass of scale words");
-      xop.bind_scales(reinterpret_cast<float *>(staged_lds), kb0 * U, KBr * U);
+      xop.bind(staged_lds, kb0 * U, KBr * U, M, wave, CT);
       xop.load_scales(sv, M, KBr * U, threadIdx.x, NW * 64);
     }
     // slot by slot, in the loop's order (the waits count loads by age); with
@@ -352,7 +393,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
           for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(a[d][r], bf, acc[r][c], sw[d][u], ex);
         } else {
           float sx;
-          xop.make(b[d][c][u], bf, sx);
+          if constexpr (X::kScaleLds)
+            xop.make_lin(c, b[d][c][u], bf, sx);
+          else
+            xop.make(b[d][c][u], bf, sx);
           const float scl = sx * sw[d][u];
 #pragma unroll
           for (int r = 0; r < RT; r++) {
@@ -697,55 +741,29 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
 
 // Host side of decode_kernel: the dynamic LDS its token policy needs (the
 // codes and scales StagedTokens quantizes, or the scales of a split's K range
-// that QuantTokens stages), and a launch that raises the kernel's LDS limit
-// once per device where that and the static reduction buffer pass 64 KB.
-template <class X>
+// and the waves' code tiles of QuantTokens), and a launch that raises the
+// kernel's LDS limit once per device where that and the static reduction
+// buffer pass 64 KB.
+template <class X, int NW, int CT>
 inline size_t decode_token_lds(int M, int K, int S, int U) {
   if constexpr (X::kStaged) {
     return StagedTokens::lds_bytes(M, K);
   } else if constexpr (X::kScaleLds) {
     const int KU = K / kGroup / U;
-    return X::scale_lds_bytes(M, (KU + S - 1) / S * U);
+    return X::lds_bytes(M, (KU + S - 1) / S * U, NW, CT);
   } else {
     return 0;
   }
 }
 
-// The fewest U-block units a wave of any split gets (floor of the smallest
-// split's units over the waves).
-inline int min_units_per_wave(int K, int S, int U, int NW) {
-  const int KU = K / kGroup / U, KBs = (KU + S - 1) / S;
-  int fewest = KU;
-  for (int sp = 0; sp < S; sp++) fewest = std::min(fewest, std::max(0, std::min(KU, (sp + 1) * KBs) - sp * KBs));
-  return fewest / NW;
-}
-
-// Quantized tokens take their scales through LDS from 17 tokens on (two or
-// more token tiles) where every wave has at least two units, so that the
-// staging and its barrier are spread over a pipeline of loads.  Measured on
-// MI355X against scales read from global memory, Llama-3-8B weights from HBM
-// (graph-free A/B, results bit-identical):
-//   6144 x 4096   20 / 32 / 64 tokens 10.6 / 12.0 / 17.9 -> 9.7 / 10.6 / 15.0 us
-//   4096 x 4096   32 / 64 tokens       9.8 / 13.1 -> 9.1 / 11.8 us
-//   4096 x 14336  20 / 32 tokens       17.6 / 18.8 -> 16.9 / 18.1 us
-//   2:4, 6144 x 4096 at 64 tokens 17.9 -> 15.0 us, 4096 x 14336 at 32 18.4 ->
-//   17.3 us.
-// At up to 16 tokens it was level to 6 % slower, and so it was with a single
-// unit per wave (the 2:4 four-block units on K = 4096: 3 to 7 % slower).
-constexpr int kScaleLdsMinTokens = 17, kScaleLdsMinUnitsPerWave = 2;
-
+// decode_kernel<W, X, ...> itself, with the dynamic LDS its token policy needs
 template <class W, class X, int RT, int CT, int NW, int D, int S>
-hipError_t launch_decode_kernel(W wop, X xop, const typename X::Scale *ws, int M, int N, int K, uint16_t *y,
-                                float *part, hipStream_t stream) {
-  if constexpr (X::kScaleLds) {
-    if (M < kScaleLdsMinTokens || min_units_per_wave(K, S, weight_unit<W>::value, NW) < kScaleLdsMinUnitsPerWave)
-      return launch_decode_kernel<W, decltype(xop.global_scales()), RT, CT, NW, D, S>(wop, xop.global_scales(), ws, M,
-                                                                                       N, K, y, part, stream);
-  }
+hipError_t launch_decode_kernel_as(W wop, X xop, const typename X::Scale *ws, int M, int N, int K, uint16_t *y,
+                                   float *part, hipStream_t stream) {
   constexpr size_t kStaticLds = sizeof(v4f) * 64 * RT * CT * (NW > 1 ? NW - 1 : 1);
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> raised[kMaxDevices];
-  const size_t lds = decode_token_lds<X>(M, K, S, weight_unit<W>::value);
+  const size_t lds = decode_token_lds<X, NW, CT>(M, K, S, weight_unit<W>::value);
   if (kStaticLds + lds > 64 * 1024) {
     if (kStaticLds + lds > 160 * 1024) return hipErrorInvalidValue;
     int dev = 0;
@@ -763,6 +781,51 @@ hipError_t launch_decode_kernel(W wop, X xop, const typename X::Scale *ws, int M
   hipLaunchKernelGGL((decode_kernel<W, X, RT, CT, NW, D, S>), dim3(bands, S), dim3(NW * 64), lds, stream, wop, xop, ws,
                      M, N, K, y, S > 1 ? part : nullptr);
   return hipGetLastError();
+}
+
+// The fewest U-block units a wave of any split gets (floor of the smallest
+// split's units over the waves).
+inline int min_units_per_wave(int K, int S, int U, int NW) {
+  const int KU = K / kGroup / U, KBs = (KU + S - 1) / S;
+  int fewest = KU;
+  for (int sp = 0; sp < S; sp++) fewest = std::min(fewest, std::max(0, std::min(KU, (sp + 1) * KBs) - sp * KBs));
+  return fewest / NW;
+}
+
+// Quantized tokens go through LDS (QuantTokensT<true>: staged scales, codes
+// read in whole rows) from 17 tokens on (two or more token tiles) where every
+// wave has at least two units, so that the scale staging and its barrier are
+// spread over a pipeline of loads; only for one-block units and at most 16
+// fragments of loads in flight per wave (RT * CT * D), where the kernel keeps
+// its registers (the four-block 2:4 units and the three-deep 64-row bands
+// spill).  Measured on MI355X against tokens read from global memory,
+// Llama-3-8B weights from HBM (A/B in one process, results bit-identical):
+//   6144 x 4096   20 / 32 / 64 tokens 10.5 / 12.0 / 17.9 -> 9.1 / 10.1 / 12.9 us
+//   4096 x 4096   32 / 64 tokens       9.9 / 13.0 -> 8.1 / 11.3 us
+//   4096 x 14336  20 / 32 tokens       17.4 / 18.7 -> 16.9 / 17.8 us
+//   2:4 at 64 tokens: 6144 x 4096 17.9 -> 12.6 us, 4096 x 4096 13.2 -> 10.9 us;
+//   2:4 4096 x 14336 at 32 tokens 18.1 -> 16.4 us.
+// The scale staging alone gave about half of that.  At up to 16 tokens it
+// was level to 6 % slower, and so it was with a single unit per wave (the
+// 2:4 four-block units on K = 4096: 3 to 7 % slower).
+constexpr int kScaleLdsMinTokens = 17, kScaleLdsMinUnitsPerWave = 2, kScaleLdsMaxFragsInFlight = 16;
+
+template <class W, class X, int RT, int CT, int NW, int D, int S>
+hipError_t launch_decode_kernel(W wop, X xop, const typename X::Scale *ws, int M, int N, int K, uint16_t *y,
+                                float *part, hipStream_t stream) {
+  constexpr int U = weight_unit<W>::value;
+  if constexpr (X::kScaleLds) {
+    using G = decltype(xop.global_scales());
+    if constexpr (U > 1 || CT < 2 || RT * CT * D > kScaleLdsMaxFragsInFlight) {
+      return launch_decode_kernel<W, G, RT, CT, NW, D, S>(wop, xop.global_scales(), ws, M, N, K, y, part, stream);
+    } else {
+      if (M < kScaleLdsMinTokens || min_units_per_wave(K, S, U, NW) < kScaleLdsMinUnitsPerWave)
+        return launch_decode_kernel<W, G, RT, CT, NW, D, S>(wop, xop.global_scales(), ws, M, N, K, y, part, stream);
+      return launch_decode_kernel_as<W, X, RT, CT, NW, D, S>(wop, xop, ws, M, N, K, y, part, stream);
+    }
+  } else {
+    return launch_decode_kernel_as<W, X, RT, CT, NW, D, S>(wop, xop, ws, M, N, K, y, part, stream);
+  }
 }
 
 // Host side of the shared-token form.  The kernel's LDS (up to 160 KB) is

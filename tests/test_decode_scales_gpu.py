@@ -1,17 +1,19 @@
-"""Decode GEMMs on quantized tokens whose per-token scales go through LDS.
+"""Decode GEMMs on quantized tokens that go through LDS.
 
-From 17 tokens on, where every wave of every K split has at least two units,
-the decode kernel copies the scales of its K range into LDS once per
-workgroup (linear loads, odd row stride) and the fragments read them there;
-below that, or with fewer units per wave, the scales come from global memory
-(gemm_decode.hpp, QuantTokensT and launch_decode_kernel).  Covered here:
+From 17 tokens on, where every wave of every K split has at least two units
+(one-block units, at most 16 fragments in flight per wave), the decode kernel
+copies the scales of its K range into LDS once per workgroup (linear loads,
+odd row stride), and each wave loads its token code tiles in whole 128-byte
+rows, writes them to its own LDS tile and reads the MFMA fragments back;
+otherwise both come from global memory as fragments (gemm_decode.hpp,
+QuantTokensT and launch_decode_kernel).  Covered here:
 
   * against the oracle: the 6144- and 4096-row Llama weights at 17 to 64
     tokens (ragged token tiles, one and two K splits), the long-K down weight
     split four ways, a ragged K (33 K blocks), dense and 2:4;
   * the two paths give the same bits where the kernel configuration is the
-    same: the first 16 rows of a 17-token call (scales through LDS) equal a
-    16-token call (scales from global memory);
+    same: the first 16 rows of a 17-token call (through LDS) equal a 16-token
+    call (from global memory);
   * graph replays of the LDS path with eager calls in between."""
 from __future__ import annotations
 

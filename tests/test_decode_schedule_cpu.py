@@ -343,3 +343,36 @@ def test_token_scale_rows_hit_distinct_banks():
         for kb in range(blocks):
             banks = {(m * ss + kb) % 64 for m in range(16)}
             assert len(banks) == 16, (blocks, kb)
+
+
+def swz(r: int) -> int:
+    """The tile kernels' 16-byte chunk swizzle of row r (gemm_common.hpp)."""
+    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2)
+
+
+@pytest.mark.parametrize("M,c", [(64, 0), (64, 3), (17, 1), (23, 1), (40, 2)])
+def test_linear_code_tile_round_trip(M, c):
+    """QuantTokensT<true>::load_lin / make_lin: each lane loads 16 bytes of a
+    whole-row run (8 rows of 128 bytes per load, rows past M clamped to M - 1),
+    writes them to the wave's LDS tile at 16 * lane (and 1024 + 16 * lane), and
+    reads back the MFMA fragment: lane (g, lr) must get bytes 16g .. 16g + 15
+    and 64 + 16g .. 64 + 16g + 15 of token min(16c + lr, M - 1)'s K block."""
+    K = 4096
+    kb = 5
+    x = [[(m * 131 + b * 7) % 251 for b in range(K)] for m in range(M)]
+    tile = [None] * 2048
+    for lane in range(64):
+        r, p = lane >> 3, lane & 7
+        for h in (0, 1):
+            row = min(16 * c + 8 * h + r, M - 1)
+            chunk = p ^ swz(8 * h + r)
+            for j in range(16):
+                tile[1024 * h + 16 * lane + j] = x[row][kb * 128 + 16 * chunk + j]
+    assert None not in tile
+    for lane in range(64):
+        g, lr = lane >> 4, lane & 15
+        m = min(16 * c + lr, M - 1)
+        lo = tile[lr * 128 + ((g ^ swz(lr)) << 4):][:16]
+        hi = tile[lr * 128 + (((g + 4) ^ swz(lr)) << 4):][:16]
+        assert lo == x[m][kb * 128 + 16 * g:][:16]
+        assert hi == x[m][kb * 128 + 64 + 16 * g:][:16]
