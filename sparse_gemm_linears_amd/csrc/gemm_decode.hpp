@@ -32,6 +32,36 @@
 
 namespace fp8lin {
 
+// A 16-row x 128-byte operand tile in whole rows.  Read as an MFMA fragment
+// (16 rows x 64 bytes per load instruction) the tile costs the memory
+// pipeline a cache-line access per row for half a line; read as two runs of
+// 8 whole rows it costs half as many.  Lane l loads row 8h + l / 8 at chunk
+// position l % 8, holding logical chunk (l % 8) ^ swz(row), for h = 0 (lo)
+// and 1 (hi); written to a 2 KB LDS tile in lane order, the tile then has
+// logical chunk p ^ swz(r) at position p of row r, and the fragment reads back
+// with the tile kernels' conflict-free offsets.  A tile is private to one
+// wave, whose LDS operations complete in order: no barrier.
+struct RowRuns {
+  uint4 lo, hi;
+};
+// rows row0 .. row0 + 15 (each clamped to last_row) of a matrix with `stride`
+// bytes per row, from byte `col` of each row
+__device__ __forceinline__ RowRuns load_row_runs(const uint8_t *base, int64_t row0, int64_t last_row, int64_t stride,
+                                                 int64_t col) {
+  const int lane = threadIdx.x & 63, q = lane >> 3, p = lane & 7;
+  RowRuns x;
+  x.lo = ldg16(base + min(row0 + q, last_row) * stride + col + 16 * (p ^ swz(q)));
+  x.hi = ldg16(base + min(row0 + 8 + q, last_row) * stride + col + 16 * (p ^ swz(q + 8)));
+  return x;
+}
+__device__ __forceinline__ v8i row_runs_to_frag(const RowRuns &x, uint8_t *tile) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
+  *reinterpret_cast<uint4 *>(tile + 16 * lane) = x.lo;
+  *reinterpret_cast<uint4 *>(tile + 1024 + 16 * lane) = x.hi;
+  return make_v8i(*reinterpret_cast<const uint4 *>(tile + lr * 128 + ((g ^ swz(lr)) << 4)),
+                  *reinterpret_cast<const uint4 *>(tile + lr * 128 + (((g + 4) ^ swz(lr)) << 4)));
+}
+
 // Tokens already quantized by fp8_quant_act: codes and one scale per K block.
 // Read as MFMA fragments, a 16-token tile of codes is 16 rows x 64 bytes per
 // load instruction, and a fragment's scales are 16 words in 16 different
@@ -40,12 +70,8 @@ namespace fp8lin {
 //   * the scales of the workgroup's K range are first copied into LDS by
 //     linear loads (rows of `ss` floats, ss odd, so that the 16 tokens of a
 //     fragment read 16 different banks);
-//   * each code tile is loaded as two runs of 8 whole 128-byte rows (lane l:
-//     row 8h + l / 8, chunk position l % 8), written to a tile of the wave's
-//     own LDS in that order and read back as the fragment: chunk position p
-//     of row r holds logical chunk p ^ swz(r), so the fragment reads are
-//     conflict-free as in the tile kernels.  No other wave touches the tile,
-//     and one wave's LDS operations complete in order, so no barrier.
+//   * each code tile goes through one of the wave's LDS tiles in whole rows
+//     (load_row_runs / row_runs_to_frag above).
 // That pays only with more than one token tile and a pipeline of loads per
 // wave; launch_decode_kernel decides per launch.
 template <bool kLds>
@@ -72,7 +98,7 @@ struct QuantTokensT {
     return ((size_t)M * scale_stride(blocks) * sizeof(float) + 15) / 16 * 16;
   }
   // dynamic LDS of a workgroup: the scales, then NW x CT code tiles
-  static size_t lds_bytes(int M, int blocks, int NW, int CT) {
+  static __host__ __device__ size_t lds_bytes(int M, int blocks, int NW, int CT) {
     return scale_lds_bytes(M, blocks) + (size_t)NW * CT * 2048;
   }
   __device__ __forceinline__ void stage(uint8_t *, int, int, int) {}
@@ -144,21 +170,15 @@ struct QuantTokensT {
   // LDS form: token tile c (rows 16c .., clamped to M - 1) of K block kb in
   // whole rows; m is this lane's token, for its scale
   __device__ __forceinline__ RawLin load_lin(int c, int m, int kb, int M) const {
-    const int lane = threadIdx.x & 63, r = lane >> 3, p = lane & 7;
-    const uint8_t *blk = xq + (int64_t)kb * kGroup;
+    const RowRuns runs = load_row_runs(xq, 16 * c, M - 1, K, (int64_t)kb * kGroup);
     RawLin x;
-    x.lo = ldg16(blk + (int64_t)min(16 * c + r, M - 1) * K + 16 * (p ^ swz(r)));
-    x.hi = ldg16(blk + (int64_t)min(16 * c + 8 + r, M - 1) * K + 16 * (p ^ swz(r + 8)));
+    x.lo = runs.lo;
+    x.hi = runs.hi;
     x.s = m * ss + (kb - kb_lo);
     return x;
   }
   __device__ __forceinline__ void make_lin(int c, const RawLin &x, v8i &frag, float &s) const {
-    const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
-    uint8_t *t = tl + c * 2048;
-    *reinterpret_cast<uint4 *>(t + 16 * lane) = x.lo;
-    *reinterpret_cast<uint4 *>(t + 1024 + 16 * lane) = x.hi;
-    frag = make_v8i(*reinterpret_cast<const uint4 *>(t + lr * 128 + ((g ^ swz(lr)) << 4)),
-                    *reinterpret_cast<const uint4 *>(t + lr * 128 + (((g + 4) ^ swz(lr)) << 4)));
+    frag = row_runs_to_frag(RowRuns{x.lo, x.hi}, tl + c * 2048);
     s = sl[x.s];
   }
   QuantTokensT<false> global_scales() const { return QuantTokensT<false>{xq, xs, K}; }
@@ -205,7 +225,7 @@ struct StagedTokens {
     v8i q;
     float s;
   };
-  static size_t lds_bytes(int M, int K) { return (size_t)M * K + (size_t)4 * M * (K / kGroup); }
+  static __host__ __device__ size_t lds_bytes(int M, int K) { return (size_t)M * K + (size_t)4 * M * (K / kGroup); }
   static constexpr int kMaxPasses = 4;  // groups per 16-lane team
   // All threads of the workgroup take part (every 16-lane team stays active).
   // Every load is issued before any arithmetic, so the staging costs one
@@ -273,15 +293,59 @@ template <class W>
 struct weight_unit<W, std::void_t<decltype(W::kUnit)>> {
   static constexpr int value = W::kUnit;
 };
+// A weight policy with kRows loads its tiles in whole rows (Frag = RowRuns)
+// and turns them into MFMA fragments through a wave-private LDS tile
+// (to_frag) just before use.
+template <class W, class = void>
+struct weight_rows {
+  static constexpr bool value = false;
+};
+template <class W>
+struct weight_rows<W, std::void_t<decltype(W::kRows)>> {
+  static constexpr bool value = W::kRows;
+};
+
+// Dynamic LDS of decode_kernel: the waves' weight tiles (kRows weights), then
+// what the token policy stages (StagedTokens' codes and scales, or
+// QuantTokensT<true>'s scales and code tiles), then the reduction buffer of
+// the waves' partial sums.  Where the three pass the 160 KB of a workgroup,
+// the reduction buffer starts at 0 instead, after a barrier at the end of the
+// main loop (every wave is then past its last use of the rest).  The host and
+// the kernel both lay it out with plan().
+constexpr size_t kDecodeMaxLds = 160 * 1024;
+template <class W, class X, int RT, int CT, int NW>
+struct DecodeLds {
+  static constexpr size_t kWeightTiles = weight_rows<W>::value ? (size_t)NW * RT * 2048 : 0;
+  static constexpr size_t kRed = NW > 1 ? (size_t)(NW - 1) * RT * CT * 64 * sizeof(v4f) : 0;
+  struct Plan {
+    size_t tokens, red_off, bytes;
+    bool alias;
+  };
+  static __host__ __device__ Plan plan(int M, int K, int S) {
+    size_t tokens = 0;
+    if constexpr (X::kStaged) {
+      tokens = StagedTokens::lds_bytes(M, K);
+    } else if constexpr (X::kScaleLds) {
+      const int U = weight_unit<W>::value, KU = K / kGroup / U;
+      tokens = X::lds_bytes(M, (KU + S - 1) / S * U, NW, CT);
+    }
+    const size_t front = (kWeightTiles + tokens + 15) / 16 * 16;
+    if (front + kRed <= kDecodeMaxLds) return Plan{tokens, front, front + kRed, false};
+    return Plan{tokens, 0, front > kRed ? front : kRed, true};
+  }
+};
 
 template <class W, class X, int RT, int CT, int NW, int D, int S = 1>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typename X::Scale *__restrict__ ws,
                                                          int M, int N, int K, uint16_t *__restrict__ y,
                                                          float *__restrict__ part) {
   static_assert(128 % (16 * RT) == 0, "a workgroup's rows must sit in one 128-row scale block");
-  __shared__ v4f red[NW > 1 ? NW - 1 : 1][RT * CT][64];
+  using Lds = DecodeLds<W, X, RT, CT, NW>;
+  extern __shared__ __align__(16) uint8_t decode_lds[];
+  uint8_t *const token_lds = decode_lds + Lds::kWeightTiles;  // what the token policy stages
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t *const wtile = decode_lds + (size_t)wave * RT * 2048;  // kRows weights: this wave's tiles
   const int g = lane >> 4, lr = lane & 15;
   constexpr int U = weight_unit<W>::value;
   const int KB = K / kGroup, KU = KB / U;  // K blocks, units of U blocks
@@ -347,20 +411,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
     if (n_w > 0)
 #pragma unroll
       for (int d = 0; d < D; d++) load_w(d, min(d, n_w - 1));
-    extern __shared__ __align__(16) uint8_t staged_lds[];
-    xop.stage(staged_lds, M, threadIdx.x, NW * 64);
+    xop.stage(token_lds, M, threadIdx.x, NW * 64);
     __syncthreads();
     if (n_w > 0)
 #pragma unroll
       for (int d = 0; d < D; d++) load_x(d, min(d, n_w - 1));
   } else {
-    extern __shared__ __align__(16) uint8_t staged_lds[];
     // token scales of this split's K blocks: loads issued before the first
     // slots' loads, LDS writes after them (the wait covers only the former)
     float sv[4];
     if constexpr (X::kScaleLds) {
       static_assert(X::kScalePass == 4, "sv holds one pass of scale words");
-      xop.bind(staged_lds, kb0 * U, KBr * U, M, wave, CT);
+      xop.bind(token_lds, kb0 * U, KBr * U, M, wave, CT);
       xop.load_scales(sv, M, KBr * U, threadIdx.x, NW * 64);
     }
     // slot by slot, in the loop's order (the waits count loads by age); with
@@ -379,7 +441,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
       __syncthreads();
     }
   }
-  auto consume = [&](int d) {
+  // consume slot d with its weight fragments `af` (a[d] itself, or for kRows
+  // weights the fragments made from it through this wave's LDS tiles)
+  auto consume_with = [&](int d, const auto &af) {
 #pragma unroll
     for (int u = 0; u < U; u++)
 #pragma unroll
@@ -390,7 +454,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
           uint32_t ex;
           xop.make(b[d][c][u], bf, ex);
 #pragma unroll
-          for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(a[d][r], bf, acc[r][c], sw[d][u], ex);
+          for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(af[r], bf, acc[r][c], sw[d][u], ex);
         } else {
           float sx;
           if constexpr (X::kScaleLds)
@@ -401,12 +465,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 #pragma unroll
           for (int r = 0; r < RT; r++) {
             if constexpr (U == 1)
-              acc[r][c] += scl * wop.mma(a[d][r], bf);
+              acc[r][c] += scl * wop.mma(af[r], bf);
             else
-              acc[r][c] += scl * wop.mma(a[d][r], bf, u);
+              acc[r][c] += scl * wop.mma(af[r], bf, u);
           }
         }
       }
+  };
+  auto consume = [&](int d) {
+    if constexpr (weight_rows<W>::value) {
+      v8i af[RT];
+#pragma unroll
+      for (int r = 0; r < RT; r++) af[r] = wop.to_frag(a[d][r], wtile + r * 2048);
+      consume_with(d, af);
+    } else {
+      consume_with(d, a[d]);
+    }
   };
   // Rounds of D blocks.  While two more full rounds remain, every slot is
   // consumed and refilled on every path, so each wait counts loads exactly
@@ -440,11 +514,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
     if (i0 + d < n_w) consume(d);
 
   if (NW > 1) {
+    // the partial sums of waves 1 .. NW - 1 meet in LDS (over the tiles and
+    // staged tokens where those leave no room: every wave is then first past
+    // its last use of them)
+    const auto plan = Lds::plan(M, K, S);
+    v4f *red = reinterpret_cast<v4f *>(decode_lds + plan.red_off);
+    if (plan.alias) __syncthreads();
     if (wave > 0) {
 #pragma unroll
       for (int r = 0; r < RT; r++)
 #pragma unroll
-        for (int c = 0; c < CT; c++) red[wave - 1][r * CT + c][lane] = acc[r][c];
+        for (int c = 0; c < CT; c++) red[((wave - 1) * RT * CT + r * CT + c) * 64 + lane] = acc[r][c];
     }
     __syncthreads();
     if (wave != 0) return;
@@ -453,7 +533,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 #pragma unroll
       for (int r = 0; r < RT; r++)
 #pragma unroll
-        for (int c = 0; c < CT; c++) acc[r][c] += red[w][r * CT + c][lane];
+        for (int c = 0; c < CT; c++) acc[r][c] += red[(w * RT * CT + r * CT + c) * 64 + lane];
   }
   if constexpr (S > 1) {
     const int sp = (int)blockIdx.y;
@@ -739,40 +819,29 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
     }
 }
 
-// Host side of decode_kernel: the dynamic LDS its token policy needs (the
-// codes and scales StagedTokens quantizes, or the scales of a split's K range
-// and the waves' code tiles of QuantTokens), and a launch that raises the
-// kernel's LDS limit once per device where that and the static reduction
-// buffer pass 64 KB.
-template <class X, int NW, int CT>
-inline size_t decode_token_lds(int M, int K, int S, int U) {
-  if constexpr (X::kStaged) {
-    return StagedTokens::lds_bytes(M, K);
-  } else if constexpr (X::kScaleLds) {
-    const int KU = K / kGroup / U;
-    return X::lds_bytes(M, (KU + S - 1) / S * U, NW, CT);
-  } else {
-    return 0;
-  }
+// Host side of decode_kernel: its dynamic LDS (DecodeLds), and a launch that
+// raises the kernel's LDS limit once per device where that passes 64 KB.
+template <class W, class X, int RT, int CT, int NW>
+inline size_t decode_lds_bytes(int M, int K, int S) {
+  return DecodeLds<W, X, RT, CT, NW>::plan(M, K, S).bytes;
 }
 
 // decode_kernel<W, X, ...> itself, with the dynamic LDS its token policy needs
 template <class W, class X, int RT, int CT, int NW, int D, int S>
 hipError_t launch_decode_kernel_as(W wop, X xop, const typename X::Scale *ws, int M, int N, int K, uint16_t *y,
                                    float *part, hipStream_t stream) {
-  constexpr size_t kStaticLds = sizeof(v4f) * 64 * RT * CT * (NW > 1 ? NW - 1 : 1);
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> raised[kMaxDevices];
-  const size_t lds = decode_token_lds<X, NW, CT>(M, K, S, weight_unit<W>::value);
-  if (kStaticLds + lds > 64 * 1024) {
-    if (kStaticLds + lds > 160 * 1024) return hipErrorInvalidValue;
+  const size_t lds = decode_lds_bytes<W, X, RT, CT, NW>(M, K, S);
+  if (lds > 64 * 1024) {
+    if (lds > kDecodeMaxLds) return hipErrorInvalidValue;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     if (!raised[dev].load(std::memory_order_acquire)) {
       e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_kernel<W, X, RT, CT, NW, D, S>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - kStaticLds));
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeMaxLds);
       if (e != hipSuccess) return e;
       raised[dev].store(true, std::memory_order_release);
     }

@@ -430,12 +430,31 @@ struct DenseWeight {
   __device__ __forceinline__ Frag load(int64_t row, int kb, int g) const {
     return load_frag_global(wq + row * K + (int64_t)kb * kGroup, g);
   }
-  __device__ __forceinline__ v4f mma(const Frag &a, const v8i &b) const {
+  __device__ __forceinline__ v4f mma(const v8i &a, const v8i &b) const {
     return mfma_16x16x128_fp8(a, b, v4f{0.f, 0.f, 0.f, 0.f});
   }
-  __device__ __forceinline__ v4f mma_e8(const Frag &a, const v8i &b, const v4f &c, uint32_t ea, uint32_t eb) const {
+  __device__ __forceinline__ v4f mma_e8(const v8i &a, const v8i &b, const v4f &c, uint32_t ea, uint32_t eb) const {
     return mfma_16x16x128_fp8_e8(a, b, c, ea, eb);
   }
+};
+
+// The dense weight for decode_kernel: each 16-row tile is loaded as two runs
+// of 8 whole rows and made into the MFMA fragment through the wave's LDS tile
+// (load_row_runs / row_runs_to_frag).  Measured on MI355X against fragment
+// loads (A/B in one process, weights from HBM, quantized tokens):
+// 6144 x 4096 at 1 / 4 / 16 / 32 tokens 7.3 / 7.9 / 9.2 / 10.3 -> 6.8 / 6.8 /
+// 8.0 / 9.5 us, 4096 x 4096 5.4 / 6.1 / 7.4 / 8.3 -> 5.3 / 5.4 / 6.7 / 8.0 us,
+// 4096 x 14336 at 4 / 8 tokens 13.1 / 15.2 -> 12.5 / 13.2 us (level at 1 and
+// 16).
+struct DenseWeightRows : DenseWeight {
+  static constexpr bool kRows = true;
+  typedef RowRuns Frag;
+  // `row` is this lane's row of a 16-row tile starting at a multiple of 16
+  __device__ __forceinline__ Frag load(int64_t row, int kb, int) const {
+    const int64_t row0 = row & ~int64_t(15);
+    return load_row_runs(wq, row0, row0 + 15, K, (int64_t)kb * kGroup);
+  }
+  __device__ __forceinline__ v8i to_frag(const Frag &x, uint8_t *tile) const { return row_runs_to_frag(x, tile); }
 };
 
 // ===================================================== split-K reduction ==
@@ -595,8 +614,23 @@ template <class X, int RT, int CT, int NW, int D, int S = 1>
 static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scale *ws, int M, int N, int K,
                                 uint16_t *y, float *part, hipStream_t stream) {
   if (S > 1 && !part) return hipErrorInvalidValue;
-  const hipError_t e =
-      launch_decode_kernel<DenseWeight, X, RT, CT, NW, D, S>(DenseWeight{wq, K}, xop, ws, M, N, K, y, part, stream);
+  // whole-row weight tiles for up to 32 quantized tokens on weights of fewer
+  // than 16384 rows (see DenseWeightRows), except one token on long K.
+  // Slower with them or level (A/B on MI355X): the 28672-row gate/up weight
+  // at one or two tokens (5-16 % slower), the 4096 x 14336 weight at one
+  // token (4 %), the tokens quantized in the kernel (one or two: 2-8 % on the
+  // smaller weights), and 33-64 tokens (-3 to +4 %: there the tiles, the
+  // staged tokens and the reduction buffer share LDS across a barrier).
+  hipError_t e = hipSuccess;
+  bool rows = false;
+  if constexpr (std::is_same<X, QuantTokens>::value) {
+    rows = N < 16384 && M <= 32 && !(M == 1 && K >= 8192);
+    if (rows)
+      e = launch_decode_kernel<DenseWeightRows, X, RT, CT, NW, D, S>(DenseWeightRows{{wq, K}}, xop, ws, M, N, K, y,
+                                                                     part, stream);
+  }
+  if (!rows)
+    e = launch_decode_kernel<DenseWeight, X, RT, CT, NW, D, S>(DenseWeight{wq, K}, xop, ws, M, N, K, y, part, stream);
   if (S == 1 || e != hipSuccess) return e;
   return launch_splitk_reduce(part, S, (int64_t)M * N, y, stream);
 }
