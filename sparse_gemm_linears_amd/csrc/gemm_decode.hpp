@@ -66,40 +66,40 @@ __device__ __forceinline__ v8i row_runs_to_frag(const RowRuns &x, uint8_t *tile)
 // Read as MFMA fragments, a 16-token tile of codes is 16 rows x 64 bytes per
 // load instruction, and a fragment's scales are 16 words in 16 different
 // 128-byte lines (one line per token row): both cost the memory pipeline a
-// line access per row for half a line or less.  With kLds, instead:
-//   * the scales of the workgroup's K range are first copied into LDS by
-//     linear loads (rows of `ss` floats, ss odd, so that the 16 tokens of a
-//     fragment read 16 different banks);
-//   * each code tile goes through one of the wave's LDS tiles in whole rows
-//     (load_row_runs / row_runs_to_frag above).
-// That pays only with more than one token tile and a pipeline of loads per
-// wave; launch_decode_kernel decides per launch.
-template <bool kLds>
+// line access per row for half a line or less.  The modes:
+//   0: both as fragments from global memory;
+//   1: each code tile goes through one of the wave's LDS tiles in whole rows
+//      (load_row_runs / row_runs_to_frag above); scales from global memory;
+//   2: as 1, and the scales of the workgroup's K range are first copied into
+//      LDS by linear loads (rows of `ss` floats, ss odd, so that the 16 tokens
+//      of a fragment read 16 different banks), behind a barrier.
+// launch_decode_kernel picks the mode per launch.
+template <int kMode>
 struct QuantTokensT {
   const uint8_t *xq;
   const float *xs;
   int K;
-  const float *sl = nullptr;  // LDS scales [M][ss] of K blocks kb_lo ..
-  uint8_t *tl = nullptr;      // this wave's code tiles in LDS, 2 KB each
+  const float *sl = nullptr;  // mode 2: LDS scales [M][ss] of K blocks kb_lo ..
+  uint8_t *tl = nullptr;      // modes 1, 2: this wave's code tiles in LDS, 2 KB each
   int kb_lo = 0, ss = 1;
-  static constexpr bool kStaged = false, kE8 = false, kScaleLds = kLds;
+  static constexpr bool kStaged = false, kE8 = false, kCodeLds = kMode >= 1, kScaleLds = kMode == 2;
   typedef float Scale;
   struct RawFrag {
     v8i q;
     float s;
   };
   struct RawLin {
-    uint4 lo, hi;  // rows 0-7 and 8-15 of the tile, chunk position lane % 8
-    int s;         // LDS index of the scale
+    uint4 lo, hi;                                // rows 0-7 and 8-15 of the tile, chunk position lane % 8
+    std::conditional_t<kScaleLds, int, float> s;  // LDS index of the scale, or the scale
   };
-  typedef std::conditional_t<kLds, RawLin, RawFrag> Raw;
+  typedef std::conditional_t<kCodeLds, RawLin, RawFrag> Raw;
   static __host__ __device__ int scale_stride(int blocks) { return blocks | 1; }
   static __host__ __device__ size_t scale_lds_bytes(int M, int blocks) {
     return ((size_t)M * scale_stride(blocks) * sizeof(float) + 15) / 16 * 16;
   }
-  // dynamic LDS of a workgroup: the scales, then NW x CT code tiles
+  // dynamic LDS of a workgroup: the scales (mode 2), then NW x CT code tiles
   static __host__ __device__ size_t lds_bytes(int M, int blocks, int NW, int CT) {
-    return scale_lds_bytes(M, blocks) + (size_t)NW * CT * 2048;
+    return (kScaleLds ? scale_lds_bytes(M, blocks) : 0) + (size_t)NW * CT * 2048;
   }
   __device__ __forceinline__ void stage(uint8_t *, int, int, int) {}
   // Where the scales of K blocks kb0 .. kb0 + blocks - 1 and this wave's code
@@ -109,7 +109,7 @@ struct QuantTokensT {
     sl = reinterpret_cast<const float *>(lds);
     kb_lo = kb0;
     ss = scale_stride(blocks);
-    tl = lds + scale_lds_bytes(M, blocks) + (size_t)wave * CT * 2048;
+    tl = lds + (kScaleLds ? scale_lds_bytes(M, blocks) : 0) + (size_t)wave * CT * 2048;
   }
   // Copies xs[m][kb_lo .. kb_lo + blocks) for every token into LDS, all
   // threads of the workgroup taking part, in passes of kScalePass words per
@@ -174,16 +174,25 @@ struct QuantTokensT {
     RawLin x;
     x.lo = runs.lo;
     x.hi = runs.hi;
-    x.s = m * ss + (kb - kb_lo);
+    if constexpr (kScaleLds)
+      x.s = m * ss + (kb - kb_lo);
+    else
+      x.s = xs[(int64_t)m * (K / kGroup) + kb];
     return x;
   }
   __device__ __forceinline__ void make_lin(int c, const RawLin &x, v8i &frag, float &s) const {
     frag = row_runs_to_frag(RowRuns{x.lo, x.hi}, tl + c * 2048);
-    s = sl[x.s];
+    if constexpr (kScaleLds)
+      s = sl[x.s];
+    else
+      s = x.s;
   }
-  QuantTokensT<false> global_scales() const { return QuantTokensT<false>{xq, xs, K}; }
+  template <int kTo>
+  QuantTokensT<kTo> as_mode() const {
+    return QuantTokensT<kTo>{xq, xs, K};
+  }
 };
-using QuantTokens = QuantTokensT<true>;
+using QuantTokens = QuantTokensT<2>;
 
 // Tokens quantized by fp8_quant_act_ue8m0: codes and one exponent byte per K
 // block; the MFMA applies 2^(e - 127) itself.
@@ -191,7 +200,7 @@ struct QuantTokensE8 {
   const uint8_t *xq;
   const uint8_t *xe;
   int K;
-  static constexpr bool kStaged = false, kE8 = true, kScaleLds = false;
+  static constexpr bool kStaged = false, kE8 = true, kCodeLds = false, kScaleLds = false;
   typedef uint8_t Scale;
   struct Raw {
     v8i q;
@@ -219,7 +228,7 @@ struct StagedTokens {
   int K;
   uint8_t *codes;
   float *scales;
-  static constexpr bool kStaged = true, kE8 = false, kScaleLds = false;
+  static constexpr bool kStaged = true, kE8 = false, kCodeLds = false, kScaleLds = false;
   typedef float Scale;
   struct Raw {
     v8i q;
@@ -307,7 +316,7 @@ struct weight_rows<W, std::void_t<decltype(W::kRows)>> {
 
 // Dynamic LDS of decode_kernel: the waves' weight tiles (kRows weights), then
 // what the token policy stages (StagedTokens' codes and scales, or
-// QuantTokensT<true>'s scales and code tiles), then the reduction buffer of
+// QuantTokensT's code tiles and scales), then the reduction buffer of
 // the waves' partial sums.  Where the three pass the 160 KB of a workgroup,
 // the reduction buffer starts at 0 instead, after a barrier at the end of the
 // main loop (every wave is then past its last use of the rest).  The host and
@@ -325,7 +334,7 @@ struct DecodeLds {
     size_t tokens = 0;
     if constexpr (X::kStaged) {
       tokens = StagedTokens::lds_bytes(M, K);
-    } else if constexpr (X::kScaleLds) {
+    } else if constexpr (X::kCodeLds) {
       const int U = weight_unit<W>::value, KU = K / kGroup / U;
       tokens = X::lds_bytes(M, (KU + S - 1) / S * U, NW, CT);
     }
@@ -389,7 +398,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
     for (int c = 0; c < CT; c++)
 #pragma unroll
       for (int u = 0; u < U; u++) {
-        if constexpr (X::kScaleLds)
+        if constexpr (X::kCodeLds)
           b[slot][c][u] = xop.load_lin(c, mrow[c], kb + u, M);
         else
           b[slot][c][u] = xop.load(mrow[c], kb + u, g);
@@ -420,9 +429,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
     // token scales of this split's K blocks: loads issued before the first
     // slots' loads, LDS writes after them (the wait covers only the former)
     float sv[4];
+    if constexpr (X::kCodeLds) xop.bind(token_lds, kb0 * U, KBr * U, M, wave, CT);
     if constexpr (X::kScaleLds) {
       static_assert(X::kScalePass == 4, "sv holds one pass of scale words");
-      xop.bind(token_lds, kb0 * U, KBr * U, M, wave, CT);
       xop.load_scales(sv, M, KBr * U, threadIdx.x, NW * 64);
     }
     // slot by slot, in the loop's order (the waits count loads by age); with
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
           for (int r = 0; r < RT; r++) acc[r][c] = wop.mma_e8(af[r], bf, acc[r][c], sw[d][u], ex);
         } else {
           float sx;
-          if constexpr (X::kScaleLds)
+          if constexpr (X::kCodeLds)
             xop.make_lin(c, b[d][c][u], bf, sx);
           else
             xop.make(b[d][c][u], bf, sx);
@@ -861,37 +870,51 @@ inline int min_units_per_wave(int K, int S, int U, int NW) {
   return fewest / NW;
 }
 
-// Quantized tokens go through LDS (QuantTokensT<true>: staged scales, codes
-// read in whole rows) from 17 tokens on (two or more token tiles) where every
-// wave has at least two units, so that the scale staging and its barrier are
-// spread over a pipeline of loads; only for one-block units and at most 16
-// fragments of loads in flight per wave (RT * CT * D), where the kernel keeps
-// its registers (the four-block 2:4 units and the three-deep 64-row bands
-// spill).  Measured on MI355X against tokens read from global memory,
-// Llama-3-8B weights from HBM (A/B in one process, results bit-identical):
+// Quantized tokens (QuantTokensT) take mode 2 (codes in whole rows through
+// LDS, scales staged in LDS behind a barrier) from 17 tokens on (two or more
+// token tiles) where every wave has at least two units, so that the staging
+// and its barrier are spread over a pipeline of loads, and only for one-block
+// units and at most 16 fragments of loads in flight per wave (RT * CT * D),
+// where the kernel keeps its registers (the four-block 2:4 units and the
+// three-deep 64-row bands spill); otherwise mode 1 (codes only, no barrier)
+// from kCodeLdsMinTokens tokens on, and mode 0 below that.  Measured on MI355X
+// against mode 0, Llama-3-8B weights from HBM (A/B in one process, results
+// bit-identical), mode 2:
 //   6144 x 4096   20 / 32 / 64 tokens 10.5 / 12.0 / 17.9 -> 9.1 / 10.1 / 12.9 us
 //   4096 x 4096   32 / 64 tokens       9.9 / 13.0 -> 8.1 / 11.3 us
 //   4096 x 14336  20 / 32 tokens       17.4 / 18.7 -> 16.9 / 17.8 us
 //   2:4 at 64 tokens: 6144 x 4096 17.9 -> 12.6 us, 4096 x 4096 13.2 -> 10.9 us;
 //   2:4 4096 x 14336 at 32 tokens 18.1 -> 16.4 us.
-// The scale staging alone gave about half of that.  At up to 16 tokens it
-// was level to 6 % slower, and so it was with a single unit per wave (the
-// 2:4 four-block units on K = 4096: 3 to 7 % slower).
+// The scale staging alone gave about half of that; up to 16 tokens it was
+// level to 6 % slower, and so it was with a single unit per wave (the 2:4
+// four-block units on K = 4096: 3 to 7 % slower).  Mode 1 against mode 0:
+//   2:4 6144 x 4096 at 8 / 12 / 16 tokens 6.5 / 6.7 / 7.1 -> 6.0 / 6.3 / 6.5 us
+//   2:4 4096 x 4096 at 16 / 24 / 32 tokens 5.7 / 6.7 / 7.5 -> 5.1 / 5.6 / 5.8 us
+//   2:4 4096 x 14336 at 8 tokens 11.4 -> 10.3 us; dense level to 4 % faster;
+// at 4 and 5 tokens level to 4 % slower.
 constexpr int kScaleLdsMinTokens = 17, kScaleLdsMinUnitsPerWave = 2, kScaleLdsMaxFragsInFlight = 16;
+constexpr int kCodeLdsMinTokens = 8;
 
 template <class W, class X, int RT, int CT, int NW, int D, int S>
 hipError_t launch_decode_kernel(W wop, X xop, const typename X::Scale *ws, int M, int N, int K, uint16_t *y,
                                 float *part, hipStream_t stream) {
   constexpr int U = weight_unit<W>::value;
   if constexpr (X::kScaleLds) {
-    using G = decltype(xop.global_scales());
-    if constexpr (U > 1 || CT < 2 || RT * CT * D > kScaleLdsMaxFragsInFlight) {
-      return launch_decode_kernel<W, G, RT, CT, NW, D, S>(wop, xop.global_scales(), ws, M, N, K, y, part, stream);
-    } else {
-      if (M < kScaleLdsMinTokens || min_units_per_wave(K, S, U, NW) < kScaleLdsMinUnitsPerWave)
-        return launch_decode_kernel<W, G, RT, CT, NW, D, S>(wop, xop.global_scales(), ws, M, N, K, y, part, stream);
-      return launch_decode_kernel_as<W, X, RT, CT, NW, D, S>(wop, xop, ws, M, N, K, y, part, stream);
+    constexpr bool kMode2Fits = U == 1 && CT >= 2 && RT * CT * D <= kScaleLdsMaxFragsInFlight;
+    if constexpr (kMode2Fits) {
+      if (M >= kScaleLdsMinTokens && min_units_per_wave(K, S, U, NW) >= kScaleLdsMinUnitsPerWave)
+        return launch_decode_kernel_as<W, X, RT, CT, NW, D, S>(wop, xop, ws, M, N, K, y, part, stream);
     }
+    // mode 1 where its registers fit (the four-block 2:4 units with more than
+    // two fragments per slot spill)
+    constexpr bool kMode1Fits = U == 1 ? RT * CT * D <= kScaleLdsMaxFragsInFlight : RT * CT <= 2;
+    if constexpr (kMode1Fits) {
+      if (M >= kCodeLdsMinTokens)
+        return launch_decode_kernel_as<W, QuantTokensT<1>, RT, CT, NW, D, S>(wop, xop.template as_mode<1>(), ws, M, N,
+                                                                             K, y, part, stream);
+    }
+    return launch_decode_kernel_as<W, QuantTokensT<0>, RT, CT, NW, D, S>(wop, xop.template as_mode<0>(), ws, M, N, K,
+                                                                         y, part, stream);
   } else {
     return launch_decode_kernel_as<W, X, RT, CT, NW, D, S>(wop, xop, ws, M, N, K, y, part, stream);
   }

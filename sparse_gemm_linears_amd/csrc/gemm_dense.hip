@@ -623,7 +623,7 @@ static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scal
   // staged tokens and the reduction buffer share LDS across a barrier).
   hipError_t e = hipSuccess;
   bool rows = false;
-  if constexpr (std::is_same<X, QuantTokens>::value) {
+  if constexpr (std::is_same<X, QuantTokens>::value && CT <= 2) {
     rows = N < 16384 && M <= 32 && !(M == 1 && K >= 8192);
     if (rows)
       e = launch_decode_kernel<DenseWeightRows, X, RT, CT, NW, D, S>(DenseWeightRows{{wq, K}}, xop, ws, M, N, K, y,

@@ -1,12 +1,17 @@
 """Decode GEMMs on quantized tokens that go through LDS.
 
-From 17 tokens on, where every wave of every K split has at least two units
-(one-block units, at most 16 fragments in flight per wave), the decode kernel
-copies the scales of its K range into LDS once per workgroup (linear loads,
-odd row stride), and each wave loads its token code tiles in whole 128-byte
-rows, writes them to its own LDS tile and reads the MFMA fragments back;
-otherwise both come from global memory as fragments (gemm_decode.hpp,
-QuantTokensT and launch_decode_kernel).  Covered here:
+The decode kernel reads quantized tokens in one of three modes
+(gemm_decode.hpp, QuantTokensT and launch_decode_kernel):
+  * mode 2, from 17 tokens on where every wave of every K split has at least
+    two one-block units and at most 16 fragments are in flight per wave: the
+    scales of the K range are copied into LDS once per workgroup (linear
+    loads, odd row stride), and each wave loads its token code tiles in whole
+    128-byte rows, writes them to its own LDS tile and reads the MFMA
+    fragments back;
+  * mode 1, from 8 tokens on where mode 2 does not apply and the registers
+    fit: the code tiles as in mode 2, the scales from global memory;
+  * mode 0 otherwise: codes and scales as fragments from global memory.
+Covered here:
 
   * against the oracle: the 6144- and 4096-row Llama weights at 17 to 64
     tokens (ragged token tiles, one and two K splits), the long-K down weight
@@ -27,10 +32,14 @@ from test_parity_gpu import assert_gemm_close, dev, llama_sparse_weight, llama_w
 
 pytestmark = pytest.mark.gpu
 
-# (M, N, K): every case takes the LDS path except where noted
-CASES = [(17, 6144, 4096), (23, 6144, 4096), (33, 6144, 4096), (64, 6144, 4096), (40, 6144, 4224),
-         (17, 4096, 4096), (48, 4096, 4096), (64, 4096, 4096), (20, 4096, 14336), (32, 4096, 14336),
-         (16, 6144, 4096)]  # the last: 16 tokens, scales from global memory
+# (M, N, K), with the mode each GEMM takes (dense / 2:4)
+CASES = [(17, 6144, 4096), (23, 6144, 4096),   # 2 / 0 (2:4 four-block units, one per wave)
+         (33, 6144, 4096), (64, 6144, 4096), (40, 6144, 4224), (48, 4096, 4096), (64, 4096, 4096),  # 2 / 2
+         (17, 4096, 4096), (24, 4096, 4096),   # 2 / 1
+         (20, 4096, 14336), (32, 4096, 14336),  # 2 / 2 (K split four ways)
+         (8, 6144, 4096), (12, 4096, 4096), (16, 6144, 4096),  # 1 / 1
+         (9, 4096, 14336),  # 1 / 0 (split K, 2:4 four-block units)
+         (5, 6144, 4096)]  # 0 / 0
 
 
 def operands(M, N, K, kind, seed_shift=0):
@@ -60,7 +69,7 @@ def test_staged_scales_match_oracle(gpu_lib, M, N, K, kind):
 def test_staged_scales_bit_identical_to_global_scales(gpu_lib, N):
     """At 16 and 17 tokens on these weights the decode kernel has the same row
     bands, waves and load depth, so each output row is summed in the same
-    order; only where the scales come from differs."""
+    order; only how the tokens are read differs (modes 1 and 2)."""
     K = 4096
     ops17, _ = operands(17, N, K, "dense")
     xq17, xs17, wq, ws = ops17

@@ -353,7 +353,7 @@ def swz(r: int) -> int:
 @pytest.mark.parametrize("M,c", [(64, 0), (64, 3), (17, 1), (23, 1), (40, 2)])
 def test_linear_code_tile_round_trip(M, c):
     """load_row_runs / row_runs_to_frag (the token code tiles of
-    QuantTokensT<true> and the weight tiles of DenseWeightRows, whose rows are
+    QuantTokensT (modes 1 and 2) and the weight tiles of DenseWeightRows, whose rows are
     never clamped): each lane loads 16 bytes of a
     whole-row run (8 rows of 128 bytes per load, rows past M clamped to M - 1),
     writes them to the wave's LDS tile at 16 * lane (and 1024 + 16 * lane), and
