@@ -302,9 +302,9 @@ template <class W>
 struct weight_unit<W, std::void_t<decltype(W::kUnit)>> {
   static constexpr int value = W::kUnit;
 };
-// A weight policy with kRows loads its tiles in whole rows (Frag = RowRuns)
-// and turns them into MFMA fragments through a wave-private LDS tile
-// (to_frag) just before use.
+// A weight policy with kRows loads its tiles in whole rows (its Frag) and
+// turns them into MFMA operands (its MFrag) through a wave-private LDS tile of
+// kTileBytes (to_frag) just before use.
 template <class W, class = void>
 struct weight_rows {
   static constexpr bool value = false;
@@ -322,9 +322,17 @@ struct weight_rows<W, std::void_t<decltype(W::kRows)>> {
 // main loop (every wave is then past its last use of the rest).  The host and
 // the kernel both lay it out with plan().
 constexpr size_t kDecodeMaxLds = 160 * 1024;
+template <class W, class = void>
+struct weight_tile_bytes {
+  static constexpr size_t value = 0;
+};
+template <class W>
+struct weight_tile_bytes<W, std::void_t<decltype(W::kTileBytes)>> {
+  static constexpr size_t value = W::kTileBytes;
+};
 template <class W, class X, int RT, int CT, int NW>
 struct DecodeLds {
-  static constexpr size_t kWeightTiles = weight_rows<W>::value ? (size_t)NW * RT * 2048 : 0;
+  static constexpr size_t kWeightTiles = weight_rows<W>::value ? (size_t)NW * RT * weight_tile_bytes<W>::value : 0;
   static constexpr size_t kRed = NW > 1 ? (size_t)(NW - 1) * RT * CT * 64 * sizeof(v4f) : 0;
   struct Plan {
     size_t tokens, red_off, bytes;
@@ -354,7 +362,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
   uint8_t *const token_lds = decode_lds + Lds::kWeightTiles;  // what the token policy stages
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint8_t *const wtile = decode_lds + (size_t)wave * RT * 2048;  // kRows weights: this wave's tiles
+  // kRows weights: this wave's tiles
+  uint8_t *const wtile = decode_lds + (size_t)wave * RT * weight_tile_bytes<W>::value;
   const int g = lane >> 4, lr = lane & 15;
   constexpr int U = weight_unit<W>::value;
   const int KB = K / kGroup, KU = KB / U;  // K blocks, units of U blocks
@@ -483,9 +492,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
   };
   auto consume = [&](int d) {
     if constexpr (weight_rows<W>::value) {
-      v8i af[RT];
+      typename W::MFrag af[RT];
 #pragma unroll
-      for (int r = 0; r < RT; r++) af[r] = wop.to_frag(a[d][r], wtile + r * 2048);
+      for (int r = 0; r < RT; r++) af[r] = wop.to_frag(a[d][r], wtile + r * weight_tile_bytes<W>::value);
       consume_with(d, af);
     } else {
       consume_with(d, a[d]);

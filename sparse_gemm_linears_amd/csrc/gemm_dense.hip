@@ -448,7 +448,9 @@ struct DenseWeight {
 // 16).
 struct DenseWeightRows : DenseWeight {
   static constexpr bool kRows = true;
+  static constexpr size_t kTileBytes = 2048;
   typedef RowRuns Frag;
+  typedef v8i MFrag;
   // `row` is this lane's row of a 16-row tile starting at a multiple of 16
   __device__ __forceinline__ Frag load(int64_t row, int kb, int) const {
     const int64_t row0 = row & ~int64_t(15);

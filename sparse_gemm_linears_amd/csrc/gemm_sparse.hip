@@ -489,6 +489,11 @@ struct SparseWeight4 {
     Frag f;
 #pragma unroll
     for (int j = 0; j < 4; j++) f.v[j] = make_v4i(ldg16(wv + row * (K / 2) + (int64_t)(kb + j) * 64 + 16 * g));
+    load_idx(row, kb, g, f.idx);
+    return f;
+  }
+  // the index words of the four blocks, word g of each in idx[0..3]
+  __device__ __forceinline__ void load_idx(int64_t row, int kb, int g, int (&idx)[4]) const {
     const uint4 m = ldg16(wm + row * (K / 8) + (int64_t)kb * 16 + 16 * g);
     // Lane group g (the 16-lane row g of the wave) holds the four words of
     // block kb + g and needs word g of every block: a 4x4 transpose across the
@@ -501,14 +506,63 @@ struct SparseWeight4 {
     const auto b = __builtin_amdgcn_permlane32_swap(m.y, m.w, false, false);
     const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
     const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-    f.idx[0] = (int)c[0];
-    f.idx[1] = (int)c[1];
-    f.idx[2] = (int)d[0];
-    f.idx[3] = (int)d[1];
-    return f;
+    idx[0] = (int)c[0];
+    idx[1] = (int)c[1];
+    idx[2] = (int)d[0];
+    idx[3] = (int)d[1];
   }
   __device__ __forceinline__ v4f mma(const Frag &a, const v8i &b, int u) const {
     return smfmac_16x16x128_fp8(a.v[u], b, a.idx[u]);
+  }
+};
+
+// The four-block operand with its values in whole rows, for decode_kernel: a
+// 16-row tile's four blocks are 256 contiguous bytes per row, loaded as four
+// runs of 4 rows (lane l: row 4i + l / 16, 16-byte chunk l % 16 of the row's
+// 256 bytes) instead of four fragment loads of 16 rows x 64 bytes each (half
+// as many cache-line accesses), then written to the wave's 4 KB LDS tile as
+// four blocks of 16 rows x 64 bytes, chunk c of row r at position
+// c ^ vswz(r) as in the tile kernel, and read back per block as the
+// fragment.  The index words come as in SparseWeight4.  Used where the
+// workgroup's outputs per lane group are one tile, or two row tiles (more
+// spill registers).  Measured on MI355X against SparseWeight4 (A/B, weights
+// from HBM): 4096 x 14336 at 1 / 4 / 8 tokens 9.8 / 10.5 / 10.2 -> 9.5 / 9.8 /
+// 9.6 us, 4096 x 4096 at 1 / 5 / 8 tokens 6.5 / 6.3 / 6.2 -> 6.0 / 5.9 / 5.8
+// us, 6144 x 4096 at 16 tokens 6.8 -> 6.4 us.
+struct SparseFrag4Rows {
+  uint4 v[4];
+  int idx[4];
+};
+struct SparseWeight4Rows : SparseWeight4 {
+  static constexpr bool kRows = true;
+  static constexpr size_t kTileBytes = 4096;
+  typedef SparseFrag4Rows Frag;
+  typedef SparseFrag4 MFrag;
+  // `row` is this lane's row of a 16-row tile starting at a multiple of 16
+  __device__ __forceinline__ Frag load(int64_t row, int kb, int g) const {
+    const int lane = threadIdx.x & 63;
+    const uint8_t *base = wv + (row & ~int64_t(15)) * (K / 2) + (int64_t)kb * 64 + 16 * (lane & 15);
+    Frag f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) f.v[i] = ldg16(base + (int64_t)(4 * i + (lane >> 4)) * (K / 2));
+    load_idx(row, kb, g, f.idx);
+    return f;
+  }
+  __device__ __forceinline__ MFrag to_frag(const Frag &f, uint8_t *tile) const {
+    const int lane = threadIdx.x & 63, g = lane >> 4, lr = lane & 15;
+    const int u = (lane >> 2) & 3, c = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 4 * i + (lane >> 4);
+      *reinterpret_cast<uint4 *>(tile + u * 1024 + r * 64 + 16 * (c ^ vswz(r))) = f.v[i];
+    }
+    MFrag m;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      m.v[b] = make_v4i(*reinterpret_cast<const uint4 *>(tile + b * 1024 + lr * 64 + 16 * (g ^ vswz(lr))));
+      m.idx[b] = f.idx[b];
+    }
+    return m;
   }
 };
 
@@ -563,9 +617,14 @@ static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, con
                                 int N, int K, uint16_t *y, float *part, hipStream_t stream) {
   constexpr int U = SparseWeight4::kUnit;
   if constexpr (RT * CT <= 4)
-    if ((K / kGroup) % U == 0 && (K / kGroup) / U >= NW)
-      return launch_decode_with<SparseWeight4, X, RT, CT, NW, 1, S>(SparseWeight4{wv, wm, K}, xop, ws, M, N, K, y,
-                                                                    part, stream);
+    if ((K / kGroup) % U == 0 && (K / kGroup) / U >= NW) {
+      if constexpr (RT * CT == 1 || (RT == 2 && CT == 1))
+        return launch_decode_with<SparseWeight4Rows, X, RT, CT, NW, 1, S>(SparseWeight4Rows{{wv, wm, K}}, xop, ws, M,
+                                                                          N, K, y, part, stream);
+      else
+        return launch_decode_with<SparseWeight4, X, RT, CT, NW, 1, S>(SparseWeight4{wv, wm, K}, xop, ws, M, N, K, y,
+                                                                      part, stream);
+    }
   return launch_decode_with<SparseWeight, X, RT, CT, NW, D, S>(SparseWeight{wv, wm, K}, xop, ws, M, N, K, y, part,
                                                                stream);
 }

@@ -378,3 +378,33 @@ def test_linear_code_tile_round_trip(M, c):
         hi = tile[lr * 128 + (((g + 4) ^ swz(lr)) << 4):][:16]
         assert lo == x[m][kb * 128 + 16 * g:][:16]
         assert hi == x[m][kb * 128 + 64 + 16 * g:][:16]
+
+
+def vswz(r: int) -> int:
+    """The 2:4 tile kernel's chunk swizzle of a 64-byte value row (gemm_sparse.hip)."""
+    return (((r >> 2) & 1) * 3) ^ (((r >> 3) & 1) << 1)
+
+
+def test_sparse_value_tile_round_trip():
+    """SparseWeight4Rows: four runs of 4 rows x 256 bytes (lane l: row 4i + l / 16,
+    16-byte chunk l % 16, i.e. block (l / 4) % 4, chunk l % 4), written to four
+    16 x 64-byte blocks with chunk c of row r at position c ^ vswz(r), read back
+    as lane (g, lr)'s fragment of block b: bytes 16g .. 16g + 15 of row lr's block
+    b values, as SparseWeight4 loads them."""
+    vals = [[(r * 37 + b * 11) % 253 for b in range(256)] for r in range(16)]  # one unit: 4 blocks x 64 B
+    tile = [None] * 4096
+    for i in range(4):
+        for lane in range(64):
+            r = 4 * i + (lane >> 4)
+            u, c = (lane >> 2) & 3, lane & 3
+            data = vals[r][16 * (lane & 15):][:16]
+            off = u * 1024 + r * 64 + 16 * (c ^ vswz(r))
+            for j in range(16):
+                assert tile[off + j] is None, "a byte written twice"
+                tile[off + j] = data[j]
+    assert None not in tile
+    for lane in range(64):
+        g, lr = lane >> 4, lane & 15
+        for b in range(4):
+            off = b * 1024 + lr * 64 + 16 * (g ^ vswz(lr))
+            assert tile[off:off + 16] == vals[lr][64 * b + 16 * g:][:16]
