@@ -41,8 +41,8 @@ CALIB_BYTES = 256 << 20    # size of the traffic-calibration copy
 # fp8_block_gemm_gate_up_m4096_traffic.md has the commands and the readings),
 # each scaled by the same counter's reading for the calibration copy.  It is
 # reported only while the kernel's sources hash to the value it was taken on.
-TRAFFIC = {"bytes_per_launch": 941634609,
-           "sources_sha256": "c681f80d04dac26451a1f39d4997abc7523b8ed9f8550c81ce73ee97b963e146"}
+TRAFFIC = {"bytes_per_launch": 941647979,
+           "sources_sha256": "261076b506f746e99290d95fb956e5166a281e19746396d2f5bf4fbc7f1bf0f5"}
 TRAFFIC_SOURCES = ("sparse_gemm_linears_amd/csrc/gemm_dense.hip", "sparse_gemm_linears_amd/csrc/gemm_common.hpp",
                    "sparse_gemm_linears_amd/csrc/device_common.hpp")
 
@@ -94,6 +94,11 @@ PROFILE_CASES = {
     "decode_sparse_gate_up_m8": ("sparse", "gate_up", 8, 20),
     "decode_sparse_gate_up_m16": ("sparse", "gate_up", 16, 20),
     "decode_sparse_down_m16": ("sparse", "down", 16, 20),
+    "decode_dense_qkv_m1": ("dense", "qkv", 1, 20),
+    "decode_dense_qkv_m16": ("dense", "qkv", 16, 20),
+    "decode_dense_qkv_m64": ("dense", "qkv", 64, 20),
+    "decode_sparse_qkv_m16": ("sparse", "qkv", 16, 20),
+    "decode_sparse_qkv_m64": ("sparse", "qkv", 64, 20),
 }
 
 
