@@ -8,8 +8,6 @@
 //      pairwise comparisons of the group;
 //   3. the block maximum of the kept magnitudes gives s = amax / 448;
 //   4. the kept codes and the nibble i0 | i1 << 2 of each group are packed.
-#include <type_traits>
-
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -26,42 +24,40 @@ struct Kept2 {
 // for activation-aware).  gij (i < j) says position i ranks before position j
 // (ties go to the lower index); a position is kept when fewer than two of the
 // other three rank before it, i.e. when it ranks before at least two of them.
-// The values come in as four scalars and are picked with selects: from an
-// array, the compiler turns the pick into an indexed load from scratch memory.
-// Two forms of the same rule, each the faster one for its score type (A/B on
-// MI355X, identical outputs):
-//  * fp64 scores: keep flags as majorities of three comparisons in bool logic,
-//    which the compiler keeps as lane masks combined by scalar instructions
-//    (6-9 % faster on the large shapes than the integer form);
-//  * integer scores: comparisons as 0/1 integers and rank counts, all vector
-//    arithmetic (6-10 % faster than the mask form there).
-__device__ __forceinline__ bool majority3(bool a, bool b, bool c) { return (a && b) || (c && (a || b)); }
+// Each comparison becomes a lane mask of the wave (one vector compare), the
+// majorities are scalar bit operations on the masks, and the four keep flags
+// go back to the lanes as select masks.  The values come in as four scalars
+// and are picked with selects: from an array, the compiler turns the pick into
+// an indexed load from scratch memory.  Against the same rule in plain bool
+// logic, where the compiler repeated every comparison in negated form and
+// spilled the masks (A/B on MI355X, weights from HBM, identical outputs):
+// 6144 x 4096 19.0 -> 16.8 us, 4096 x 4096 14.4 -> 12.6 us, 28672 x 4096
+// 63.6 -> 62.4 us, 4096 x 14336 34.4 -> 33.5 us (activation-aware).
+typedef unsigned long long LaneMask;
+__device__ __forceinline__ LaneMask lanes_where(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ bool lane_in(LaneMask m) { return __builtin_amdgcn_inverse_ballot_w64(m); }
+__device__ __forceinline__ LaneMask majority3(LaneMask a, LaneMask b, LaneMask c) { return (a & b) | (c & (a | b)); }
 
-template <typename SC>
+template <bool kNib, typename SC>
 __device__ __forceinline__ Kept2 select_two(float v0, float v1, float v2, float v3, SC s0, SC s1, SC s2, SC s3) {
-  bool k0, k1, k2, k3;
-  if constexpr (std::is_same_v<SC, double>) {
-    const bool g01 = s0 >= s1, g02 = s0 >= s2, g03 = s0 >= s3;
-    const bool g12 = s1 >= s2, g13 = s1 >= s3, g23 = s2 >= s3;
-    k0 = majority3(g01, g02, g03);
-    k1 = majority3(!g01, g12, g13);
-    k2 = majority3(!g02, !g12, g23);
-    k3 = majority3(!g03, !g13, !g23);
-  } else {
-    const uint32_t g01 = s0 >= s1, g02 = s0 >= s2, g03 = s0 >= s3;
-    const uint32_t g12 = s1 >= s2, g13 = s1 >= s3, g23 = s2 >= s3;
-    // number of positions ranking before each position
-    k0 = 3u - (g01 + g02 + g03) < 2u;
-    k1 = g01 + 2u - (g12 + g13) < 2u;
-    k2 = g02 + g12 + 1u - g23 < 2u;
-    k3 = g03 + g13 + g23 < 2u;
-  }
+  const LaneMask g01 = lanes_where(s0 >= s1), g02 = lanes_where(s0 >= s2), g03 = lanes_where(s0 >= s3);
+  const LaneMask g12 = lanes_where(s1 >= s2), g13 = lanes_where(s1 >= s3), g23 = lanes_where(s2 >= s3);
+  const bool k0 = lane_in(majority3(g01, g02, g03));
+  const bool k1 = lane_in(majority3(~g01, g12, g13));
+  const bool k2 = lane_in(majority3(~g02, ~g12, g23));
+  const bool k3 = lane_in(majority3(~g03, ~g13, ~g23));
   Kept2 r;
   r.first = k0 ? v0 : (k1 ? v1 : v2);
   r.second = k3 ? v3 : (k2 ? v2 : v1);
-  const uint32_t i0 = k0 ? 0u : (k1 ? 1u : 2u);
-  const uint32_t i1 = k3 ? 3u : (k2 ? 2u : 1u);
-  r.nib = i0 | (i1 << 2);
+  // made here, in registers: otherwise the compiler sinks the selects to their
+  // uses after the block reduction and keeps (spills) every mask until then
+  asm volatile("" : "+v"(r.first), "+v"(r.second));
+  r.nib = 0;
+  if constexpr (kNib) {
+    const uint32_t i0 = k0 ? 0u : (k1 ? 1u : 2u);
+    const uint32_t i1 = k3 ? 3u : (k2 ? 2u : 1u);
+    r.nib = i0 | (i1 << 2);
+  }
   return r;
 }
 
@@ -105,6 +101,7 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
   for (int i = 0; i < 8; i++) raw[i] = *reinterpret_cast<const uint4*>(wp + (int64_t)i * 16 * K);
 
   Kept2 kept[8][2];
+  uint32_t mbs[8];
   uint32_t amax_bits = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -116,14 +113,19 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
       const float v2 = bf16_to_f32(hi & 0xFFFFu), v3 = __uint_as_float(hi & 0xFFFF0000u);
       if constexpr (AWARE) {
         // |w| * c is exact in fp64 (8 + 24 significant bits)
-        kept[i][h] = select_two(v0, v1, v2, v3, fabs((double)v0) * c[4 * h], fabs((double)v1) * c[4 * h + 1],
-                                fabs((double)v2) * c[4 * h + 2], fabs((double)v3) * c[4 * h + 3]);
+        kept[i][h] = select_two<MODE != 1>(v0, v1, v2, v3, fabs((double)v0) * c[4 * h],
+                                           fabs((double)v1) * c[4 * h + 1], fabs((double)v2) * c[4 * h + 2],
+                                           fabs((double)v3) * c[4 * h + 3]);
       } else {
-        kept[i][h] = select_two(v0, v1, v2, v3, lo & 0x7FFFu, (lo >> 16) & 0x7FFFu, hi & 0x7FFFu, (hi >> 16) & 0x7FFFu);
+        kept[i][h] = select_two<MODE != 1>(v0, v1, v2, v3, lo & 0x7FFFu, (lo >> 16) & 0x7FFFu, hi & 0x7FFFu,
+                                           (hi >> 16) & 0x7FFFu);
       }
       amax_bits = max(amax_bits, max(__float_as_uint(kept[i][h].first) & 0x7FFFFFFFu,
                                      __float_as_uint(kept[i][h].second) & 0x7FFFFFFFu));
     }
+    // the row's two meta nibbles, made now for the same reason
+    mbs[i] = kept[i][0].nib | (kept[i][1].nib << 4);
+    if constexpr (MODE != 1) asm volatile("" : "+v"(mbs[i]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off, 64));
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
     // the 16 lanes of a row segment hold its 16 consecutive meta bytes: the
     // first lane of each quad gathers the bytes of lanes 1, 2, 3 of its quad
     // (DPP quad broadcasts) for one 4-byte store
-    const uint32_t mb = kept[i][0].nib | (kept[i][1].nib << 4);
+    const uint32_t mb = mbs[i];
     const uint32_t m4 = mb | ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x55, 0xF, 0xF, false) << 8) |
                         ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xAA, 0xF, 0xF, false) << 16) |
                         ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xFF, 0xF, 0xF, false) << 24);
