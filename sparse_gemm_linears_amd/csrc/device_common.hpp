@@ -14,7 +14,22 @@ constexpr int kGroup = 128;  // activation group / weight block edge
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// A 16-byte load of data that is read once, with the non-temporal hint.  A
+// streaming read over rotated copies of >= 1 GiB (timing probe on MI355X, 512
+// workgroups, each load instruction covering whole 128-byte lines) took
+// 18.1 us for 117 MB with it and 20.4 us without (6.5 against 5.7 TB/s);
+// 59 MB: 10.4 against 11.4 us.  Used where a wave's load covers whole lines
+// and A/B timing agreed: the decode weights read in whole rows, the weight
+// quantizers' and the 2:4 pruner's inputs.  Loads that take a line in two
+// halves (MFMA fragments of 64-byte runs) and the activation quantizer were
+// slower with it.
+__device__ __forceinline__ uint4 ldg16_stream(const void *p) {
+  const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 

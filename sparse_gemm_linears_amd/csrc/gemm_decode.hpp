@@ -45,13 +45,16 @@ struct RowRuns {
   uint4 lo, hi;
 };
 // rows row0 .. row0 + 15 (each clamped to last_row) of a matrix with `stride`
-// bytes per row, from byte `col` of each row
+// bytes per row, from byte `col` of each row; kStream: read-once data
+template <bool kStream = false>
 __device__ __forceinline__ RowRuns load_row_runs(const uint8_t *base, int64_t row0, int64_t last_row, int64_t stride,
                                                  int64_t col) {
   const int lane = threadIdx.x & 63, q = lane >> 3, p = lane & 7;
+  const uint8_t *lo = base + min(row0 + q, last_row) * stride + col + 16 * (p ^ swz(q));
+  const uint8_t *hi = base + min(row0 + 8 + q, last_row) * stride + col + 16 * (p ^ swz(q + 8));
   RowRuns x;
-  x.lo = ldg16(base + min(row0 + q, last_row) * stride + col + 16 * (p ^ swz(q)));
-  x.hi = ldg16(base + min(row0 + 8 + q, last_row) * stride + col + 16 * (p ^ swz(q + 8)));
+  x.lo = kStream ? ldg16_stream(lo) : ldg16(lo);
+  x.hi = kStream ? ldg16_stream(hi) : ldg16(hi);
   return x;
 }
 __device__ __forceinline__ v8i row_runs_to_frag(const RowRuns &x, uint8_t *tile) {

@@ -445,7 +445,11 @@ struct DenseWeight {
 // 6144 x 4096 at 1 / 4 / 16 / 32 tokens 7.3 / 7.9 / 9.2 / 10.3 -> 6.8 / 6.8 /
 // 8.0 / 9.5 us, 4096 x 4096 5.4 / 6.1 / 7.4 / 8.3 -> 5.3 / 5.4 / 6.7 / 8.0 us,
 // 4096 x 14336 at 4 / 8 tokens 13.1 / 15.2 -> 12.5 / 13.2 us (level at 1 and
-// 16).
+// 16).  Whole rows let the loads carry the non-temporal hint (each load
+// instruction covers whole lines): against the same tiles with plain loads,
+// 6144 x 4096 6.7 / 6.8 / 7.8 -> 6.4 / 6.3 / 7.2 us at 1 / 2 / 16 tokens,
+// 4096 x 14336 12.4 / 13.3 -> 11.6 / 12.4 us at 2 / 8 tokens.  Fragment loads
+// (half lines per instruction) were up to 13 % slower with the hint.
 struct DenseWeightRows : DenseWeight {
   static constexpr bool kRows = true;
   static constexpr size_t kTileBytes = 2048;
@@ -454,7 +458,7 @@ struct DenseWeightRows : DenseWeight {
   // `row` is this lane's row of a 16-row tile starting at a multiple of 16
   __device__ __forceinline__ Frag load(int64_t row, int kb, int) const {
     const int64_t row0 = row & ~int64_t(15);
-    return load_row_runs(wq, row0, row0 + 15, K, (int64_t)kb * kGroup);
+    return load_row_runs<true>(wq, row0, row0 + 15, K, (int64_t)kb * kGroup);
   }
   __device__ __forceinline__ v8i to_frag(const Frag &x, uint8_t *tile) const { return row_runs_to_frag(x, tile); }
 };
@@ -617,16 +621,18 @@ static hipError_t launch_decode(X xop, const uint8_t *wq, const typename X::Scal
                                 uint16_t *y, float *part, hipStream_t stream) {
   if (S > 1 && !part) return hipErrorInvalidValue;
   // whole-row weight tiles for up to 32 quantized tokens on weights of fewer
-  // than 16384 rows (see DenseWeightRows), except one token on long K.
-  // Slower with them or level (A/B on MI355X): the 28672-row gate/up weight
-  // at one or two tokens (5-16 % slower), the 4096 x 14336 weight at one
-  // token (4 %), the tokens quantized in the kernel (one or two: 2-8 % on the
-  // smaller weights), and 33-64 tokens (-3 to +4 %: there the tiles, the
-  // staged tokens and the reduction buffer share LDS across a barrier).
+  // than 16384 rows (see DenseWeightRows).  Slower with them or level (A/B on
+  // MI355X): the 28672-row gate/up weight at one or two tokens (5-16 %
+  // slower, and still 12 % / 4 % with the non-temporal loads), the tokens
+  // quantized in the kernel (one or two: 2-8 % on the smaller weights), and
+  // 33-64 tokens (-3 to +4 %: there the tiles, the staged tokens and the
+  // reduction buffer share LDS across a barrier).  The 4096 x 14336 weight at
+  // one token had been 4 % slower with them; with the non-temporal loads it
+  // is 5 % faster (11.7 -> 11.1 us).
   hipError_t e = hipSuccess;
   bool rows = false;
   if constexpr (std::is_same<X, QuantTokens>::value && CT <= 2) {
-    rows = N < 16384 && M <= 32 && !(M == 1 && K >= 8192);
+    rows = N < 16384 && M <= 32;
     if (rows)
       e = launch_decode_kernel<DenseWeightRows, X, RT, CT, NW, D, S>(DenseWeightRows{{wq, K}}, xop, ws, M, N, K, y,
                                                                      part, stream);

@@ -528,7 +528,10 @@ struct SparseWeight4 {
 // spill registers).  Measured on MI355X against SparseWeight4 (A/B, weights
 // from HBM): 4096 x 14336 at 1 / 4 / 8 tokens 9.8 / 10.5 / 10.2 -> 9.5 / 9.8 /
 // 9.6 us, 4096 x 4096 at 1 / 5 / 8 tokens 6.5 / 6.3 / 6.2 -> 6.0 / 5.9 / 5.8
-// us, 6144 x 4096 at 16 tokens 6.8 -> 6.4 us.
+// us, 6144 x 4096 at 16 tokens 6.8 -> 6.4 us.  The value loads take the
+// non-temporal hint (whole lines per load instruction): 6144 x 4096 at 8 / 16
+// tokens 6.1 / 6.3 -> 5.75 / 5.8 us, 4096 x 14336 at 1 / 4 / 8 tokens 9.5 /
+// 9.9 / 9.7 -> 9.3 / 9.4 / 9.2 us.
 struct SparseFrag4Rows {
   uint4 v[4];
   int idx[4];
@@ -544,7 +547,7 @@ struct SparseWeight4Rows : SparseWeight4 {
     const uint8_t *base = wv + (row & ~int64_t(15)) * (K / 2) + (int64_t)kb * 64 + 16 * (lane & 15);
     Frag f;
 #pragma unroll
-    for (int i = 0; i < 4; i++) f.v[i] = ldg16(base + (int64_t)(4 * i + (lane >> 4)) * (K / 2));
+    for (int i = 0; i < 4; i++) f.v[i] = ldg16_stream(base + (int64_t)(4 * i + (lane >> 4)) * (K / 2));
     load_idx(row, kb, g, f.idx);
     return f;
   }

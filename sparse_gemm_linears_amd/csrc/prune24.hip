@@ -98,7 +98,12 @@ __global__ __launch_bounds__(256) void prune24_kernel(const uint16_t* __restrict
   const uint16_t* wp = w + row0 * K + kcol;
   uint4 raw[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) raw[i] = *reinterpret_cast<const uint4*>(wp + (int64_t)i * 16 * K);
+  for (int i = 0; i < 8; i++) {
+    // read once, except by the per-tensor form's first pass (its second pass
+    // reads the weight again)
+    const uint16_t* rp = wp + (int64_t)i * 16 * K;
+    raw[i] = MODE == 1 ? *reinterpret_cast<const uint4*>(rp) : ldg16_stream(rp);
+  }
 
   Kept2 kept[8][2];
   uint32_t mbs[8];

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void quant_wblock_kernel(const uint16_t* __res
   const int64_t base = ((int64_t)nb * kGroup + (t >> 4)) * K + (int64_t)kb * kGroup + col;
   uint4 raw[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) raw[i] = *reinterpret_cast<const uint4*>(w + base + (int64_t)i * 16 * K);
+  for (int i = 0; i < 8; i++) raw[i] = ldg16_stream(w + base + (int64_t)i * 16 * K);
   uint32_t amax_bits = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void quant_wblock_ue8m0_kernel(const uint16_t*
   const int64_t base = ((int64_t)nb * kGroup + (t >> 4)) * K + (int64_t)kb * kGroup + col;
   uint4 raw[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) raw[i] = *reinterpret_cast<const uint4*>(w + base + (int64_t)i * 16 * K);
+  for (int i = 0; i < 8; i++) raw[i] = ldg16_stream(w + base + (int64_t)i * 16 * K);
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
