@@ -116,8 +116,7 @@ __device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
 
 // Pack four fp32 accumulators into four bf16 (RNE) for one 8-byte store.
 __device__ __forceinline__ uint2 pack_bf16x4(const v4f &v) {
-  return make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                    f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+  return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 // Token scales of a BM-row tile, staged in LDS in groups of SB K blocks
