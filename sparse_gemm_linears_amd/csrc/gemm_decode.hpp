@@ -617,18 +617,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(W wop, X xop, const typ
 // word staggers the tokens' banks); then (split units only) the partial sums
 // of the waves, double-buffered by band parity: the wave that adds band j's
 // partials reads buffer j & 1 before the barrier of band j + 1, and the next
-// writes to that buffer come after it.
+// writes to that buffer come after it; then (weights read in whole rows) each
+// wave's weight tiles.
 struct SharedTokenLayout {
   int KBs, XS, SS;
-  size_t red_off, bytes;
-  __host__ __device__ SharedTokenLayout(int M, int K, int S, int NW, int RT) {
+  size_t red_off, tiles_off, bytes;
+  __host__ __device__ SharedTokenLayout(int M, int K, int S, int NW, int RT, size_t wtiles = 0) {
     KBs = K / kGroup / S;
     XS = (KBs + ((KBs & 1) ? 2 : 1)) * kGroup;
     SS = KBs + 1;
     red_off = ((size_t)M * XS + (size_t)4 * M * SS + 15) / 16 * 16;
-    bytes = red_off + (size_t)2 * NW * RT * 64 * sizeof(v4f);
+    tiles_off = red_off + (size_t)2 * NW * RT * 64 * sizeof(v4f);
+    bytes = tiles_off + wtiles;
   }
 };
+template <class W, bool R = weight_rows<W>::value>
+struct weight_mfrag {
+  typedef typename W::Frag type;
+};
+template <class W>
+struct weight_mfrag<W, true> {
+  typedef typename W::MFrag type;
+};
+template <class W, int RT, int NW>
+constexpr size_t shared_weight_tiles() {
+  return weight_rows<W>::value ? (size_t)NW * RT * weight_tile_bytes<W>::value : 0;
+}
 
 template <class W, int RT, int NW, int D, int S, bool WB = false>
 __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uint8_t *__restrict__ xq,
@@ -641,8 +655,10 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
-  const SharedTokenLayout L(M, K, S, WB ? 0 : NW, RT);
+  const SharedTokenLayout L(M, K, S, WB ? 0 : NW, RT, shared_weight_tiles<W, RT, NW>());
   const int KB = K / kGroup, US = L.KBs / U;  // K blocks per row, units per split
+  // kRows weights: this wave's tiles
+  uint8_t *const wtile = shared_tokens + L.tiles_off + (size_t)wave * RT * weight_tile_bytes<W>::value;
   uint8_t *codes = shared_tokens;
   float *scales = reinterpret_cast<float *>(shared_tokens + (size_t)M * L.XS);
   v4f *red = reinterpret_cast<v4f *>(shared_tokens + L.red_off);
@@ -744,6 +760,14 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
   const int f_lo = (g ^ swz(m)) << 4, f_hi = ((g + 4) ^ swz(m)) << 4;
   auto consume = [&](int d, const Item &it) {
     const int kr = unit_of(it) * U;  // first K block of the unit, relative to the split
+    typename weight_mfrag<W>::type af[RT];
+#pragma unroll
+    for (int r = 0; r < RT; r++) {
+      if constexpr (weight_rows<W>::value)
+        af[r] = wop.to_frag(a[d][r], wtile + r * weight_tile_bytes<W>::value);
+      else
+        af[r] = a[d][r];
+    }
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const uint8_t *blk = xrow + (kr + u) * kGroup;
@@ -752,9 +776,9 @@ __global__ __launch_bounds__(NW * 64) void decode_shared_kernel(W wop, const uin
 #pragma unroll
       for (int r = 0; r < RT; r++) {
         if constexpr (U == 1)
-          acc[r] += scl * wop.mma(a[d][r], bf);
+          acc[r] += scl * wop.mma(af[r], bf);
         else
-          acc[r] += scl * wop.mma(a[d][r], bf, u);
+          acc[r] += scl * wop.mma(af[r], bf, u);
       }
     }
   };
@@ -943,10 +967,11 @@ constexpr int kSharedTokenMaxLds = 160 * 1024;
 // sums must fit the LDS.  One workgroup per compute unit per split, or two
 // for at most 8 tokens with the split units (whose staging is cheaper;
 // measured on MI355X), each streaming several row bands.
-inline int shared_decode_grid(int M, int N, int K, int S, int U, int NW, int RT, int cus, bool wb = false) {
+inline int shared_decode_grid(int M, int N, int K, int S, int U, int NW, int RT, int cus, bool wb = false,
+                              size_t wtiles = 0) {
   const int KB = K / kGroup;
   if (M < 1 || M > 16 || N % (16 * RT) != 0 || KB % (S * U) != 0 || (!wb && KB / S / U < NW)) return 0;
-  if (SharedTokenLayout(M, K, S, wb ? 0 : NW, RT).bytes > (size_t)kSharedTokenMaxLds) return 0;
+  if (SharedTokenLayout(M, K, S, wb ? 0 : NW, RT, wtiles).bytes > (size_t)kSharedTokenMaxLds) return 0;
   const int bands = N / (16 * RT);
   return std::min(bands, (!wb && M <= 8 ? 2 : 1) * cus) * S;
 }
@@ -967,7 +992,7 @@ hipError_t launch_decode_shared(W wop, const uint8_t *xq, const float *xs, const
     raised[dev].store(true, std::memory_order_release);
   }
   if (S > 1 && !part) return hipErrorInvalidValue;
-  const SharedTokenLayout L(M, K, S, WB ? 0 : NW, RT);
+  const SharedTokenLayout L(M, K, S, WB ? 0 : NW, RT, shared_weight_tiles<W, RT, NW>());
   hipLaunchKernelGGL((decode_shared_kernel<W, RT, NW, D, S, WB>), dim3(grid), dim3(NW * 64), L.bytes, stream, wop, xq,
                      xs, ws, M, N, K, y, part);
   return hipGetLastError();

@@ -695,6 +695,18 @@ static hipError_t launch_dense_decode(X xop, const uint8_t *wq, const typename X
     // weights, and not used on long K, which splits K instead.
     if constexpr (std::is_same<X, QuantTokens>::value) {
       if (M >= 3 && M <= 16 && K < 8192 && N >= 16384) {
+        // whole-row weight tiles from 12 tokens, or from 5 on K >= 6144, where
+        // they fit beside the staged tokens (A/B, weights from HBM, identical
+        // outputs: 28672 x 4096 at 16 tokens 25.4 -> 23.6 us, 18432 x 7168 at
+        // 8 tokens 30.1 -> 26.0 us; slower at 3 tokens, +2-5 %, and on
+        // 28672 x 4096 at 8, +7 %)
+        if (M >= 12 || (M >= 5 && K >= 6144)) {
+          const int gr = shared_decode_grid(M, N, K, 1, 1, 16, 1, device_cu_count(), false,
+                                            shared_weight_tiles<DenseWeightRows, 1, 16>());
+          if (gr > 0)
+            return launch_decode_shared<DenseWeightRows, 1, 16, 2, 1>(DenseWeightRows{{wq, K}}, xop.xq, xop.xs, ws, M,
+                                                                      N, K, y, nullptr, gr, stream);
+        }
         const int grid = shared_decode_grid(M, N, K, 1, 1, 16, 1, device_cu_count());
         if (grid > 0)
           return launch_decode_shared<DenseWeight, 1, 16, 2, 1>(DenseWeight{wq, K}, xop.xq, xop.xs, ws, M, N, K, y,

@@ -671,6 +671,16 @@ static hipError_t launch_sparse_decode(X xop, const uint8_t *wv, const uint8_t *
       if (M >= 3 && M <= 16 && K < 8192 && N >= 16384) {
         const int cus = device_cu_count();
         if (M >= 5) {
+          // whole-row weight tiles where they fit beside the staged tokens
+          // (A/B, weights from HBM, identical outputs: 28672 x 4096 at 5 / 8
+          // / 12 / 16 tokens 16.9 / 16.8 / 17.4 / 18.0 -> 15.8 / 15.8 / 16.3
+          // / 16.7 us, 18432 x 7168 at 5 / 8 / 12 tokens 20.0 / 20.5 / 21.6
+          // -> 18.8 / 19.0 / 19.8 us)
+          const int gr = shared_decode_grid(M, N, K, 1, SparseWeight4::kUnit, 16, 1, cus, true,
+                                            shared_weight_tiles<SparseWeight4Rows, 1, 16>());
+          if (gr > 0)
+            return launch_decode_shared<SparseWeight4Rows, 1, 16, 2, 1, true>(
+                SparseWeight4Rows{{wv, wm, K}}, xop.xq, xop.xs, ws, M, N, K, y, nullptr, gr, stream);
           const int grid = shared_decode_grid(M, N, K, 1, SparseWeight4::kUnit, 16, 1, cus, true);
           if (grid > 0)
             return launch_decode_shared<SparseWeight4, 1, 16, 2, 1, true>(SparseWeight4{wv, wm, K}, xop.xq, xop.xs,

@@ -32,8 +32,10 @@ def acts(M, K, seed):
 
 @pytest.mark.parametrize("M,N,K", [(3, 16384, 2048), (5, 16384, 2048), (7, 16384, 5120), (8, 28672, 4096),
                                    (11, 28672, 4096), (16, 28672, 4096), (16, 16384, 2048), (4, 32768, 4096),
-                                   (13, 16384, 7168)])
+                                   (13, 16384, 7168), (6, 16384, 7168)])
 def test_dense_shared_decode(gpu_lib, M, N, K):
+    """Weight tiles in whole rows from 12 tokens (or 5 on K >= 6144) where the LDS holds them: (16, 28672, 4096),
+    (16, 16384, 2048), (13, 16384, 7168) and (6, 16384, 7168); fragments at 3-11 tokens on shorter K."""
     _, (xq, xs) = acts(M, K, 41 + M)
     wq, ws = oracle.quant_wblock(si.weights(N, K, seed=7 + N % 97))
     y = gpu_lib.fp8_block_gemm(dev(xq), dev(xs), dev(wq), dev(ws))
@@ -41,8 +43,10 @@ def test_dense_shared_decode(gpu_lib, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(3, 16384, 4096), (6, 16384, 5120), (8, 28672, 4096), (12, 16384, 2048),
-                                   (16, 28672, 4096), (16, 16384, 7168)])
+                                   (16, 28672, 4096), (16, 16384, 7168), (5, 18432, 7168)])
 def test_sparse_shared_decode(gpu_lib, M, N, K):
+    """From 5 tokens the weight comes in whole-row tiles where they fit beside the staged tokens; (16, 16384, 7168)
+    does not fit and keeps fragments."""
     _, (xq, xs) = acts(M, K, 43 + M)
     w = si.weights(N, K, seed=11 + N % 89)
     vals, meta, ws = oracle.prune24_compress(w)
