@@ -646,7 +646,27 @@ static hipError_t launch_decode_for(X xop, const uint8_t *wv, const uint8_t *wm,
   if constexpr (!X::kStaged && CT == 4)
     if (splits == 2) return launch_decode<X, 2, CT, 8, 2, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);
   if constexpr (CT == 1)
-    if (M <= 4) return launch_decode<X, 1, CT, 16, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);
+    if (M <= 4) {
+      // Up to 4 quantized tokens on K with fewer four-block units than 16
+      // waves (K < 8192): whole-row four-block tiles over fewer waves, each
+      // wave with one or two units in flight.  Against one block at a time
+      // over 16 waves (A/B, weights from HBM, outputs equal to 5e-5): 6144 x
+      // 4096 at 1 / 2 / 4 tokens 7.4 / 8.0 / 8.6 -> 5.4 / 5.4 / 5.4 us (32-row
+      // bands, 8 waves), 4096 x 4096 5.1 / 5.3 / 5.7 -> 4.7 / 4.7 / 4.7 us (8
+      // waves), 28672 x 4096 at 1 / 2 tokens 20.4 / 22.0 -> 17.1 / 17.3 us (4
+      // waves, two units in flight).
+      if constexpr (!X::kStaged)
+        if ((K / kGroup) % SparseWeight4::kUnit == 0 && (K / kGroup) / SparseWeight4::kUnit >= 8 &&
+            (K / kGroup) / SparseWeight4::kUnit < 16) {
+          const SparseWeight4Rows w4{{wv, wm, K}};
+          if (N >= 16384)
+            return launch_decode_with<SparseWeight4Rows, X, 1, CT, 4, 2, 1>(w4, xop, ws, M, N, K, y, part, stream);
+          if (N >= 6144)
+            return launch_decode_with<SparseWeight4Rows, X, 2, CT, 8, 1, 1>(w4, xop, ws, M, N, K, y, part, stream);
+          return launch_decode_with<SparseWeight4Rows, X, 1, CT, 8, 1, 1>(w4, xop, ws, M, N, K, y, part, stream);
+        }
+      return launch_decode<X, 1, CT, 16, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);
+    }
   if constexpr (CT <= 2)
     if (N >= 16384) return launch_decode<X, 4, CT, 8, 3>(xop, wv, wm, ws, M, N, K, y, part, stream);
   if (N >= 6144) return launch_decode<X, 2, CT, 8, 2>(xop, wv, wm, ws, M, N, K, y, part, stream);

@@ -315,7 +315,7 @@ def run_sparse(gpu_lib, xq, xs, vals, meta, ws):
     return gpu_lib.fp8_sparse24_gemm(dev(xq), dev(xs), dev(vals), dev(meta), dev(ws))
 
 
-@pytest.mark.parametrize("M", [16, 4096])
+@pytest.mark.parametrize("M", [1, 2, 4, 16, 4096])
 @pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
 def test_sparse_gemm_llama(gpu_lib, name, K, N, M):
     _, (xq, xs) = llama_acts(M, K)
@@ -324,6 +324,18 @@ def test_sparse_gemm_llama(gpu_lib, name, K, N, M):
     rows = sample_tile_rows(M, 12) if M > 16 else np.arange(M)
     ref = oracle.sparse24_gemm(xq, xs, vals, meta, ws, rows=rows)
     assert_gemm_close(y[torch.from_numpy(rows).to(DEV)], ref, f"{name} M={M}")
+
+
+# 1-4 tokens with 8-15 four-block units per row (K of 4096-8064): whole-row
+# tiles over 4 waves (N >= 16384), 32-row bands over 8 waves (6144 <= N <
+# 16384) or 16-row bands over 8 waves.
+@pytest.mark.parametrize("M,N,K", [(3, 6400, 5120), (1, 16384, 6144), (2, 640, 7680), (4, 384, 4608)])
+def test_sparse_decode_few_tokens(gpu_lib, M, N, K):
+    x = si.activations(M, K, outliers=True, seed=M + N % 101)
+    xq, xs = oracle.quant_act(x)
+    vals, meta, ws = oracle.prune24_compress(si.weights(N, K, seed=3 + K % 7))
+    y = run_sparse(gpu_lib, xq, xs, vals, meta, ws)
+    assert_gemm_close(y, oracle.sparse24_gemm(xq, xs, vals, meta, ws), f"{M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 512, 512), (1, 256, 384), (40, 384, 256), (65, 384, 640),
