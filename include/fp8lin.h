@@ -361,6 +361,10 @@ fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *
 /*
  * The same fused decode-sized linear with a 2:4-compressed weight from
  * prune24_compress; bit-identical to fp8_quant_act then fp8_sparse24_gemm.
+ * One or two tokens are quantized inside the kernel as above, except on K a
+ * multiple of 512 from 4096 to 7680, where fp8_sparse24_gemm streams the
+ * weight in whole-row four-block tiles faster than the in-kernel form: there
+ * the call is the two calls.
  *
  *   x [M,K] bf16, M <= 64; wvals [N,K/2], wmeta [N,K/8], ws [N/128,K/128]; y [M,N] bf16
  */

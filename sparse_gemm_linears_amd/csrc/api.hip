@@ -335,7 +335,7 @@ fp8l_status fp8_block_linear(const uint16_t *x, const uint8_t *wq, const float *
   if (any_alias(outs, 1, ins, 3)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
   fp8lin::CallScratch sc;
-  const size_t tokens = fp8lin::linear_token_bytes(M, N, K);
+  const size_t tokens = fp8lin::linear_token_bytes(M, N, K, false);
   if (hipError_t e = sc.acquire(fp8lin::gemm_partial_bytes(M, N, K, fp8lin::device_cu_count()), tokens, stream))
     return launched(e);
   const hipError_t e = fp8lin::launch_dense_linear(x, wq, ws, M, N, K, y, sc.tokens(), sc.partials(), stream);
@@ -354,7 +354,7 @@ fp8l_status fp8_sparse24_linear(const uint16_t *x, const uint8_t *wvals, const u
   if (any_alias(outs, 1, ins, 4)) return FP8L_ERR_ALIAS;
   if (fp8l_status st = check_device()) return st;
   fp8lin::CallScratch sc;
-  const size_t tokens = fp8lin::linear_token_bytes(M, N, K);
+  const size_t tokens = fp8lin::linear_token_bytes(M, N, K, true);
   if (hipError_t e = sc.acquire(fp8lin::gemm_partial_bytes(M, N, K, fp8lin::device_cu_count()), tokens, stream))
     return launched(e);
   const hipError_t e = fp8lin::launch_sparse_linear(x, wvals, wmeta, ws, M, N, K, y, sc.tokens(), sc.partials(),

@@ -735,8 +735,8 @@ size_t swiglu_partial_bytes(int64_t M, int64_t I, int64_t K, int cus) {
   return (size_t)p.splits * (size_t)M * (size_t)(2 * I) * sizeof(float);
 }
 
-size_t linear_token_bytes(int64_t M, int64_t N, int64_t K) {
-  if (!use_tile_kernel(M, N, K) && staged_tokens_fit(M, K)) return 0;  // quantized inside the decode kernel
+size_t linear_token_bytes(int64_t M, int64_t N, int64_t K, bool sparse) {
+  if (linear_staged(M, N, K, sparse)) return 0;  // quantized inside the decode kernel
   return token_codes_bytes(M, K) + (size_t)M * (size_t)(K / kGroup) * sizeof(float);
 }
 
@@ -810,7 +810,7 @@ hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const u
 // from three tokens on: every decode workgroup would re-quantize all M x K).
 hipError_t launch_dense_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
                                int64_t K, uint16_t *y, uint8_t *tokens, float *part, hipStream_t stream) {
-  if (!use_tile_kernel(M, N, K) && staged_tokens_fit(M, K))
+  if (linear_staged(M, N, K, false))
     return launch_dense_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wq, ws, (int)M, (int)N, (int)K, y, part,
                                stream);
   if (!tokens) return hipErrorInvalidValue;

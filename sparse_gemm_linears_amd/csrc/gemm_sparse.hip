@@ -633,6 +633,13 @@ static hipError_t launch_decode(X xop, const uint8_t *wv, const uint8_t *wm, con
 }
 
 
+// Up to 4 quantized tokens: K whose four-block units number 8 to 15 takes
+// the whole-row four-block tiles over 4 or 8 waves (launch_decode_for).
+static inline bool few_token_rows4(int64_t K) {
+  const int64_t units = K / kGroup / SparseWeight4::kUnit;
+  return (K / kGroup) % SparseWeight4::kUnit == 0 && units >= 8 && units < 16;
+}
+
 // Decode configuration (measured on MI355X over the Llama-3-8B shapes): more
 // rows per workgroup when N is large enough to keep every CU busy, since each
 // workgroup re-reads the M x K activations from L2.  K splits as in the dense
@@ -656,8 +663,7 @@ static hipError_t launch_decode_for(X xop, const uint8_t *wv, const uint8_t *wm,
       // waves), 28672 x 4096 at 1 / 2 tokens 20.4 / 22.0 -> 17.1 / 17.3 us (4
       // waves, two units in flight).
       if constexpr (!X::kStaged)
-        if ((K / kGroup) % SparseWeight4::kUnit == 0 && (K / kGroup) / SparseWeight4::kUnit >= 8 &&
-            (K / kGroup) / SparseWeight4::kUnit < 16) {
+        if (few_token_rows4(K)) {
           const SparseWeight4Rows w4{{wv, wm, K}};
           if (N >= 16384)
             return launch_decode_with<SparseWeight4Rows, X, 1, CT, 4, 2, 1>(w4, xop, ws, M, N, K, y, part, stream);
@@ -735,12 +741,20 @@ hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   return e;
 }
 
+bool linear_staged(int64_t M, int64_t N, int64_t K, bool sparse) {
+  return !use_tile_kernel(M, N, K) && staged_tokens_fit(M, K) && !(sparse && few_token_rows4(K));
+}
+
 // As the dense linear: in-kernel quantization for one or two tokens, else
-// fp8_quant_act into the call's scratch tokens and fp8_sparse24_gemm.
+// fp8_quant_act into the call's scratch tokens and fp8_sparse24_gemm.  The
+// staged form sums in the order of the one-block kernel over 16 waves, so it
+// is not used where fp8_sparse24_gemm takes the whole-row four-block tiles
+// (few_token_rows4): there the two calls run, and the result stays
+// bit-identical to them.
 hipError_t launch_sparse_linear(const uint16_t *x, const uint8_t *wv, const uint8_t *wm, const float *ws, int64_t M,
                                 int64_t N, int64_t K, uint16_t *y, uint8_t *tokens, float *part,
                                 hipStream_t stream) {
-  if (!use_tile_kernel(M, N, K) && staged_tokens_fit(M, K))
+  if (linear_staged(M, N, K, true))
     return launch_sparse_decode(StagedTokens{x, (int)K, nullptr, nullptr}, wv, wm, ws, (int)M, (int)N, (int)K, y,
                                 part, stream);
   if (!tokens) return hipErrorInvalidValue;

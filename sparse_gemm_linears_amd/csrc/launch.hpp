@@ -50,10 +50,13 @@ size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, int cus);
 // The same for fp8_block_gemm_swiglu (the stacked [gate; up] GEMM of 2I rows
 // when it runs on smaller tiles or split K).
 size_t swiglu_partial_bytes(int64_t M, int64_t I, int64_t K, int cus);
+// Whether the fused linear call quantizes the tokens inside the decode kernel
+// (one or two tokens), for the dense or the 2:4 weight.
+bool linear_staged(int64_t M, int64_t N, int64_t K, bool sparse);
 // Scratch of the fused linear calls: the quantized tokens (codes, then fp32
 // scales at a 256-byte aligned offset; 0 bytes when the tokens are quantized
 // inside the decode kernel) and the partials of the GEMM that follows.
-size_t linear_token_bytes(int64_t M, int64_t N, int64_t K);
+size_t linear_token_bytes(int64_t M, int64_t N, int64_t K, bool sparse);
 inline size_t token_codes_bytes(int64_t M, int64_t K) { return ((size_t)M * (size_t)K + 255) / 256 * 256; }
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
 
