@@ -346,7 +346,8 @@ fp8l_status fp8_block_gemm_swiglu(const uint8_t *xq, const float *xs, const uint
  *   y [M,N] bf16
  * y is bit-identical to fp8_quant_act(x) followed by fp8_block_gemm on the
  * resulting codes and scales.  One or two tokens (with the M x K codes fitting
- * in 36 KB of LDS) are quantized inside the weight-streaming kernel: every
+ * in 36 KB of LDS, and K < 8192, where fp8_block_gemm streams the weight over
+ * four waves) are quantized inside the weight-streaming kernel: every
  * workgroup quantizes the tokens into LDS and the codes are never written out.
  * Otherwise, where re-quantizing in every workgroup would cost more than it
  * saves, the call is those two calls, with the codes in library scratch memory.

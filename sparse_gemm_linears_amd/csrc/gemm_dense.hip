@@ -805,9 +805,10 @@ hipError_t launch_dense_grouped_gemm(const uint8_t *xq, const float *xs, const u
   return hipGetLastError();
 }
 
-// One or two tokens: quantized inside the decode kernel (StagedTokens).  More:
-// fp8_quant_act into library scratch memory, then fp8_block_gemm (measured faster
-// from three tokens on: every decode workgroup would re-quantize all M x K).
+// One or two tokens on K < 8192: quantized inside the decode kernel
+// (StagedTokens; linear_staged says where).  Otherwise fp8_quant_act into
+// library scratch memory, then fp8_block_gemm (measured faster from three
+// tokens on: every decode workgroup would re-quantize all M x K).
 hipError_t launch_dense_linear(const uint16_t *x, const uint8_t *wq, const float *ws, int64_t M, int64_t N,
                                int64_t K, uint16_t *y, uint8_t *tokens, float *part, hipStream_t stream) {
   if (linear_staged(M, N, K, false))

@@ -741,8 +741,14 @@ hipError_t launch_sparse_gemm(const uint8_t *xq, const float *xs, const uint8_t 
   return e;
 }
 
+// Where the GEMM itself takes a form that the in-kernel quantization does not
+// have, the linear call runs the two calls: the 2:4 whole-row four-block tiles
+// (few_token_rows4), and the dense four-wave form on K >= 8192 (measured on
+// MI355X, 4096 x 14336 at one token: 13.4 us as two calls against 14.8 us
+// quantized in the 16-wave kernel).
 bool linear_staged(int64_t M, int64_t N, int64_t K, bool sparse) {
-  return !use_tile_kernel(M, N, K) && staged_tokens_fit(M, K) && !(sparse && few_token_rows4(K));
+  if (use_tile_kernel(M, N, K) || !staged_tokens_fit(M, K)) return false;
+  return sparse ? !few_token_rows4(K) : K < 8192;
 }
 
 // As the dense linear: in-kernel quantization for one or two tokens, else

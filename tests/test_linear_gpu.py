@@ -37,7 +37,7 @@ def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
     return torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [1, 5, 8, 16, 32, 37, 64])
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 16, 32, 37, 64])
 @pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
 def test_block_linear_llama(gpu_lib, name, K, N, M):
     x = si.activations(M, K)
@@ -52,7 +52,7 @@ def test_block_linear_llama(gpu_lib, name, K, N, M):
                       f"{name} M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 16, 40, 64])
+@pytest.mark.parametrize("M", [1, 2, 16, 40, 64])
 @pytest.mark.parametrize("name,K,N", si.LLAMA3_8B)
 def test_sparse24_linear_llama(gpu_lib, name, K, N, M):
     x = si.activations(M, K)
