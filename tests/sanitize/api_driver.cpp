@@ -127,8 +127,13 @@ static void plans() {
         const size_t sw = fp8lin::swiglu_partial_bytes(M, N, K, cus);
         EXPECT(sw == 0 || sw % ((size_t)M * 2 * N * 4) == 0);
         if (M <= 64) {
-          const size_t tb = fp8lin::linear_token_bytes(M, N, K);
-          EXPECT(tb == 0 || tb >= (size_t)M * K + (size_t)M * (K / 128) * 4);
+          for (bool sparse : {false, true}) {
+            const size_t tb = fp8lin::linear_token_bytes(M, N, K, sparse);
+            // no scratch tokens exactly where the call quantizes in the kernel
+            EXPECT((tb == 0) == fp8lin::linear_staged(M, N, K, sparse));
+            EXPECT(tb == 0 || tb >= (size_t)M * K + (size_t)M * (K / 128) * 4);
+            if (fp8lin::linear_staged(M, N, K, sparse)) EXPECT(M <= 2);
+          }
         }
       }
     }
