@@ -650,14 +650,15 @@ static hipError_t launch_decode_for(X xop, const uint8_t *wv, const uint8_t *wm,
   const int splits = X::kStaged ? 1 : decode_splits(M, N, K);
   if constexpr (!X::kStaged && CT <= 2)
     if (splits == 4) {
-      // One token tile: whole-row four-block tiles over 32-row bands, K in
-      // two splits (the partials hold four).  Measured on MI355X, 4096 x 14336
-      // from HBM (A/B, graph replay): 12 / 16 tokens 13.1 / 13.45 -> 11.7 /
-      // 11.9 us against four splits of 64-row bands with fragment loads;
-      // four splits of 32-row bands over 4 waves 11.9 / 12.4, over 8 waves
-      // level, 16-row bands 15.5 / 16.4; 64-row whole-row bands spill.
-      if constexpr (CT == 1)
-        if ((K / kGroup) % SparseWeight4::kUnit == 0)
+      // Whole-row four-block tiles over 32-row bands, K in two splits (the
+      // partials hold four).  Measured on MI355X, 4096 x 14336 from HBM (A/B,
+      // graph replay) against four splits of 64-row bands with fragment
+      // loads: 12 / 16 tokens 13.1 / 13.45 -> 11.7 / 11.9 us (four splits of
+      // 32-row bands over 4 waves 11.9 / 12.4, over 8 waves level, 16-row
+      // bands 15.5 / 16.4; 64-row whole-row bands spill); 20 / 24 / 32 tokens
+      // 16.5 / 16.9 / 17.3 -> 14.2 / 15.0 / 16.2 us (16-row bands 18.0 / 18.3
+      // / 19.0, fragment loads 15.6 / 16.4 / 18.0).
+      if ((K / kGroup) % SparseWeight4::kUnit == 0)
           return launch_decode_with<SparseWeight4Rows, X, 2, CT, 8, 1, 2>(SparseWeight4Rows{{wv, wm, K}}, xop, ws, M,
                                                                           N, K, y, part, stream);
       return launch_decode<X, 4, CT, 8, 2, 4>(xop, wv, wm, ws, M, N, K, y, part, stream);
