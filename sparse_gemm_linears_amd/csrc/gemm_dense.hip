@@ -661,12 +661,15 @@ static hipError_t launch_decode_for(X xop, const uint8_t *wq, const typename X::
   const int splits = X::kStaged ? 1 : decode_splits(M, N, K);
   if constexpr (!X::kStaged && CT <= 2)
     if (splits == 4) {
-      // one token tile: 32-row bands, K in two splits (the partials hold
-      // four).  4096 x 14336 from HBM (A/B, graph replay): 12 / 16 tokens
-      // 14.8 / 15.0 -> 13.7 / 14.35 us; 64-row bands in two splits 17.9 /
-      // 18.5, 32-row bands in four 14.4 / 15.0.
+      // 32-row bands, K in two splits (the partials hold four).  4096 x
+      // 14336 from HBM (A/B, graph replay) against 64-row bands in four
+      // splits: 12 / 16 tokens 14.8 / 15.0 -> 13.7 / 14.35 us (64-row bands
+      // in two splits 17.9 / 18.5, 32-row bands in four 14.4 / 15.0); 20 / 24
+      // / 32 tokens, one K block in flight per wave, 16.2 / 16.45 / 16.95 ->
+      // 14.97 / 15.4 / 16.17 us (two in flight 15.2 / 15.5 / 16.2, four
+      // splits 18.2 / 18.6 / 19.3).
       if constexpr (CT == 1) return launch_decode<X, 2, CT, 8, 2, 2>(xop, wq, ws, M, N, K, y, part, stream);
-      return launch_decode<X, 4, CT, 8, 2, 4>(xop, wq, ws, M, N, K, y, part, stream);
+      return launch_decode<X, 2, CT, 8, 1, 2>(xop, wq, ws, M, N, K, y, part, stream);
     }
   if constexpr (!X::kStaged && CT == 4)
     if (splits == 2) return launch_decode<X, 2, CT, 8, 2, 2>(xop, wq, ws, M, N, K, y, part, stream);
